@@ -1,0 +1,153 @@
+/*
+ * coalesce.h -- C ABI of the MI355X (gfx950) fused-epilogue GEMM and softplus
+ * MLP megakernel library (libcoalesce.so).
+ *
+ * Every pointer argument named as device memory is a device pointer owned by
+ * the caller; the library keeps no pointer after a call returns and never
+ * allocates device memory on these paths.  `stream` is a hipStream_t passed
+ * as void* (NULL = the legacy default stream).  Calls only enqueue work:
+ * they return before the GPU has run it, and a fault inside a kernel shows
+ * up at the caller's next synchronisation of that stream.
+ *
+ * Errors: every entry point validates its arguments on the host before it
+ * launches anything.  On any return other than COALESCE_OK nothing has been
+ * launched and no output has been written; coalesce_last_error() then gives
+ * a one-line explanation (thread-local, valid until the next call on the
+ * same thread).
+ *   COALESCE_ERR_INVALID_ARGUMENT  a NULL pointer where data is needed, a
+ *                                  negative extent, a leading dimension
+ *                                  shorter than the row, an unknown enum.
+ *   COALESCE_ERR_UNSUPPORTED       a valid request this build does not
+ *                                  implement (alignment, dtype combination,
+ *                                  MLP width or depth), see each function.
+ *   COALESCE_ERR_DEVICE            a HIP call failed (launch or device query).
+ *
+ * Layout: every matrix is row-major with a leading dimension (elements
+ * between consecutive rows) and unit inner stride.  Alignment: base
+ * pointers must be 16-byte aligned and ld * element_size a multiple of 16
+ * bytes, so that every row can be moved with 128-bit accesses.  The extents
+ * M, N, K themselves are arbitrary (partial tiles are masked).
+ */
+#ifndef COALESCE_H
+#define COALESCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  COALESCE_OK = 0,
+  COALESCE_ERR_INVALID_ARGUMENT = 1,
+  COALESCE_ERR_UNSUPPORTED = 2,
+  COALESCE_ERR_DEVICE = 3
+} coalesce_status;
+
+typedef enum { COALESCE_F32 = 0, COALESCE_F16 = 1, COALESCE_BF16 = 2 } coalesce_dtype;
+
+typedef enum {
+  COALESCE_ACT_NONE = 0,
+  COALESCE_ACT_GELU_ERF = 1, /* 0.5 z (1 + erf(z / sqrt 2)) */
+  COALESCE_ACT_SOFTPLUS = 2  /* ln(1 + e^z), evaluated as z above 20 */
+} coalesce_act;
+
+/*
+ * Y = act(A . B + bias) with the bias add and the activation applied to the
+ * fp32 accumulators in registers, then one rounding to out_dtype and one
+ * store of Y.  Defined by the "Coalesce" README ("Fusion study": GEMM + bias
+ * + GELU fused into the GEMM kernel; "Notes for future sessions": GELU is
+ * the erf form), with softplus as in the "MLP Megakernel" README.
+ *
+ *   A     device, M x K, in_dtype, leading dimension lda >= K
+ *   B     device, K x N, in_dtype, leading dimension ldb >= N
+ *   bias  device, N elements of in_dtype (added to every row), or NULL
+ *   Y     device, M x N, out_dtype, leading dimension ldy >= N (written)
+ * Accumulation is fp32 (fp32 MFMA for F32 inputs, bf16/fp16 MFMA otherwise);
+ * bias and activation are computed in fp32; the store rounds to nearest even.
+ * Supported (in_dtype -> out_dtype): F32->F32, BF16->BF16, BF16->F32,
+ * F16->F16, F16->F32.  M, N, K must be below 2^31; M == 0 or N == 0 is a
+ * no-op; K == 0 gives Y = act(bias) (act(0) without a bias), and A, B may
+ * then be NULL.  Y must not overlap A, B or bias.
+ */
+coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb, const void* bias,
+                                       void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                       coalesce_dtype in_dtype, coalesce_dtype out_dtype, coalesce_act act,
+                                       void* stream);
+
+/*
+ * Persistent MLP megakernel ("MLP Megakernel" README, "Architecture" and
+ * "Key ideas"):
+ *   h_0 = x;  h_l = act(h_{l-1} W_l) for l < L;  out = h_{L-1} W_L
+ * with no biases and a linear last layer, in ONE launch whose intermediate
+ * activations stay on chip (fp16 MFMA operands, fp32 accumulation, the
+ * activation in fp32, h_l rounded to fp16 only as the next layer's operand).
+ * The grid is min(#CUs x occupancy, #tiles) workgroups that walk the row
+ * tiles round-robin.
+ *
+ *   x     device, M x dims[0] fp16, leading dimension ldx >= dims[0]
+ *   W     HOST array of L device pointers; W[l] is dims[l] x dims[l+1] fp16,
+ *         dense row-major (the x @ W orientation)
+ *   dims  HOST array of L + 1 widths
+ *   out   device, M x dims[L] fp16, leading dimension ldo >= dims[L] (written)
+ * Supported: dtype F16; hidden_act SOFTPLUS (or NONE: a linear chain); all
+ * widths equal to 64 (L = 1..8) or to 128 (L = 1..4).  M == 0 is a no-op.
+ */
+coalesce_status coalesce_mlp_forward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims, int32_t L,
+                                     void* out, int64_t ldo, int64_t M, coalesce_dtype dtype, coalesce_act hidden_act,
+                                     void* stream);
+
+/*
+ * As coalesce_mlp_forward, with the persistent grid size chosen by the
+ * caller: num_workgroups > 0 launches exactly that many workgroups (each
+ * walks the tiles round-robin), 0 picks min(#CUs x occupancy, #tiles).  The
+ * result does not depend on the grid size, bit for bit.
+ */
+coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                          int32_t L, void* out, int64_t ldo, int64_t M, coalesce_dtype dtype,
+                                          coalesce_act hidden_act, int64_t num_workgroups, void* stream);
+
+/*
+ * Unfused baseline, step 2: Y = X + bias (bias broadcast over rows), each
+ * element converted to fp32, added, and rounded once to y_dtype.  The
+ * elementwise-kernel design of the "Fuse Elementwise Ops" page (vectorised
+ * 128-bit loads, bounds-guarded tails).
+ *   X device M x N (x_dtype, ldx), bias device N elements (bias_dtype),
+ *   Y device M x N (y_dtype, ldy); Y may equal X (in place) when the types
+ *   and leading dimensions match.
+ */
+coalesce_status coalesce_bias_add(const void* X, int64_t ldx, const void* bias, void* Y, int64_t ldy, int64_t M,
+                                  int64_t N, coalesce_dtype x_dtype, coalesce_dtype bias_dtype, coalesce_dtype y_dtype,
+                                  void* stream);
+
+/*
+ * Unfused baseline, step 3: Y = act(X) elementwise in fp32, rounded once to
+ * the storage type.  X and Y are device M x N of `dtype`; Y may equal X.
+ */
+coalesce_status coalesce_activation(const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t M, int64_t N,
+                                    coalesce_dtype dtype, coalesce_act act, void* stream);
+
+/*
+ * Benchmark helper: stream `bytes` of device memory at `buf` through the
+ * cache hierarchy with 128-bit reads so that the L2 and the MALL hold none
+ * of the operands of the next timed kernel (the "Coalesce" README's harness
+ * flushes the cache before every timed run).  `sink` is a device pointer to
+ * at least 4 bytes that receives a value derived from the data (it keeps
+ * the reads alive).  buf must be 16-byte aligned, bytes a multiple of 16.
+ */
+coalesce_status coalesce_flush_caches(const void* buf, size_t bytes, void* sink, void* stream);
+
+/* Number of compute units of the current device (cached per device). */
+int32_t coalesce_device_cu_count(void);
+
+const char* coalesce_status_string(coalesce_status s);
+const char* coalesce_last_error(void);
+/* Library version, major * 10000 + minor * 100 + patch. */
+int32_t coalesce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* COALESCE_H */

@@ -1,0 +1,291 @@
+// C ABI of libcoalesce: argument validation on the host, tile/grid choice,
+// and the launch on the caller's stream.  Nothing is launched unless every
+// check passes; no device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <mutex>
+
+#include "../../include/coalesce.h"
+#include "launch.hpp"
+
+using namespace coalesce;
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+coalesce_status fail(coalesce_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+coalesce_status ok() {
+  g_last_error[0] = '\0';
+  return COALESCE_OK;
+}
+
+coalesce_status device_fail(hipError_t e, const char* what) {
+  return fail(COALESCE_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_props_mutex;
+int g_cu_count[kMaxDevices] = {0};
+
+// CU count of the current device, queried once per device.
+coalesce_status current_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(COALESCE_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_props_mutex);
+  if (g_cu_count[dev] == 0) {
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
+    if (cus <= 0) return fail(COALESCE_ERR_DEVICE, "device reports %d compute units", cus);
+    g_cu_count[dev] = cus;
+  }
+  *out = g_cu_count[dev];
+  return COALESCE_OK;
+}
+
+bool valid_dtype(int d) { return d == COALESCE_F32 || d == COALESCE_F16 || d == COALESCE_BF16; }
+bool valid_act(int a) { return a == COALESCE_ACT_NONE || a == COALESCE_ACT_GELU_ERF || a == COALESCE_ACT_SOFTPLUS; }
+int64_t dsize(int d) { return d == COALESCE_F32 ? 4 : 2; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+const int64_t kMaxExtent = (int64_t)INT32_MAX;
+
+// Byte range [lo, hi) covered by a rows x cols matrix with leading dimension ld.
+struct Range {
+  uintptr_t lo, hi;
+};
+Range span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t es) {
+  uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  if (!p || rows <= 0 || cols <= 0) return {lo, lo};
+  return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * es)};
+}
+bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+
+int act_code(coalesce_act a) {
+  return a == COALESCE_ACT_GELU_ERF ? ACT_GELU : a == COALESCE_ACT_SOFTPLUS ? ACT_SOFTPLUS : ACT_NONE;
+}
+
+}  // namespace
+
+extern "C" {
+
+coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb, const void* bias,
+                                       void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                       coalesce_dtype in_dtype, coalesce_dtype out_dtype, coalesce_act act,
+                                       void* stream) {
+  if (M < 0 || N < 0 || K < 0)
+    return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative extent (M=%lld N=%lld K=%lld)", (long long)M, (long long)N,
+                (long long)K);
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (!valid_act(act)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown activation %d", (int)act);
+  const bool combo_ok = (in_dtype == COALESCE_F32 && out_dtype == COALESCE_F32) ||
+                        (in_dtype == COALESCE_BF16 && (out_dtype == COALESCE_BF16 || out_dtype == COALESCE_F32)) ||
+                        (in_dtype == COALESCE_F16 && (out_dtype == COALESCE_F16 || out_dtype == COALESCE_F32));
+  if (!combo_ok)
+    return fail(COALESCE_ERR_UNSUPPORTED, "dtype combination in=%d out=%d not supported", (int)in_dtype,
+                (int)out_dtype);
+  if (M > kMaxExtent || N > kMaxExtent || K > kMaxExtent)
+    return fail(COALESCE_ERR_UNSUPPORTED, "extents must be below 2^31");
+  if (M == 0 || N == 0) return ok();
+  const int64_t is = dsize(in_dtype), os = dsize(out_dtype);
+  if (!Y) return fail(COALESCE_ERR_INVALID_ARGUMENT, "Y is NULL");
+  if (ldy < N) return fail(COALESCE_ERR_INVALID_ARGUMENT, "ldy (%lld) < N (%lld)", (long long)ldy, (long long)N);
+  if (K > 0) {
+    if (!A || !B) return fail(COALESCE_ERR_INVALID_ARGUMENT, "A or B is NULL with K > 0");
+    if (lda < K) return fail(COALESCE_ERR_INVALID_ARGUMENT, "lda (%lld) < K (%lld)", (long long)lda, (long long)K);
+    if (ldb < N) return fail(COALESCE_ERR_INVALID_ARGUMENT, "ldb (%lld) < N (%lld)", (long long)ldb, (long long)N);
+    if (!aligned16(A) || !aligned16(B)) return fail(COALESCE_ERR_UNSUPPORTED, "A and B must be 16-byte aligned");
+    if ((lda * is) % 16 || (ldb * is) % 16)
+      return fail(COALESCE_ERR_UNSUPPORTED, "lda and ldb must span a multiple of 16 bytes");
+  }
+  if (!aligned16(Y) || (ldy * os) % 16)
+    return fail(COALESCE_ERR_UNSUPPORTED, "Y must be 16-byte aligned with ldy spanning a multiple of 16 bytes");
+  if (bias && !aligned16(bias)) return fail(COALESCE_ERR_UNSUPPORTED, "bias must be 16-byte aligned");
+  const Range ry = span(Y, M, N, ldy, os);
+  if ((K > 0 && (overlap(ry, span(A, M, K, lda, is)) || overlap(ry, span(B, K, N, ldb, is)))) ||
+      overlap(ry, span(bias, 1, N, N, is)))
+    return fail(COALESCE_ERR_INVALID_ARGUMENT, "Y overlaps an input");
+
+  int cus = 0;
+  coalesce_status s = current_cus(&cus);
+  if (s != COALESCE_OK) return s;
+  GemmParams p{};
+  p.A = A;
+  p.B = B;
+  p.bias = bias;
+  p.Y = Y;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldy = ldy;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  hipError_t e;
+  if (in_dtype == COALESCE_F32)
+    e = launch_gemm32(p, act_code(act), (hipStream_t)stream, cus);
+  else
+    e = launch_gemm16(p, in_dtype == COALESCE_BF16 ? DT_BF16 : DT_F16, out_dtype == COALESCE_F32 ? DT_F32 : (in_dtype == COALESCE_BF16 ? DT_BF16 : DT_F16),
+                      act_code(act), (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "GEMM launch");
+  return ok();
+}
+
+coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                          int32_t L, void* out, int64_t ldo, int64_t M, coalesce_dtype dtype,
+                                          coalesce_act hidden_act, int64_t num_workgroups, void* stream) {
+  if (L < 1) return fail(COALESCE_ERR_INVALID_ARGUMENT, "L must be at least 1 (got %d)", (int)L);
+  if (!W || !dims) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W or dims is NULL");
+  if (M < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative M");
+  if (num_workgroups < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative workgroup count");
+  if (!valid_dtype(dtype)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (!valid_act(hidden_act)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown activation");
+  for (int l = 0; l <= L; ++l)
+    if (dims[l] <= 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dims[%d] = %lld is not positive", l, (long long)dims[l]);
+  if (dtype != COALESCE_F16) return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel takes fp16 only");
+  if (hidden_act == COALESCE_ACT_GELU_ERF)
+    return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel supports softplus or no hidden activation");
+  const int64_t D = dims[0];
+  for (int l = 1; l <= L; ++l)
+    if (dims[l] != D) return fail(COALESCE_ERR_UNSUPPORTED, "all MLP widths must be equal");
+  if (D != 64 && D != 128) return fail(COALESCE_ERR_UNSUPPORTED, "MLP width %lld not supported (64 or 128)", (long long)D);
+  if ((D == 128 && L > 4) || (D == 64 && L > 8))
+    return fail(COALESCE_ERR_UNSUPPORTED, "%d layers of width %lld do not fit in LDS", (int)L, (long long)D);
+  if (M > kMaxExtent - 64) return fail(COALESCE_ERR_UNSUPPORTED, "M must be below 2^31 - 64");
+  if (M == 0) return ok();
+  if (!x || !out) return fail(COALESCE_ERR_INVALID_ARGUMENT, "x or out is NULL");
+  if (ldx < D || ldo < D) return fail(COALESCE_ERR_INVALID_ARGUMENT, "ldx/ldo shorter than the row");
+  if (!aligned16(x) || !aligned16(out) || (ldx * 2) % 16 || (ldo * 2) % 16)
+    return fail(COALESCE_ERR_UNSUPPORTED, "x and out must be 16-byte aligned with 16-byte row pitch");
+  const Range ro = span(out, M, D, ldo, 2);
+  if (overlap(ro, span(x, M, D, ldx, 2))) return fail(COALESCE_ERR_INVALID_ARGUMENT, "out overlaps x");
+  MlpParams p{};
+  for (int l = 0; l < L; ++l) {
+    if (!W[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W[%d] is NULL", l);
+    if (!aligned16(W[l])) return fail(COALESCE_ERR_UNSUPPORTED, "W[%d] must be 16-byte aligned", l);
+    if (overlap(ro, span(W[l], D, D, D, 2))) return fail(COALESCE_ERR_INVALID_ARGUMENT, "out overlaps W[%d]", l);
+    p.W[l] = W[l];
+  }
+  int cus = 0;
+  coalesce_status s = current_cus(&cus);
+  if (s != COALESCE_OK) return s;
+  p.x = x;
+  p.out = out;
+  p.ldx = ldx;
+  p.ldo = ldo;
+  p.M = (int)M;
+  const int64_t tiles = (M + mlp_tile_rows() - 1) / mlp_tile_rows();
+  p.num_tiles = (int)tiles;
+  int64_t nwg = num_workgroups;
+  if (nwg == 0) {
+    const int64_t per_wg = mlp_waves_per_workgroup();
+    const int64_t need = (tiles + per_wg - 1) / per_wg;
+    nwg = need < cus ? need : cus;  // one 8-wave workgroup per CU
+  }
+  if (nwg > (int64_t)INT32_MAX) return fail(COALESCE_ERR_UNSUPPORTED, "workgroup count too large");
+  hipError_t e = launch_mlp(p, (int)D, (int)L, act_code(hidden_act), (int)nwg, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "MLP launch");
+  return ok();
+}
+
+coalesce_status coalesce_mlp_forward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims, int32_t L,
+                                     void* out, int64_t ldo, int64_t M, coalesce_dtype dtype, coalesce_act hidden_act,
+                                     void* stream) {
+  return coalesce_mlp_forward_grid(x, ldx, W, dims, L, out, ldo, M, dtype, hidden_act, 0, stream);
+}
+
+static coalesce_status check_elementwise(const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t M, int64_t N,
+                                         int64_t es) {
+  if (M < 0 || N < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative extent");
+  if (M > kMaxExtent || N > kMaxExtent) return fail(COALESCE_ERR_UNSUPPORTED, "extents must be below 2^31");
+  if (M == 0 || N == 0) return COALESCE_OK;
+  if (!X || !Y) return fail(COALESCE_ERR_INVALID_ARGUMENT, "X or Y is NULL");
+  if (ldx < N || ldy < N) return fail(COALESCE_ERR_INVALID_ARGUMENT, "leading dimension shorter than the row");
+  if (!aligned16(X) || !aligned16(Y) || (ldx * es) % 16 || (ldy * es) % 16)
+    return fail(COALESCE_ERR_UNSUPPORTED, "X and Y must be 16-byte aligned with 16-byte row pitch");
+  if (X != Y && overlap(span(X, M, N, ldx, es), span(Y, M, N, ldy, es)))
+    return fail(COALESCE_ERR_INVALID_ARGUMENT, "X and Y overlap without being identical");
+  if (X == Y && ldx != ldy) return fail(COALESCE_ERR_INVALID_ARGUMENT, "in-place call with different pitches");
+  return COALESCE_OK;
+}
+
+coalesce_status coalesce_bias_add(const void* X, int64_t ldx, const void* bias, void* Y, int64_t ldy, int64_t M,
+                                  int64_t N, coalesce_dtype x_dtype, coalesce_dtype bias_dtype, coalesce_dtype y_dtype,
+                                  void* stream) {
+  if (!valid_dtype(x_dtype) || !valid_dtype(bias_dtype) || !valid_dtype(y_dtype))
+    return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (x_dtype != bias_dtype || x_dtype != y_dtype)
+    return fail(COALESCE_ERR_UNSUPPORTED, "bias_add needs one dtype for X, bias and Y");
+  coalesce_status s = check_elementwise(X, ldx, Y, ldy, M, N, dsize(x_dtype));
+  if (s != COALESCE_OK) return s;
+  if (M == 0 || N == 0) return ok();
+  if (!bias) return fail(COALESCE_ERR_INVALID_ARGUMENT, "bias is NULL");
+  int cus = 0;
+  s = current_cus(&cus);
+  if (s != COALESCE_OK) return s;
+  const DType dt = x_dtype == COALESCE_F32 ? DT_F32 : x_dtype == COALESCE_F16 ? DT_F16 : DT_BF16;
+  hipError_t e = launch_bias_add(X, ldx, bias, Y, ldy, (int)M, (int)N, dt, dt, dt, (hipStream_t)stream, cus);
+  if (e != hipSuccess) return device_fail(e, "bias_add launch");
+  return ok();
+}
+
+coalesce_status coalesce_activation(const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t M, int64_t N,
+                                    coalesce_dtype dtype, coalesce_act act, void* stream) {
+  if (!valid_dtype(dtype)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (!valid_act(act)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown activation");
+  coalesce_status s = check_elementwise(X, ldx, Y, ldy, M, N, dsize(dtype));
+  if (s != COALESCE_OK) return s;
+  if (M == 0 || N == 0) return ok();
+  int cus = 0;
+  s = current_cus(&cus);
+  if (s != COALESCE_OK) return s;
+  const DType dt = dtype == COALESCE_F32 ? DT_F32 : dtype == COALESCE_F16 ? DT_F16 : DT_BF16;
+  hipError_t e = launch_activation(X, ldx, Y, ldy, (int)M, (int)N, dt, act_code(act), (hipStream_t)stream, cus);
+  if (e != hipSuccess) return device_fail(e, "activation launch");
+  return ok();
+}
+
+coalesce_status coalesce_flush_caches(const void* buf, size_t bytes, void* sink, void* stream) {
+  if (bytes == 0) return ok();
+  if (!buf || !sink) return fail(COALESCE_ERR_INVALID_ARGUMENT, "buf or sink is NULL");
+  if (!aligned16(buf) || bytes % 16) return fail(COALESCE_ERR_UNSUPPORTED, "buf must be 16-byte aligned, bytes a multiple of 16");
+  int cus = 0;
+  coalesce_status s = current_cus(&cus);
+  if (s != COALESCE_OK) return s;
+  hipError_t e = launch_flush(buf, bytes, sink, (hipStream_t)stream, cus);
+  if (e != hipSuccess) return device_fail(e, "flush launch");
+  return ok();
+}
+
+int32_t coalesce_device_cu_count(void) {
+  int cus = 0;
+  if (current_cus(&cus) != COALESCE_OK) return -1;
+  return cus;
+}
+
+const char* coalesce_status_string(coalesce_status s) {
+  switch (s) {
+    case COALESCE_OK: return "COALESCE_OK";
+    case COALESCE_ERR_INVALID_ARGUMENT: return "COALESCE_ERR_INVALID_ARGUMENT";
+    case COALESCE_ERR_UNSUPPORTED: return "COALESCE_ERR_UNSUPPORTED";
+    case COALESCE_ERR_DEVICE: return "COALESCE_ERR_DEVICE";
+  }
+  return "COALESCE_ERR_UNKNOWN";
+}
+
+const char* coalesce_last_error(void) { return g_last_error; }
+
+int32_t coalesce_version(void) { return 100; }
+
+}  // extern "C"

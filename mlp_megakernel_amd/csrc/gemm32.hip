@@ -1,0 +1,253 @@
+// Fused GEMM + bias + activation for fp32 inputs on the gfx950 fp32 MFMA.
+//
+// Same method as the 16-bit kernel (bias and activation applied to the fp32
+// accumulators in registers, one store of Y), on v_mfma_f32_16x16x4_f32:
+//   * workgroup tile BM x BN (128 x 128, or 64 x 64 when the problem has too
+//     few 128 x 128 tiles to occupy the GPU), K step 32, 4 waves in a 2 x 2
+//     grid; each wave computes Y^T blocks (A operand = B^T, B operand = A^T)
+//     so each lane holds 4 consecutive n of one row m;
+//   * per 16-deep k group a wave reads its A^T operand as one 128-bit LDS read
+//     per 16 rows (4 consecutive k, one per MFMA) and its B^T operand as 32-bit
+//     reads; fp32 MFMA takes one k per lane, so no transpose is needed;
+//   * 2 LDS stages filled by 16-byte direct-to-LDS copies one K step ahead;
+//     2 workgroups per CU (64 KB of LDS each at 128 x 128).
+// The fp32 MFMA accumulates in fp32 with the hardware's own summation order,
+// which is the same for the fused kernel and for the same kernel run with
+// act = NONE and no bias (the unfused baseline's GEMM step), so the fused and
+// unfused results agree bit for bit.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace coalesce {
+namespace {
+
+constexpr int BK = 32, THREADS = 256;
+
+__device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// A tile: BM rows of 32 floats (8 chunks of 4); chunk c of row m at slot c ^ (m & 7).
+// B tile: 32 rows of BN floats (BN / 4 chunks); chunk c of row k at slot c ^ 4 ((k >> 2) & 1).
+__device__ __forceinline__ int swzA(int m) { return m & 7; }
+__device__ __forceinline__ int swzB(int k) { return ((k >> 2) & 1) << 2; }
+
+template <int BM, int BN>
+struct Cfg {
+  static constexpr int A_BLOCKS = BM * BK * 4 / 1024;  // 1 KB copies per stage for A
+  static constexpr int B_BLOCKS = BK * BN * 4 / 1024;
+  static constexpr int B_ROWS_PER_BLOCK = 1024 / (BN * 4);
+  static constexpr int B_CHUNKS = BN / 4;
+  static constexpr int WM = BM / 2, WN = BN / 2;  // wave tile
+  static constexpr int MT = WM / 16, NT = WN / 16;
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void fill_dma(const GemmParams& p, int m0, int n0, int k0, int nlast, float* sa, float* sb,
+                                         int wu, int lane) {
+  typedef Cfg<BM, BN> C;
+  const float* A = (const float*)p.A;
+  const float* B = (const float*)p.B;
+#pragma unroll
+  for (int j = 0; j < C::A_BLOCKS / 4; ++j) {
+    const int blk = wu * (C::A_BLOCKS / 4) + j;
+    const int row = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swzA(row);
+    const int gm = min(m0 + row, p.M - 1);
+    dma16(A + (int64_t)gm * p.lda + k0 + c * 4, lds_addr(sa) + blk * 1024);
+  }
+#pragma unroll
+  for (int j = 0; j < C::B_BLOCKS / 4; ++j) {
+    const int blk = wu * (C::B_BLOCKS / 4) + j;
+    const int row = blk * C::B_ROWS_PER_BLOCK + lane / C::B_CHUNKS;
+    const int c = (lane % C::B_CHUNKS) ^ swzB(row);
+    const int gn = min(n0 + c * 4, nlast);
+    dma16(B + (int64_t)(k0 + row) * p.ldb + gn, lds_addr(sb) + blk * 1024);
+  }
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void fill_tail(const GemmParams& p, int m0, int n0, int k0, int nlast, float* sa, float* sb,
+                                          int w, int lane) {
+  typedef Cfg<BM, BN> C;
+  const float* A = (const float*)p.A;
+  const float* B = (const float*)p.B;
+  f32x4 ra[C::A_BLOCKS / 4], rb[C::B_BLOCKS / 4];
+#pragma unroll
+  for (int j = 0; j < C::A_BLOCKS / 4; ++j) {
+    const int blk = w * (C::A_BLOCKS / 4) + j;
+    const int row = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swzA(row);
+    const int gm = min(m0 + row, p.M - 1);
+    const int k = k0 + c * 4;
+    f32x4 v = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (k < p.K) {
+      v = *(const f32x4*)(A + (int64_t)gm * p.lda + k);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (k + e >= p.K) v[e] = 0.f;
+    }
+    ra[j] = v;
+  }
+#pragma unroll
+  for (int j = 0; j < C::B_BLOCKS / 4; ++j) {
+    const int blk = w * (C::B_BLOCKS / 4) + j;
+    const int row = blk * C::B_ROWS_PER_BLOCK + lane / C::B_CHUNKS;
+    const int c = (lane % C::B_CHUNKS) ^ swzB(row);
+    const int gn = min(n0 + c * 4, nlast);
+    f32x4 v = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if (k0 + row < p.K) v = *(const f32x4*)(B + (int64_t)(k0 + row) * p.ldb + gn);
+    rb[j] = v;
+  }
+#pragma unroll
+  for (int j = 0; j < C::A_BLOCKS / 4; ++j) *(f32x4*)(sa + (w * (C::A_BLOCKS / 4) + j) * 256 + lane * 4) = ra[j];
+#pragma unroll
+  for (int j = 0; j < C::B_BLOCKS / 4; ++j) *(f32x4*)(sb + (w * (C::B_BLOCKS / 4) + j) * 256 + lane * 4) = rb[j];
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void compute_stage(const float* sa, const float* sb, f32x4 (&acc)[Cfg<BM, BN>::NT][Cfg<BM, BN>::MT],
+                                              int wm, int wn, int lane) {
+  typedef Cfg<BM, BN> C;
+  const int q = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kg = 0; kg < BK / 16; ++kg) {
+    f32x4 a4[C::MT];
+#pragma unroll
+    for (int s = 0; s < C::MT; ++s) {
+      const int m = wm * C::WM + 16 * s + q;
+      const int c = (4 * kg + g) ^ swzA(m);
+      a4[s] = *(const f32x4*)(sa + m * BK + c * 4);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int k = 16 * kg + 4 * g + e;
+      float bt[C::NT];
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t) {
+        const int n = wn * C::WN + 16 * t + q;
+        bt[t] = sb[k * BN + ((((n >> 2) ^ swzB(k))) << 2) + (n & 3)];
+      }
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int s = 0; s < C::MT; ++s) acc[t][s] = mfma16x16x4(bt[t], a4[s][e], acc[t][s]);
+    }
+  }
+}
+
+template <int BM, int BN, int ACT, bool HAS_BIAS>
+__global__ __launch_bounds__(THREADS, 2) void gemm32_kernel(GemmParams p) {
+  typedef Cfg<BM, BN> C;
+  __shared__ __attribute__((aligned(1024))) float sA0[BM * BK];
+  __shared__ __attribute__((aligned(1024))) float sB0[BK * BN];
+  __shared__ __attribute__((aligned(1024))) float sA1[BM * BK];
+  __shared__ __attribute__((aligned(1024))) float sB1[BK * BN];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int wm = w & 1, wn = w >> 1;
+  const int nlast = ((p.N - 1) >> 2) << 2;
+
+  f32x4 acc[C::NT][C::MT];
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+    for (int s = 0; s < C::MT; ++s) acc[t][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int kfull = p.K / BK;
+  const int ktiles = (p.K + BK - 1) / BK;
+  if (ktiles > 0) {
+    if (kfull > 0)
+      fill_dma<BM, BN>(p, m0, n0, 0, nlast, sA0, sB0, wu, lane);
+    else
+      fill_tail<BM, BN>(p, m0, n0, 0, nlast, sA0, sB0, wu, lane);
+  }
+  for (int kt = 0; kt < ktiles; kt += 2) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int k = kt + half;
+      if (k < ktiles) {
+        float* ca = half ? sA1 : sA0;
+        float* cb = half ? sB1 : sB0;
+        float* na = half ? sA0 : sA1;
+        float* nb = half ? sB0 : sB1;
+        wait_vmcnt0();
+        __syncthreads();
+        if (k + 1 < ktiles) {
+          if (k + 1 < kfull)
+            fill_dma<BM, BN>(p, m0, n0, (k + 1) * BK, nlast, na, nb, wu, lane);
+          else
+            fill_tail<BM, BN>(p, m0, n0, (k + 1) * BK, nlast, na, nb, wu, lane);
+        }
+        compute_stage<BM, BN>(ca, cb, acc, wm, wn, lane);
+      }
+    }
+  }
+
+  const int q = lane & 15, g = lane >> 4;
+  const float* bias = (const float*)p.bias;
+  float* Y = (float*)p.Y;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t) {
+    const int n = n0 + wn * C::WN + 16 * t + 4 * g;
+    if (n >= p.N) continue;
+    const int valid = min(4, p.N - n);
+    f32x4 bv = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if constexpr (HAS_BIAS) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bv[r] = r < valid ? bias[n + r] : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < C::MT; ++s) {
+      const int m = m0 + wm * C::WM + 16 * s + q;
+      if (m < p.M) {
+        f32x4 v = acc[t][s];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = apply_act<ACT>(v[r] + bv[r]);
+        float* dst = Y + (int64_t)m * p.ldy + n;
+        if (valid == 4) {
+          *(f32x4*)dst = v;
+        } else {
+          for (int r = 0; r < valid; ++r) dst[r] = v[r];
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int ACT>
+hipError_t launch_cfg(GemmParams p, hipStream_t stream) {
+  p.tiles_m = (p.M + BM - 1) / BM;
+  p.tiles_n = (p.N + BN - 1) / BN;
+  p.group_m = 8;
+  dim3 grid(p.tiles_m * p.tiles_n), block(THREADS);
+  if (p.bias)
+    hipLaunchKernelGGL((gemm32_kernel<BM, BN, ACT, true>), grid, block, 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm32_kernel<BM, BN, ACT, false>), grid, block, 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_act(GemmParams p, int act, hipStream_t stream) {
+  switch (act) {
+    case ACT_GELU: return launch_cfg<BM, BN, ACT_GELU>(p, stream);
+    case ACT_SOFTPLUS: return launch_cfg<BM, BN, ACT_SOFTPLUS>(p, stream);
+    default: return launch_cfg<BM, BN, ACT_NONE>(p, stream);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm32(GemmParams p, int act, hipStream_t stream, int num_cus) {
+  // 128 x 128 tiles when they give at least one workgroup per CU, else 64 x 64.
+  const long tiles128 = (long)((p.M + 127) / 128) * ((p.N + 127) / 128);
+  if (tiles128 >= num_cus) return launch_act<128, 128>(p, act, stream);
+  return launch_act<64, 64>(p, act, stream);
+}
+
+}  // namespace coalesce

@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI that need no GPU.
+
+The library must load and export every entry point declared in
+include/coalesce.h, and every invalid or unsupported request must be
+rejected on the host, before any device call, with the documented status
+(so these run with fake pointer values and no GPU present).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mlp_megakernel_amd as mk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "coalesce.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(coalesce_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared() == sorted(mk.SIGNATURES), "binding signatures must cover exactly the header's entry points"
+
+
+def test_library_exports_every_symbol():
+    lib = mk.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert lib.coalesce_version() == 100
+    assert lib.coalesce_status_string(2) == b"COALESCE_ERR_UNSUPPORTED"
+
+
+P = 0x10000  # a 16-byte aligned fake device address; never dereferenced
+INV, UNS = mk.ERR_INVALID_ARGUMENT, mk.ERR_UNSUPPORTED
+
+
+def gemm(**kw):
+    a = dict(A=P, lda=64, B=P * 2, ldb=64, bias=None, Y=P * 4, ldy=64, M=8, N=64, K=64, i=mk.F32, o=mk.F32,
+             act=mk.ACT_GELU_ERF)
+    a.update(kw)
+    lib = mk.load_library()
+    return lib.coalesce_gemm_bias_act(a["A"], a["lda"], a["B"], a["ldb"], a["bias"], a["Y"], a["ldy"], a["M"],
+                                      a["N"], a["K"], a["i"], a["o"], a["act"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(M=-1), INV), (dict(N=-3), INV), (dict(K=-2), INV),
+    (dict(i=7), INV), (dict(act=9), INV),
+    (dict(Y=None), INV), (dict(A=None), INV), (dict(B=None), INV),
+    (dict(lda=63), INV), (dict(ldb=10), INV), (dict(ldy=60), INV),
+    (dict(i=mk.F32, o=mk.BF16), UNS), (dict(i=mk.BF16, o=mk.F16), UNS), (dict(i=mk.F16, o=mk.BF16), UNS),
+    (dict(A=P + 4), UNS), (dict(Y=P + 8), UNS), (dict(bias=P * 8 + 2), UNS),
+    (dict(lda=66), UNS), (dict(ldy=65), UNS),
+    (dict(M=1 << 31), UNS),
+    (dict(Y=P + 256), INV),  # Y overlaps A
+])
+def test_gemm_rejects_before_launch(kw, status):
+    assert gemm(**kw) == status
+    assert len(mk.load_library().coalesce_last_error()) > 0
+
+
+def test_gemm_empty_is_ok_without_device():
+    assert gemm(M=0) == mk.OK
+    assert gemm(N=0, Y=None) == mk.OK
+
+
+def mlp(D=128, L=3, dims=None, **kw):
+    lib = mk.load_library()
+    dims = dims if dims is not None else [D] * (L + 1)
+    W = (ctypes.c_void_p * max(L, 1))(*[P * (16 + l) for l in range(L)])
+    d = (ctypes.c_int64 * len(dims))(*dims)
+    a = dict(x=P, ldx=D, out=P * 64, ldo=D, M=100, dt=mk.F16, act=mk.ACT_SOFTPLUS, g=0)
+    a.update(kw)
+    return lib.coalesce_mlp_forward_grid(a["x"], a["ldx"], ctypes.cast(W, ctypes.c_void_p),
+                                         ctypes.cast(d, ctypes.c_void_p), L, a["out"], a["ldo"], a["M"], a["dt"],
+                                         a["act"], a["g"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), INV), (dict(M=-1), INV), (dict(g=-1), INV), (dict(dt=5), INV), (dict(act=4), INV),
+    (dict(x=None), INV), (dict(out=None), INV), (dict(ldx=100), INV), (dict(ldo=127), INV),
+    (dict(dt=mk.BF16), UNS), (dict(act=mk.ACT_GELU_ERF), UNS),
+    (dict(D=96), UNS), (dict(D=128, L=5), UNS), (dict(D=64, L=9), UNS),
+    (dict(dims=[128, 64, 128, 128]), UNS),
+    (dict(x=P + 2), UNS), (dict(ldx=132), UNS),
+])
+def test_mlp_rejects_before_launch(kw, status):
+    assert mlp(**kw) == status
+
+
+def test_mlp_empty_batch_is_ok():
+    assert mlp(M=0, x=None, out=None) == mk.OK
+
+
+def test_elementwise_and_flush_reject():
+    lib = mk.load_library()
+    assert lib.coalesce_bias_add(P, 64, P * 2, P * 4, 64, 4, 64, mk.F32, mk.F16, mk.F32, None) == UNS
+    assert lib.coalesce_bias_add(P, 64, None, P * 4, 64, 4, 64, mk.F32, mk.F32, mk.F32, None) == INV
+    assert lib.coalesce_activation(P, 32, P * 4, 64, 4, 64, mk.F32, mk.ACT_GELU_ERF, None) == INV
+    assert lib.coalesce_activation(P, 64, P + 64, 64, 4, 64, mk.F32, mk.ACT_GELU_ERF, None) == INV
+    assert lib.coalesce_flush_caches(P + 4, 1024, P, None) == UNS
+    assert lib.coalesce_flush_caches(None, 1024, P, None) == INV
+    assert lib.coalesce_flush_caches(None, 0, None, None) == mk.OK
