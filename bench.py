@@ -1,0 +1,343 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused GEMM epilogue and the MLP megakernel on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  The primary workload (default: the bf16 FFN
+up-projection, M=8192 tokens, K=4096, N=16384, + bias + GELU(erf)) is timed
+as K back-to-back steps bracketed by device synchronisation, each step one
+coalesce_gemm_bias_act call on inputs already resident in HBM; `value` is its
+TFLOP/s.  The same line carries
+
+  * roofline: the dominant kernel's algorithmic FLOPs per launch divided by
+    its mean duration from HIP events recorded on the launch stream;
+  * mlp: rows/s of the 3-layer (D=128, 2^20 rows) and 5-layer (D=64, 2^22
+    rows) softplus megakernels, timed the same way, with their HBM roofline;
+  * pages_harness: the "Coalesce" README's timing method for every workload
+    -- >= 1 s of warm-up, then 100 runs each preceded by a 512 MiB cache
+    flush and bracketed by their own event pair, median / p10 / p90 -- for
+    the fused kernel and for the unfused GEMM -> bias -> activation baseline
+    (per-layer GEMM -> softplus for the MLPs);
+  * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
+    sample of the primary workload.
+All inputs are synthetic and seeded (datagen).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "fused GEMM+bias+GELU TFLOP/s & % MFMA peak; MLP megakernel rows/sec"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+FLUSH_BYTES = 512 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="bf16_ffn_up_gelu")
+    ap.add_argument("--no-harness", action="store_true", help="skip the flushed median-of-100 sweep")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mlp", action="store_true")
+    ap.add_argument("--harness-iters", type=int, default=100)
+    ap.add_argument("--harness-warmup-ms", type=float, default=1000.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-traffic", action="store_true",
+                    help="also run a known-size read sweep and a known-size read+write kernel "
+                         "(for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the workloads shard by rows with no exchange "
+              "(see DESIGN.md), but multi-GPU runs are not part of it. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import datagen
+    import mlp_megakernel_amd as mk
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    mk.load_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    flush_buf = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    flush_buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+
+    def flush():
+        mk.flush_caches(flush_buf, sink)
+
+    # ------------------------------------------------------------------ inputs
+    def gemm_case(w):
+        A, B, bias = datagen.gemm_inputs(w)
+        A, B, bias = A.to(dev), B.to(dev), bias.to(dev)
+        odt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w.out_dtype]
+        Y = torch.empty((w.M, w.N), dtype=odt, device=dev)
+        Z = torch.empty((w.M, w.N), dtype=A.dtype, device=dev)
+        Z2 = torch.empty((w.M, w.N), dtype=A.dtype, device=dev)
+        Yu = torch.empty((w.M, w.N), dtype=A.dtype, device=dev)
+
+        def fused():
+            mk.gemm_bias_act(A, B, bias, act=w.act, out=Y)
+
+        def unfused():
+            mk.gemm_bias_act(A, B, None, act="none", out=Z)
+            mk.bias_add(Z, bias, out=Z2)
+            mk.activation(Z2, w.act, out=Yu)
+
+        return fused, unfused
+
+    def mlp_case(w):
+        x, Ws = datagen.mlp_inputs(w)
+        x = x.to(dev)
+        Ws = [t.to(dev) for t in Ws]
+        out = torch.empty((w.M, w.dims[-1]), dtype=torch.float16, device=dev)
+        hs = [torch.empty((w.M, d), dtype=torch.float16, device=dev) for d in w.dims[1:]]
+        hs2 = [torch.empty((w.M, d), dtype=torch.float16, device=dev) for d in w.dims[1:]]
+
+        def fused():
+            mk.mlp_forward(x, Ws, out=out)
+
+        def unfused():
+            h = x
+            for l, Wl in enumerate(Ws):
+                mk.gemm_bias_act(h, Wl, None, act="none", out=hs[l])
+                h = hs[l]
+                if l < w.L - 1:
+                    mk.activation(h, "softplus", out=hs2[l])
+                    h = hs2[l]
+
+        return fused, unfused
+
+    # ----------------------------------------------------------------- timing
+    def timed_steps(fn, steps, warmup):
+        """K back-to-back steps; wall time and per-launch event durations."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = [a.elapsed_time(b) for a, b in ev]
+        return wall * 1e3 / steps, float(np.mean(kern)), kern
+
+    def pages_harness(fn):
+        """>= warmup_ms of continuous GPU work, then N x {flush, event, fn, event}; median."""
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        spent, reps = 0.0, 1
+        while spent < args.harness_warmup_ms:
+            s.record(stream)
+            for _ in range(reps):
+                fn()
+            e.record(stream)
+            e.synchronize()
+            spent += s.elapsed_time(e)
+            reps = min(reps * 2, 256)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.harness_iters)]
+        for a, b in ev:
+            flush()
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        t = np.array([a.elapsed_time(b) for a, b in ev])
+        return {"median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
+                "p90_ms": float(np.percentile(t, 90)), "iters": int(args.harness_iters)}
+
+    def roofline_gemm(w, mean_ms):
+        flops = w.flops()
+        ach = flops / (mean_ms * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[w.in_dtype]
+        return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": measured_traffic("gemm16_kernel/" + w.name), "kernel": "gemm16_kernel" if w.in_dtype != "f32"
+                else "gemm32_kernel", "algorithmic_flop_per_launch": flops,
+                "algorithmic_bytes_per_launch": w.bytes(), "mean_launch_ms": round(mean_ms, 5)}
+
+    def roofline_mlp(w, mean_ms):
+        by = w.bytes()
+        ach = by / (mean_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("mlp_kernel/" + w.name),
+                "kernel": "mlp_kernel",
+                "algorithmic_bytes_per_launch": by, "algorithmic_flop_per_launch": w.flops(),
+                "mfma_tflops": round(w.flops() / (mean_ms * 1e-3) / 1e12, 2), "mean_launch_ms": round(mean_ms, 5)}
+
+    result = {}
+    prim = datagen.WORKLOADS[args.workload]
+    is_mlp = isinstance(prim, datagen.MlpWorkload)
+
+    # -------------------------------------------------------- primary workload
+    print("bench: generating %s" % prim.name, file=sys.stderr, flush=True)
+    fused, unfused = (mlp_case if is_mlp else gemm_case)(prim)
+    ms_step, mean_kernel_ms, _ = timed_steps(fused, args.steps, args.warmup)
+    if is_mlp:
+        value = prim.M / (ms_step * 1e-3)
+        unit, dtype = "rows/s", "f16"
+        roof = roofline_mlp(prim, mean_kernel_ms)
+        cfg = {"workload": prim.name, "rows": prim.M, "dims": list(prim.dims), "hidden_act": "softplus"}
+    else:
+        value = prim.flops() / (ms_step * 1e-3) / 1e12
+        unit, dtype = "TFLOP/s", prim.in_dtype
+        roof = roofline_gemm(prim, mean_kernel_ms)
+        cfg = {"workload": prim.name, "M": prim.M, "N": prim.N, "K": prim.K, "act": "gelu_erf",
+               "in_dtype": prim.in_dtype, "out_dtype": prim.out_dtype, "accumulate": "f32"}
+    cfg["description"] = prim.description
+    result.update({"metric": METRIC, "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": args.steps,
+                   "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+                   "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": cfg})
+    if not is_mlp:
+        result["pct_mfma_peak"] = round(100.0 * value / PEAK_TFLOPS[prim.in_dtype], 2)
+    result["roofline"] = roof
+    harness = {}
+    if not args.no_harness:
+        print("bench: pages harness %s" % prim.name, file=sys.stderr, flush=True)
+        hf, hu = pages_harness(fused), pages_harness(unfused)
+        harness[prim.name] = {"fused": hf, "unfused": hu, "fused_speedup": round(hu["median_ms"] / hf["median_ms"], 4)}
+        if not is_mlp:
+            harness[prim.name]["fused_tflops"] = round(prim.flops() / (hf["median_ms"] * 1e-3) / 1e12, 2)
+    del fused, unfused
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------- MLP metrics
+    if not args.no_mlp:
+        mlp_res = {}
+        for w in (datagen.MLP3, datagen.MLP5):
+            if w.name == prim.name:
+                continue
+            print("bench: %s" % w.name, file=sys.stderr, flush=True)
+            f, u = mlp_case(w)
+            ms, mk_ms, _ = timed_steps(f, max(10, args.steps // 2), 5)
+            mlp_res[w.name] = {"rows_per_s": round(w.M / (ms * 1e-3), 1), "ms_per_call": round(ms, 5),
+                               "roofline": roofline_mlp(w, mk_ms)}
+            if not args.no_harness:
+                hf, hu = pages_harness(f), pages_harness(u)
+                harness[w.name] = {"fused": hf, "unfused": hu, "rows_per_s": round(w.M / (hf["median_ms"] * 1e-3), 1),
+                                   "fused_speedup": round(hu["median_ms"] / hf["median_ms"], 4)}
+            del f, u
+            torch.cuda.empty_cache()
+        result["mlp"] = mlp_res
+        if datagen.MLP3.name in mlp_res:
+            result["mlp_rows_per_sec"] = mlp_res[datagen.MLP3.name]["rows_per_s"]
+
+    # ------------------------------------------- the other GEMM workloads (harness)
+    if not args.no_harness:
+        for name in ("fp32_gemm_gelu_512", "fp32_gemm_gelu_1024", "fp32_gemm_gelu_2048", "fp32_gemm_gelu_4096",
+                     "bf16_ffn_up_gelu"):
+            w = datagen.WORKLOADS[name]
+            if name == prim.name:
+                continue
+            print("bench: pages harness %s" % name, file=sys.stderr, flush=True)
+            f, u = gemm_case(w)
+            hf, hu = pages_harness(f), pages_harness(u)
+            harness[name] = {"fused": hf, "unfused": hu, "fused_speedup": round(hu["median_ms"] / hf["median_ms"], 4),
+                             "fused_tflops": round(w.flops() / (hf["median_ms"] * 1e-3) / 1e12, 2),
+                             "pct_peak": round(100 * w.flops() / (hf["median_ms"] * 1e-3) / 1e12 /
+                                               PEAK_TFLOPS[w.in_dtype], 2)}
+            del f, u
+            torch.cuda.empty_cache()
+        result["pages_harness"] = harness
+
+    if args.calibrate_traffic:
+        # Known-size kernels for scaling the FETCH_SIZE / WRITE_SIZE counters:
+        # the flush sweep reads exactly 512 MiB; the activation kernel on a
+        # 256 MiB fp16 tensor reads 256 MiB and writes 256 MiB.
+        print("bench: traffic calibration kernels", file=sys.stderr, flush=True)
+        flush()
+        t = torch.zeros((8192, 16384), dtype=torch.float16, device=dev)
+        mk.activation(t, "none", out=torch.empty_like(t))
+        torch.cuda.synchronize()
+        result["traffic_calibration"] = {"flush_read_bytes": FLUSH_BYTES, "activation_read_bytes": t.numel() * 2,
+                                         "activation_write_bytes": t.numel() * 2}
+
+    # ------------------------------------------------------------ CPU baseline
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(prim, args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def measured_traffic(key):
+    """HBM bytes per launch from the committed counter runs (profiles/traffic.json),
+    or None when the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            entry = json.load(f).get(key)
+        if not entry:
+            return None
+        h = hashlib.sha256()
+        for src in entry["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != entry["source_sha256"]:
+            return None
+        return float(entry["fetch_bytes"]) + float(entry["write_bytes"])
+    except (OSError, ValueError, KeyError):
+        return None
+
+
+def cpu_baseline(w, target_s):
+    """Time the fp64 oracle (as it stands) on a bounded row sample of workload w."""
+    import numpy as np
+
+    import datagen
+    import oracle
+
+    threads = oracle.max_threads()
+    if isinstance(w, datagen.MlpWorkload):
+        x, Ws = datagen.mlp_inputs(w)
+        x64 = datagen.to_f64(x[: 1 << 16])
+        W64 = [datagen.to_f64(t) for t in Ws]
+        rows = 4096
+        while True:
+            t0 = time.perf_counter()
+            oracle.mlp_forward(x64[:rows], W64)
+            dt = time.perf_counter() - t0
+            if dt * 2 >= target_s or rows >= x64.shape[0]:
+                break
+            rows = min(x64.shape[0], int(rows * max(2.0, target_s / max(dt, 1e-3) * 0.9)))
+        return {"value": round(rows / dt, 1), "unit": "rows/s", "cores": threads, "kind": "oracle",
+                "sample": "%d of %d rows of %s, fp64 naive loops, %.1f s" % (rows, w.M, w.name, dt)}
+    A, B, bias = datagen.gemm_inputs(w)
+    A64, B64, b64 = datagen.to_f64(A), datagen.to_f64(B), datagen.to_f64(bias)
+    rows = max(1, threads)
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm_bias_act(A64, B64, b64, act="gelu", rows=np.arange(rows))
+        dt = time.perf_counter() - t0
+        if dt * 2 >= target_s or rows >= w.M:
+            break
+        rows = min(w.M, int(rows * max(2.0, target_s / max(dt, 1e-3) * 0.9)))
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d of %d rows of %s (all %d columns), fp64 naive triple loop, %.1f s"
+                      % (rows, w.M, w.name, w.N, dt)}
+
+
+if __name__ == "__main__":
+    main()
