@@ -67,7 +67,8 @@ typedef enum {
  * Accumulation is fp32 (fp32 MFMA for F32 inputs, bf16/fp16 MFMA otherwise);
  * bias and activation are computed in fp32; the store rounds to nearest even.
  * Supported (in_dtype -> out_dtype): F32->F32, BF16->BF16, BF16->F32,
- * F16->F16, F16->F32.  M, N, K must be below 2^31; M == 0 or N == 0 is a
+ * F16->F16, F16->F32.  M, N, K must be below 2^31 (and, for 16-bit inputs,
+ * lda <= 2^23, ldb <= 2^25); M == 0 or N == 0 is a
  * no-op; K == 0 gives Y = act(bias) (act(0) without a bias), and A, B may
  * then be NULL.  Y must not overlap A, B or bias.
  */

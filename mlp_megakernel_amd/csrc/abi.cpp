@@ -109,6 +109,10 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
     if (!aligned16(A) || !aligned16(B)) return fail(COALESCE_ERR_UNSUPPORTED, "A and B must be 16-byte aligned");
     if ((lda * is) % 16 || (ldb * is) % 16)
       return fail(COALESCE_ERR_UNSUPPORTED, "lda and ldb must span a multiple of 16 bytes");
+    // the 16-bit kernel addresses a 256-row A tile and a 64-row B slab with
+    // 32-bit byte offsets
+    if (is == 2 && (lda > (int64_t(1) << 23) || ldb > (int64_t(1) << 25)))
+      return fail(COALESCE_ERR_UNSUPPORTED, "16-bit inputs need lda <= 2^23 and ldb <= 2^25");
   }
   if (!aligned16(Y) || (ldy * os) % 16)
     return fail(COALESCE_ERR_UNSUPPORTED, "Y must be 16-byte aligned with ldy spanning a multiple of 16 bytes");

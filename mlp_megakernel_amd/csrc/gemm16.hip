@@ -2,22 +2,29 @@
 //
 // Y = act(A . B + bias) ("Coalesce" README, "Fusion study"): the bias add and
 // the activation run on the fp32 accumulators in registers and Y is written
-// once.  Tile plan (hand-budgeted against the 512 VGPRs a lane has when one
-// wave runs per SIMD):
+// once.  Tile plan (hand-budgeted against the 512 registers a lane has when
+// one wave runs per SIMD):
 //   * workgroup tile 256 (m) x 256 (n), K step 64, 4 waves in a 2 x 2 grid,
 //     each wave owning a 128 x 128 block of Y;
 //   * the wave computes Y^T blocks with v_mfma_f32_16x16x32 -- A operand =
 //     B^T (rows n), B operand = A^T (columns m) -- so every lane ends up with
 //     4 consecutive n of one row m, which makes bias loads and Y stores
 //     contiguous;
-//   * accumulators: 8 x 8 sub-tiles x 4 fp32 = 256 registers; operand
-//     fragments for one 32-deep k slice: 8 + 8 x 4 = 64 registers;
-//   * global -> LDS copies are 16-byte direct-to-LDS loads (no VGPR staging),
-//     double-buffered (2 x 64 KB of the 160 KB LDS), issued one K step ahead;
+//   * accumulators: 8 x 8 sub-tiles x 4 fp32 = 256 registers (AGPRs); operand
+//     fragments for one 32-deep k slice: 8 + 8 x 4 = 64 registers, double
+//     buffered;
+//   * global -> LDS copies are 16-byte direct-to-LDS loads (no VGPR staging)
+//     addressed as an SGPR base plus a per-lane 32-bit offset fixed for the
+//     whole tile; two LDS stages of 64 KB; K step k + 2 is copied while step
+//     k + 1 is consumed;
 //   * B is K x N with n contiguous, so its MFMA fragments (8 consecutive k of
 //     one n) come from the transposing LDS read ds_read_b64_tr_b16;
-//   * LDS rows are XOR-swizzled in 16-byte chunks so that the fragment reads
-//     spread over the banks.
+//   * LDS rows are XOR-swizzled in 16-byte chunks so that fragment reads
+//     spread over the banks;
+//   * each 32-deep slice is issued as 8 groups of {2 copies, 3 fragment reads
+//     of the next slice, 8 MFMAs}, fenced so the compiler keeps that
+//     interleave: the copies never arrive as a burst that stalls the wave's
+//     in-order issue, and the MFMA pipe is fed between them.
 // The last, partial K step (K not a multiple of 64) goes through masked
 // register loads that zero every element past K.  Rows past M read a
 // clamped (valid) row and are never stored; columns past N are masked.
@@ -40,49 +47,100 @@ struct Stage {
   T* b;
 };
 
-// Direct-to-LDS copy of the full K step starting at k0.  Wave w fills A rows
-// [64 w, 64 w + 64) (8 copies of 8 rows) and B rows [16 w, 16 w + 16) (8
-// copies of 2 rows); each copy is one 1 KB LDS block, lane l's 16 bytes going
-// to slot l of the block.
+// Per-lane byte offsets of the 16 direct copies of one K step, relative to
+// the tile's A base (A + m0 * lda + k0) and B base (B + n0 + k0 * ldb).
+// Copy j < 8 fills A rows 64 w + 8 j .. + 7 (one 1 KB LDS block, lane l's 16
+// bytes at slot l); copy 8 + j fills B rows 16 w + 2 j, + 1.
+struct DmaPlan {
+  uint32_t a[8];
+  uint32_t b[8];
+};
+
 template <typename T>
-__device__ __forceinline__ void issue_dma(const GemmParams& p, int m0, int n0, int k0, int nlast, Stage<T> st,
-                                          int w_uniform, int lane) {
-  const T* A = (const T*)p.A;
-  const T* B = (const T*)p.B;
+__device__ __forceinline__ DmaPlan make_plan(const GemmParams& p, int m0, int n0, int w, int lane) {
+  DmaPlan d;
   const int rsub = lane >> 3;
   const int cA = (lane & 7) ^ swzA(rsub);
-  const uint32_t a_base = lds_addr(st.a) + (uint32_t)w_uniform * (64 * BK * (int)sizeof(T));
-  const uint32_t b_base = lds_addr(st.b) + (uint32_t)w_uniform * (16 * BN * (int)sizeof(T));
+  const int nlast = ((p.N - 1) >> 3) << 3;
+  // 32-bit arithmetic is exact here: the host checks 256 * lda and 64 * ldb
+  // bytes fit in 32 bits.
+  const uint32_t lda_b = (uint32_t)p.lda * (uint32_t)sizeof(T);
+  const uint32_t ldb_b = (uint32_t)p.ldb * (uint32_t)sizeof(T);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    int row = w_uniform * 64 + j * 8 + rsub;
-    int gm = min(m0 + row, p.M - 1);
-    dma16(A + (int64_t)gm * p.lda + k0 + cA * 8, a_base + j * (8 * BK * (int)sizeof(T)));
+    const int gm = min(m0 + w * 64 + j * 8 + rsub, p.M - 1);
+    d.a[j] = (uint32_t)(gm - m0) * lda_b + (uint32_t)(cA * 8 * (int)sizeof(T));
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    int row = w_uniform * 16 + j * 2 + (lane >> 5);
-    int cB = (lane & 31) ^ swzB(row);
-    int gn = min(n0 + cB * 8, nlast);
-    dma16(B + (int64_t)(k0 + row) * p.ldb + gn, b_base + j * (2 * BN * (int)sizeof(T)));
+    const int row = w * 16 + j * 2 + (lane >> 5);
+    const int cB = (lane & 31) ^ swzB(row);
+    const int gn = min(n0 + cB * 8, nlast);
+    d.b[j] = (uint32_t)row * ldb_b + (uint32_t)((gn - n0) * (int)sizeof(T));
   }
+  return d;
+}
+
+// Uniform (SGPR) 64-bit base for a direct copy.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16-byte direct copy: global (SGPR base + per-lane 32-bit offset) -> LDS
+// (wave-uniform byte address + 16 * lane).
+__device__ __forceinline__ void dma16_off(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Copy j (0..15) of K step k into stage st.
+template <typename T>
+__device__ __forceinline__ void dma_copy(int j, const DmaPlan& d, const void* abase, const void* bbase, Stage<T> st,
+                                         int wu) {
+  if (j < 8)
+    dma16_off(abase, d.a[j], lds_addr(st.a) + (uint32_t)(wu * 64 + j * 8) * (BK * (int)sizeof(T)));
+  else
+    dma16_off(bbase, d.b[j - 8], lds_addr(st.b) + (uint32_t)(wu * 16 + (j - 8) * 2) * (BN * (int)sizeof(T)));
+}
+
+template <typename T>
+__device__ __forceinline__ const void* a_base(const GemmParams& p, int m0, int k0) {
+  return uniform_ptr((const T*)p.A + (int64_t)m0 * p.lda + k0);
+}
+template <typename T>
+__device__ __forceinline__ const void* b_base(const GemmParams& p, int n0, int k0) {
+  return uniform_ptr((const T*)p.B + (int64_t)k0 * p.ldb + n0);
+}
+
+// All 16 copies of a full K step at once (prologue only).
+template <typename T>
+__device__ __forceinline__ void dma_all(const GemmParams& p, const DmaPlan& d, int m0, int n0, int k0, Stage<T> st,
+                                        int wu) {
+  const void* ab = a_base<T>(p, m0, k0);
+  const void* bb = b_base<T>(p, n0, k0);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) dma_copy<T>(j, d, ab, bb, st, wu);
 }
 
 // Partial last K step: masked loads (elements at k >= K become 0), written to
 // the same LDS slots the direct copies would use.
 template <typename T>
-__device__ __forceinline__ void tail_fill(const GemmParams& p, int m0, int n0, int k0, int nlast, Stage<T> st, int w,
-                                          int lane) {
+__device__ __forceinline__ void tail_fill(const GemmParams& p, int m0, int n0, int k0, Stage<T> st, int w, int lane) {
   const T* A = (const T*)p.A;
   const T* B = (const T*)p.B;
   const int rsub = lane >> 3;
   const int cA = (lane & 7) ^ swzA(rsub);
   const int kA = k0 + cA * 8;
+  const int nlast = ((p.N - 1) >> 3) << 3;
   i16x8 ra[8], rb[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    int row = w * 64 + j * 8 + rsub;
-    int gm = min(m0 + row, p.M - 1);
+    const int gm = min(m0 + w * 64 + j * 8 + rsub, p.M - 1);
     i16x8 v = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
     if (kA < p.K) {
       v = *(const i16x8*)(A + (int64_t)gm * p.lda + kA);
@@ -94,9 +152,9 @@ __device__ __forceinline__ void tail_fill(const GemmParams& p, int m0, int n0, i
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    int row = w * 16 + j * 2 + (lane >> 5);
-    int cB = (lane & 31) ^ swzB(row);
-    int gn = min(n0 + cB * 8, nlast);
+    const int row = w * 16 + j * 2 + (lane >> 5);
+    const int cB = (lane & 31) ^ swzB(row);
+    const int gn = min(n0 + cB * 8, nlast);
     i16x8 v = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
     if (k0 + row < p.K) v = *(const i16x8*)(B + (int64_t)(k0 + row) * p.ldb + gn);
     rb[j] = v;
@@ -107,62 +165,71 @@ __device__ __forceinline__ void tail_fill(const GemmParams& p, int m0, int n0, i
   for (int j = 0; j < 8; ++j) *(i16x8*)(st.b + (w * 16 + j * 2) * BN + lane * 8) = rb[j];
 }
 
+// Operand fragments of one 32-deep k slice (ks = 0 or 1 of a stage):
+//   bf[s]: B operand = A^T, rows m = 128 wm + 16 s + (lane & 15), k = 8 (lane >> 4) + e;
+//   af[t]: A operand = B^T, rows n = 128 wn + 16 t + (lane & 15), same k, as two
+//          transposing reads of 4 k (lo: e = 0..3, hi: e = 4..7).
+struct Frags {
+  i16x8 a[8];
+  i16x8 b[8];
+};
+
 template <typename T>
-__device__ __forceinline__ void fill_stage(const GemmParams& p, int kt, int kfull, int m0, int n0, int nlast,
-                                           Stage<T> st, int w_uniform, int lane) {
-  if (kt < kfull)
-    issue_dma<T>(p, m0, n0, kt * BK, nlast, st, w_uniform, lane);
-  else
-    tail_fill<T>(p, m0, n0, kt * BK, nlast, st, w_uniform, lane);
+__device__ __forceinline__ i16x8 read_bf(Stage<T> st, int ks, int wm, int s, int lane) {
+  const int m = wm * 128 + 16 * s + (lane & 15);
+  const int c = (4 * ks + (lane >> 4)) ^ swzA(m);
+  return *(const i16x8*)(st.a + m * BK + c * 8);
 }
 
-// Operand fragments of one 32-deep k slice (ks = 0 or 1 of the stage).
-//   bf[s]: B operand = A^T, rows m = 128 wm + 16 s + (lane & 15), k = 8 (lane >> 4) + e
-//   af[t]: A operand = B^T, rows n = 128 wn + 16 t + (lane & 15), same k, via two
-//          transposing reads of 4 k each.
 template <typename T>
-__device__ __forceinline__ void read_frags(Stage<T> st, int ks, int wm, int wn, int lane, i16x8 (&af)[8],
-                                           i16x8 (&bf)[8]) {
-  const int q = lane & 15, b = lane >> 4;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    int m = wm * 128 + 16 * s + q;
-    int c = (4 * ks + b) ^ swzA(m);
-    bf[s] = *(const i16x8*)(st.a + m * BK + c * 8);
-  }
+__device__ __forceinline__ i16x4 read_af_half(Stage<T> st, int ks, int wn, int t, int half, int lane) {
+  const int q = lane & 15;
+  const int n = wn * 128 + 16 * t + 4 * (q & 3);
+  const int k = 32 * ks + 8 * (lane >> 4) + 4 * half + (q >> 2);
+  return lds_read_tr16(st.b + k * BN + (((n >> 3) ^ swzB(k)) << 3) + (n & 7));
+}
+
+// One slice: 8 groups of {2 copies of K step k + 2 when `copy` (a uniform
+// branch around the copies only), 3 reads of the next slice's fragments, the
+// 8 MFMAs of sub-tile row t}.  A scheduling fence closes every group.  The
+// MFMAs never sit inside a branch, so the accumulators stay in AGPRs.  On the
+// last K step the "next" reads fetch stale but in-bounds LDS and are unused.
+template <typename T>
+__device__ __forceinline__ void slice(const Frags& cur, f32x4 (&acc)[8][8], Frags& nxt, Stage<T> rst, int rks, int wm,
+                                      int wn, int lane, bool copy, const DmaPlan& d, const void* ab, const void* bb,
+                                      Stage<T> cst, int wu) {
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
-    int n = wn * 128 + 16 * t + 4 * (q & 3);
-    int k = 32 * ks + 8 * b + (q >> 2);
-    i16x4 lo = lds_read_tr16(st.b + k * BN + (((n >> 3) ^ swzB(k)) << 3) + (n & 7));
-    i16x4 hi = lds_read_tr16(st.b + (k + 4) * BN + (((n >> 3) ^ swzB(k + 4)) << 3) + (n & 7));
-    af[t] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if (copy) {
+      dma_copy<T>(2 * t, d, ab, bb, cst, wu);
+      dma_copy<T>(2 * t + 1, d, ab, bb, cst, wu);
+    }
+    const i16x4 lo = read_af_half<T>(rst, rks, wn, t, 0, lane);
+    const i16x4 hi = read_af_half<T>(rst, rks, wn, t, 1, lane);
+    nxt.a[t] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    nxt.b[t] = read_bf<T>(rst, rks, wm, t, lane);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) acc[t][s] = mfma16x16x32(cur.a[t], cur.b[s], acc[t][s], T());
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 template <typename T>
-__device__ __forceinline__ void mfma_slice(const i16x8 (&af)[8], const i16x8 (&bf)[8], f32x4 (&acc)[8][8]) {
+__device__ __forceinline__ void read_all(Frags& f, Stage<T> st, int ks, int wm, int wn, int lane) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int s = 0; s < 8; ++s) acc[t][s] = mfma16x16x32(af[t], bf[s], acc[t][s], T());
-}
-
-// Interleave the 24 LDS reads of the next slice with the 64 MFMAs of this one.
-__device__ __forceinline__ void interleave_reads_with_mfma() {
-#pragma unroll
-  for (int i = 0; i < 24; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+  for (int t = 0; t < 8; ++t) {
+    const i16x4 lo = read_af_half<T>(st, ks, wn, t, 0, lane);
+    const i16x4 hi = read_af_half<T>(st, ks, wn, t, 1, lane);
+    f.a[t] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    f.b[t] = read_bf<T>(st, ks, wm, t, lane);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
 }
 
-template <typename T, typename TO>
+template <typename TO>
 __device__ __forceinline__ void store4(TO* dst, f32x4 v, int valid) {
   if constexpr (sizeof(TO) == 2) {
     typedef TO to4 __attribute__((ext_vector_type(4)));
-    to4 o = (to4){(TO)v[0], (TO)v[1], (TO)v[2], (TO)v[3]};
+    const to4 o = (to4){(TO)v[0], (TO)v[1], (TO)v[2], (TO)v[3]};
     if (valid >= 4) {
       *(to4*)dst = o;
     } else {
@@ -179,41 +246,51 @@ __device__ __forceinline__ void store4(TO* dst, f32x4 v, int valid) {
 
 template <typename T, typename TO, int ACT, bool HAS_BIAS>
 __global__ __launch_bounds__(THREADS, 1) void gemm16_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(1024))) T sA0[BM * BK];
-  __shared__ __attribute__((aligned(1024))) T sB0[BK * BN];
-  __shared__ __attribute__((aligned(1024))) T sA1[BM * BK];
-  __shared__ __attribute__((aligned(1024))) T sB1[BK * BN];
-  const Stage<T> st0{sA0, sB0}, st1{sA1, sB1};
+  // The two stages of A (and of B) are adjacent, 32 KB apart, so switching
+  // stage is an immediate offset on every LDS read rather than new address
+  // registers.
+  __shared__ __attribute__((aligned(1024))) T sA[2][BM * BK];
+  __shared__ __attribute__((aligned(1024))) T sB[2][BK * BN];
+  const Stage<T> st0{sA[0], sB[0]}, st1{sA[1], sB[1]};
 
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int wm = w & 1, wn = w >> 1;
-  const int nlast = ((p.N - 1) >> 3) << 3;
+
   f32x4 acc[8][8];
 #pragma unroll
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int s = 0; s < 8; ++s) acc[t][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // Main loop.  Per K step (one LDS stage, two 32-deep slices):
-  //   slice 0 MFMAs run while slice 1 fragments are read;
-  //   then the barrier that frees the stage (all waves hold their fragments)
-  //   and publishes the other stage (its copies waited for);
-  //   the copy of K step kt + 2 is issued into the freed stage;
-  //   slice 1 MFMAs run while slice 0 fragments of the next stage are read.
   const int kfull = p.K / BK;
   const int ktiles = (p.K + BK - 1) / BK;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  i16x8 fa0[8], fb0[8], fa1[8], fb1[8];
+  const DmaPlan d = make_plan<T>(p, m0, n0, wu, lane);
+  Frags f0, f1;
   if (ktiles > 0) {
-    fill_stage<T>(p, 0, kfull, m0, n0, nlast, st0, wu, lane);
+    if (kfull > 0)
+      dma_all<T>(p, d, m0, n0, 0, st0, wu);
+    else
+      tail_fill<T>(p, m0, n0, 0, st0, wu, lane);
     wait_vmcnt0();
     __syncthreads();
-    if (ktiles > 1) fill_stage<T>(p, 1, kfull, m0, n0, nlast, st1, wu, lane);
-    read_frags<T>(st0, 0, wm, wn, lane, fa0, fb0);
+    if (ktiles > 1) {
+      if (kfull > 1)
+        dma_all<T>(p, d, m0, n0, BK, st1, wu);
+      else
+        tail_fill<T>(p, m0, n0, BK, st1, wu, lane);
+    }
+    read_all<T>(f0, st0, 0, wm, wn, lane);
   }
+  // Per K step k (stage cur; the other stage holds step k + 1 or is filling):
+  //   slice 0: MFMAs on f0 while f1 (slice 1 of cur) is read;
+  //   barrier: every wave has its fragments of cur, so cur is free, and the
+  //            copies of step k + 1 have landed;
+  //   slice 1: MFMAs on f1 while step k + 2 is copied into cur and f0
+  //            (slice 0 of step k + 1) is read.
   for (int kt = 0; kt < ktiles; kt += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -221,17 +298,16 @@ __global__ __launch_bounds__(THREADS, 1) void gemm16_kernel(GemmParams p) {
       if (k < ktiles) {
         const Stage<T> cur = half ? st1 : st0;
         const Stage<T> nxt = half ? st0 : st1;
-        read_frags<T>(cur, 1, wm, wn, lane, fa1, fb1);
-        mfma_slice<T>(fa0, fb0, acc);
-        interleave_reads_with_mfma();
+        slice<T>(f0, acc, f1, cur, 1, wm, wn, lane, false, d, nullptr, nullptr, cur, wu);
         if (k + 1 < ktiles) {
           wait_vmcnt0();
           __syncthreads();
-          if (k + 2 < ktiles) fill_stage<T>(p, k + 2, kfull, m0, n0, nlast, cur, wu, lane);
-          read_frags<T>(nxt, 0, wm, wn, lane, fa0, fb0);
         }
-        mfma_slice<T>(fa1, fb1, acc);
-        interleave_reads_with_mfma();
+        if (k + 2 < ktiles && k + 2 >= kfull) tail_fill<T>(p, m0, n0, (k + 2) * BK, cur, wu, lane);
+        const bool copy = k + 2 < kfull;
+        const void* ab = a_base<T>(p, m0, (k + 2) * BK);
+        const void* bb = b_base<T>(p, n0, (k + 2) * BK);
+        slice<T>(f1, acc, f0, nxt, 0, wm, wn, lane, copy, d, ab, bb, cur, wu);
       }
     }
   }
@@ -257,7 +333,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm16_kernel(GemmParams p) {
         f32x4 v = acc[t][s];
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = apply_act<ACT>(v[r] + bv[r]);
-        store4<T, TO>(Y + (int64_t)m * p.ldy + n, v, valid);
+        store4<TO>(Y + (int64_t)m * p.ldy + n, v, valid);
       }
     }
   }
