@@ -170,6 +170,9 @@ coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void
   if (M == 0) return ok();
   if (!x || !out) return fail(COALESCE_ERR_INVALID_ARGUMENT, "x or out is NULL");
   if (ldx < D || ldo < D) return fail(COALESCE_ERR_INVALID_ARGUMENT, "ldx/ldo shorter than the row");
+  // a 64-row tile is addressed with 32-bit byte offsets
+  if (ldx > (int64_t(1) << 24) || ldo > (int64_t(1) << 24))
+    return fail(COALESCE_ERR_UNSUPPORTED, "ldx and ldo must be at most 2^24");
   if (!aligned16(x) || !aligned16(out) || (ldx * 2) % 16 || (ldo * 2) % 16)
     return fail(COALESCE_ERR_UNSUPPORTED, "x and out must be 16-byte aligned with 16-byte row pitch");
   const Range ro = span(out, M, D, ldo, 2);
@@ -189,16 +192,8 @@ coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void
   p.ldx = ldx;
   p.ldo = ldo;
   p.M = (int)M;
-  const int64_t tiles = (M + mlp_tile_rows() - 1) / mlp_tile_rows();
-  p.num_tiles = (int)tiles;
-  int64_t nwg = num_workgroups;
-  if (nwg == 0) {
-    const int64_t per_wg = mlp_waves_per_workgroup();
-    const int64_t need = (tiles + per_wg - 1) / per_wg;
-    nwg = need < cus ? need : cus;  // one 8-wave workgroup per CU
-  }
-  if (nwg > (int64_t)INT32_MAX) return fail(COALESCE_ERR_UNSUPPORTED, "workgroup count too large");
-  hipError_t e = launch_mlp(p, (int)D, (int)L, act_code(hidden_act), (int)nwg, (hipStream_t)stream);
+  if (num_workgroups > (int64_t)INT32_MAX) return fail(COALESCE_ERR_UNSUPPORTED, "workgroup count too large");
+  hipError_t e = launch_mlp(p, (int)D, (int)L, act_code(hidden_act), (int)num_workgroups, cus, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "MLP launch");
   return ok();
 }

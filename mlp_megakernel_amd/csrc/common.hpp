@@ -91,7 +91,8 @@ template <typename T> __device__ __forceinline__ T from_f32(float v) { return (T
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds_addr) {
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr);
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
+  // one wait state between the M0 write and the LDS-DMA instruction that reads it
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base) : "memory", "m0");
 }
 #pragma clang diagnostic pop
 

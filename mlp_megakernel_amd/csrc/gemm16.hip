@@ -34,12 +34,37 @@
 namespace coalesce {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64, THREADS = 256;
+constexpr int BM = 256, BN = 256, BK = 64;
 
-// A tile: 256 rows of 64 k (128 B = 8 chunks); chunk c of row m at slot c ^ (m & 7).
-// B tile: 64 rows of 256 n (512 B = 32 chunks); chunk c of row k at slot c ^ 2 (k & 3).
-__device__ __forceinline__ int swzA(int m) { return m & 7; }
-__device__ __forceinline__ int swzB(int k) { return (k & 3) << 1; }
+// Wave geometry.  NW = 4: one wave per SIMD, each owning 128 x 128 of the
+// tile (256 accumulators).  NW = 8: two waves per SIMD, each owning 128 (m)
+// x 64 (n) (128 accumulators), so that one wave's memory stalls are covered
+// by the other wave's MFMAs.
+template <int NW>
+struct Geo {
+  static constexpr int THREADS = NW * 64;
+  static constexpr int WGN = NW / 2;        // waves along n
+  static constexpr int WN = BN / WGN;       // wave tile width (n)
+  static constexpr int NT = WN / 16;        // 16-wide n sub-tiles per wave
+  static constexpr int MT = 8;              // 16-row m sub-tiles per wave (128 rows)
+  static constexpr int CA = 32 / NW;        // 1 KB A copies per wave per K step
+  static constexpr int CB = 32 / NW;        // 1 KB B copies per wave per K step
+};
+
+// LDS layouts, 16-byte chunks XOR-swizzled so that every fragment read is
+// free of bank conflicts whether the LDS serves 128 or 256 bytes per clock:
+//   A tile: 256 rows of 64 k (128 B = 8 chunks); chunk c of row m sits at slot
+//     c ^ swzA(m).  A 128-bit read by 16 lanes (rows m0..m0+15, one chunk)
+//     hits 16 distinct 16-byte slots of a 256-byte window, and any 8
+//     consecutive rows hit 8 distinct slots of a 128-byte window.
+//   B tile: 64 rows of 256 n (512 B = 32 chunks); chunk c of row k sits at slot
+//     c ^ swzB(k).  A transposing read by 32 lanes (rows k0..k0+3 and
+//     k0+8..k0+11, two chunks, two 8-byte halves) hits 32 distinct 8-byte
+//     slots of a 256-byte window.
+// Neither swizzle depends on the sub-tile index s, the slice ks or the half of
+// a transposing read, so those stay immediate offsets of the LDS reads.
+__device__ __forceinline__ int swzA(int m) { return ((m >> 1) & 7) ^ ((m & 1) << 2); }
+__device__ __forceinline__ int swzB(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
 
 template <typename T>
 struct Stage {
@@ -51,29 +76,32 @@ struct Stage {
 // the tile's A base (A + m0 * lda + k0) and B base (B + n0 + k0 * ldb).
 // Copy j < 8 fills A rows 64 w + 8 j .. + 7 (one 1 KB LDS block, lane l's 16
 // bytes at slot l); copy 8 + j fills B rows 16 w + 2 j, + 1.
+template <int NW>
 struct DmaPlan {
-  uint32_t a[8];
-  uint32_t b[8];
+  uint32_t a[Geo<NW>::CA];
+  uint32_t b[Geo<NW>::CB];
 };
 
-template <typename T>
-__device__ __forceinline__ DmaPlan make_plan(const GemmParams& p, int m0, int n0, int w, int lane) {
-  DmaPlan d;
+template <typename T, int NW>
+__device__ __forceinline__ DmaPlan<NW> make_plan(const GemmParams& p, int m0, int n0, int w, int lane) {
+  typedef Geo<NW> G;
+  DmaPlan<NW> d;
   const int rsub = lane >> 3;
-  const int cA = (lane & 7) ^ swzA(rsub);
   const int nlast = ((p.N - 1) >> 3) << 3;
   // 32-bit arithmetic is exact here: the host checks 256 * lda and 64 * ldb
   // bytes fit in 32 bits.
   const uint32_t lda_b = (uint32_t)p.lda * (uint32_t)sizeof(T);
   const uint32_t ldb_b = (uint32_t)p.ldb * (uint32_t)sizeof(T);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int gm = min(m0 + w * 64 + j * 8 + rsub, p.M - 1);
+  for (int j = 0; j < G::CA; ++j) {
+    const int row = (w * G::CA + j) * 8 + rsub;
+    const int cA = (lane & 7) ^ swzA(row);
+    const int gm = min(m0 + row, p.M - 1);
     d.a[j] = (uint32_t)(gm - m0) * lda_b + (uint32_t)(cA * 8 * (int)sizeof(T));
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = w * 16 + j * 2 + (lane >> 5);
+  for (int j = 0; j < G::CB; ++j) {
+    const int row = (w * G::CB + j) * 2 + (lane >> 5);
     const int cB = (lane & 31) ^ swzB(row);
     const int gn = min(n0 + cB * 8, nlast);
     d.b[j] = (uint32_t)row * ldb_b + (uint32_t)((gn - n0) * (int)sizeof(T));
@@ -94,18 +122,22 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 // 16-byte direct copy: global (SGPR base + per-lane 32-bit offset) -> LDS
 // (wave-uniform byte address + 16 * lane).
 __device__ __forceinline__ void dma16_off(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds) : "memory", "m0");
+  // one wait state between the M0 write and the LDS-DMA instruction that reads it
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(lds)
+               : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
-// Copy j (0..15) of K step k into stage st.
-template <typename T>
-__device__ __forceinline__ void dma_copy(int j, const DmaPlan& d, const void* abase, const void* bbase, Stage<T> st,
-                                         int wu) {
-  if (j < 8)
-    dma16_off(abase, d.a[j], lds_addr(st.a) + (uint32_t)(wu * 64 + j * 8) * (BK * (int)sizeof(T)));
+// Copy j (0 .. CA + CB - 1) of a K step into stage st.
+template <typename T, int NW>
+__device__ __forceinline__ void dma_copy(int j, const DmaPlan<NW>& d, const void* abase, const void* bbase,
+                                         Stage<T> st, int wu) {
+  typedef Geo<NW> G;
+  if (j < G::CA)
+    dma16_off(abase, d.a[j], lds_addr(st.a) + (uint32_t)((wu * G::CA + j) * 8) * (BK * (int)sizeof(T)));
   else
-    dma16_off(bbase, d.b[j - 8], lds_addr(st.b) + (uint32_t)(wu * 16 + (j - 8) * 2) * (BN * (int)sizeof(T)));
+    dma16_off(bbase, d.b[j - G::CA],
+              lds_addr(st.b) + (uint32_t)((wu * G::CB + j - G::CA) * 2) * (BN * (int)sizeof(T)));
 }
 
 template <typename T>
@@ -117,30 +149,31 @@ __device__ __forceinline__ const void* b_base(const GemmParams& p, int n0, int k
   return uniform_ptr((const T*)p.B + (int64_t)k0 * p.ldb + n0);
 }
 
-// All 16 copies of a full K step at once (prologue only).
-template <typename T>
-__device__ __forceinline__ void dma_all(const GemmParams& p, const DmaPlan& d, int m0, int n0, int k0, Stage<T> st,
-                                        int wu) {
+// All copies of a full K step at once (prologue only).
+template <typename T, int NW>
+__device__ __forceinline__ void dma_all(const GemmParams& p, const DmaPlan<NW>& d, int m0, int n0, int k0,
+                                        Stage<T> st, int wu) {
   const void* ab = a_base<T>(p, m0, k0);
   const void* bb = b_base<T>(p, n0, k0);
 #pragma unroll
-  for (int j = 0; j < 16; ++j) dma_copy<T>(j, d, ab, bb, st, wu);
+  for (int j = 0; j < Geo<NW>::CA + Geo<NW>::CB; ++j) dma_copy<T, NW>(j, d, ab, bb, st, wu);
 }
 
 // Partial last K step: masked loads (elements at k >= K become 0), written to
 // the same LDS slots the direct copies would use.
-template <typename T>
+template <typename T, int NW>
 __device__ __forceinline__ void tail_fill(const GemmParams& p, int m0, int n0, int k0, Stage<T> st, int w, int lane) {
+  typedef Geo<NW> G;
   const T* A = (const T*)p.A;
   const T* B = (const T*)p.B;
   const int rsub = lane >> 3;
-  const int cA = (lane & 7) ^ swzA(rsub);
-  const int kA = k0 + cA * 8;
   const int nlast = ((p.N - 1) >> 3) << 3;
-  i16x8 ra[8], rb[8];
+  i16x8 ra[G::CA], rb[G::CB];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int gm = min(m0 + w * 64 + j * 8 + rsub, p.M - 1);
+  for (int j = 0; j < G::CA; ++j) {
+    const int row = (w * G::CA + j) * 8 + rsub;
+    const int kA = k0 + ((lane & 7) ^ swzA(row)) * 8;
+    const int gm = min(m0 + row, p.M - 1);
     i16x8 v = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
     if (kA < p.K) {
       v = *(const i16x8*)(A + (int64_t)gm * p.lda + kA);
@@ -151,8 +184,8 @@ __device__ __forceinline__ void tail_fill(const GemmParams& p, int m0, int n0, i
     ra[j] = v;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = w * 16 + j * 2 + (lane >> 5);
+  for (int j = 0; j < G::CB; ++j) {
+    const int row = (w * G::CB + j) * 2 + (lane >> 5);
     const int cB = (lane & 31) ^ swzB(row);
     const int gn = min(n0 + cB * 8, nlast);
     i16x8 v = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
@@ -160,18 +193,19 @@ __device__ __forceinline__ void tail_fill(const GemmParams& p, int m0, int n0, i
     rb[j] = v;
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) *(i16x8*)(st.a + (w * 64 + j * 8) * BK + lane * 8) = ra[j];
+  for (int j = 0; j < G::CA; ++j) *(i16x8*)(st.a + (w * G::CA + j) * 8 * BK + lane * 8) = ra[j];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) *(i16x8*)(st.b + (w * 16 + j * 2) * BN + lane * 8) = rb[j];
+  for (int j = 0; j < G::CB; ++j) *(i16x8*)(st.b + (w * G::CB + j) * 2 * BN + lane * 8) = rb[j];
 }
 
 // Operand fragments of one 32-deep k slice (ks = 0 or 1 of a stage):
-//   bf[s]: B operand = A^T, rows m = 128 wm + 16 s + (lane & 15), k = 8 (lane >> 4) + e;
-//   af[t]: A operand = B^T, rows n = 128 wn + 16 t + (lane & 15), same k, as two
-//          transposing reads of 4 k (lo: e = 0..3, hi: e = 4..7).
+//   b[s]: B operand = A^T, rows m = 128 wm + 16 s + (lane & 15), k = 8 (lane >> 4) + e;
+//   a[t]: A operand = B^T, rows n = WN wn + 16 t + (lane & 15), same k, as two
+//         transposing reads of 4 k (lo: e = 0..3, hi: e = 4..7).
+template <int NW>
 struct Frags {
-  i16x8 a[8];
-  i16x8 b[8];
+  i16x8 a[Geo<NW>::NT];
+  i16x8 b[Geo<NW>::MT];
 };
 
 template <typename T>
@@ -181,48 +215,53 @@ __device__ __forceinline__ i16x8 read_bf(Stage<T> st, int ks, int wm, int s, int
   return *(const i16x8*)(st.a + m * BK + c * 8);
 }
 
-template <typename T>
+template <typename T, int NW>
 __device__ __forceinline__ i16x4 read_af_half(Stage<T> st, int ks, int wn, int t, int half, int lane) {
   const int q = lane & 15;
-  const int n = wn * 128 + 16 * t + 4 * (q & 3);
+  const int n = wn * Geo<NW>::WN + 16 * t + 4 * (q & 3);
   const int k = 32 * ks + 8 * (lane >> 4) + 4 * half + (q >> 2);
   return lds_read_tr16(st.b + k * BN + (((n >> 3) ^ swzB(k)) << 3) + (n & 7));
 }
 
-// One slice: 8 groups of {2 copies of K step k + 2 when `copy` (a uniform
-// branch around the copies only), 3 reads of the next slice's fragments, the
-// 8 MFMAs of sub-tile row t}.  A scheduling fence closes every group.  The
-// MFMAs never sit inside a branch, so the accumulators stay in AGPRs.  On the
-// last K step the "next" reads fetch stale but in-bounds LDS and are unused.
-template <typename T>
-__device__ __forceinline__ void slice(const Frags& cur, f32x4 (&acc)[8][8], Frags& nxt, Stage<T> rst, int rks, int wm,
-                                      int wn, int lane, bool copy, const DmaPlan& d, const void* ab, const void* bb,
-                                      Stage<T> cst, int wu) {
+// One slice: NT groups of {2 copies of K step k + 2 when `copy` (a uniform
+// branch around the copies only), the next slice's fragment reads for
+// sub-tile t (and MT / NT of the m sub-tiles), the MT MFMAs of sub-tile t}.
+// A scheduling fence closes every group.  The MFMAs never sit inside a
+// branch, so the accumulators stay in AGPRs.  On the last K step the "next"
+// reads fetch stale but in-bounds LDS and are unused.
+template <typename T, int NW>
+__device__ __forceinline__ void slice(const Frags<NW>& cur, f32x4 (&acc)[Geo<NW>::NT][Geo<NW>::MT], Frags<NW>& nxt,
+                                      Stage<T> rst, int rks, int wm, int wn, int lane, bool copy,
+                                      const DmaPlan<NW>& d, const void* ab, const void* bb, Stage<T> cst, int wu) {
+  typedef Geo<NW> G;
+  constexpr int BPG = G::MT / G::NT;  // m-side fragment reads per group
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
+  for (int t = 0; t < G::NT; ++t) {
     if (copy) {
-      dma_copy<T>(2 * t, d, ab, bb, cst, wu);
-      dma_copy<T>(2 * t + 1, d, ab, bb, cst, wu);
+      dma_copy<T, NW>(2 * t, d, ab, bb, cst, wu);
+      dma_copy<T, NW>(2 * t + 1, d, ab, bb, cst, wu);
     }
-    const i16x4 lo = read_af_half<T>(rst, rks, wn, t, 0, lane);
-    const i16x4 hi = read_af_half<T>(rst, rks, wn, t, 1, lane);
+    const i16x4 lo = read_af_half<T, NW>(rst, rks, wn, t, 0, lane);
+    const i16x4 hi = read_af_half<T, NW>(rst, rks, wn, t, 1, lane);
     nxt.a[t] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    nxt.b[t] = read_bf<T>(rst, rks, wm, t, lane);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc[t][s] = mfma16x16x32(cur.a[t], cur.b[s], acc[t][s], T());
+    for (int i = 0; i < BPG; ++i) nxt.b[t * BPG + i] = read_bf<T>(rst, rks, wm, t * BPG + i, lane);
+#pragma unroll
+    for (int s = 0; s < G::MT; ++s) acc[t][s] = mfma16x16x32(cur.a[t], cur.b[s], acc[t][s], T());
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void read_all(Frags& f, Stage<T> st, int ks, int wm, int wn, int lane) {
+template <typename T, int NW>
+__device__ __forceinline__ void read_all(Frags<NW>& f, Stage<T> st, int ks, int wm, int wn, int lane) {
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const i16x4 lo = read_af_half<T>(st, ks, wn, t, 0, lane);
-    const i16x4 hi = read_af_half<T>(st, ks, wn, t, 1, lane);
+  for (int t = 0; t < Geo<NW>::NT; ++t) {
+    const i16x4 lo = read_af_half<T, NW>(st, ks, wn, t, 0, lane);
+    const i16x4 hi = read_af_half<T, NW>(st, ks, wn, t, 1, lane);
     f.a[t] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    f.b[t] = read_bf<T>(st, ks, wm, t, lane);
   }
+#pragma unroll
+  for (int s = 0; s < Geo<NW>::MT; ++s) f.b[s] = read_bf<T>(st, ks, wm, s, lane);
 }
 
 template <typename TO>
@@ -244,8 +283,9 @@ __device__ __forceinline__ void store4(TO* dst, f32x4 v, int valid) {
   }
 }
 
-template <typename T, typename TO, int ACT, bool HAS_BIAS>
-__global__ __launch_bounds__(THREADS, 1) void gemm16_kernel(GemmParams p) {
+template <typename T, typename TO, int ACT, bool HAS_BIAS, int NW>
+__global__ __launch_bounds__(Geo<NW>::THREADS, 1) void gemm16_kernel(GemmParams p) {
+  typedef Geo<NW> G;
   // The two stages of A (and of B) are adjacent, 32 KB apart, so switching
   // stage is an immediate offset on every LDS read rather than new address
   // registers.
@@ -260,30 +300,30 @@ __global__ __launch_bounds__(THREADS, 1) void gemm16_kernel(GemmParams p) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int wm = w & 1, wn = w >> 1;
 
-  f32x4 acc[8][8];
+  f32x4 acc[G::NT][G::MT];
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+  for (int t = 0; t < G::NT; ++t)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) acc[t][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < G::MT; ++s) acc[t][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   const int kfull = p.K / BK;
   const int ktiles = (p.K + BK - 1) / BK;
-  const DmaPlan d = make_plan<T>(p, m0, n0, wu, lane);
-  Frags f0, f1;
+  const DmaPlan<NW> d = make_plan<T, NW>(p, m0, n0, wu, lane);
+  Frags<NW> f0, f1;
   if (ktiles > 0) {
     if (kfull > 0)
-      dma_all<T>(p, d, m0, n0, 0, st0, wu);
+      dma_all<T, NW>(p, d, m0, n0, 0, st0, wu);
     else
-      tail_fill<T>(p, m0, n0, 0, st0, wu, lane);
+      tail_fill<T, NW>(p, m0, n0, 0, st0, wu, lane);
     wait_vmcnt0();
     __syncthreads();
     if (ktiles > 1) {
       if (kfull > 1)
-        dma_all<T>(p, d, m0, n0, BK, st1, wu);
+        dma_all<T, NW>(p, d, m0, n0, BK, st1, wu);
       else
-        tail_fill<T>(p, m0, n0, BK, st1, wu, lane);
+        tail_fill<T, NW>(p, m0, n0, BK, st1, wu, lane);
     }
-    read_all<T>(f0, st0, 0, wm, wn, lane);
+    read_all<T, NW>(f0, st0, 0, wm, wn, lane);
   }
   // Per K step k (stage cur; the other stage holds step k + 1 or is filling):
   //   slice 0: MFMAs on f0 while f1 (slice 1 of cur) is read;
@@ -298,16 +338,16 @@ __global__ __launch_bounds__(THREADS, 1) void gemm16_kernel(GemmParams p) {
       if (k < ktiles) {
         const Stage<T> cur = half ? st1 : st0;
         const Stage<T> nxt = half ? st0 : st1;
-        slice<T>(f0, acc, f1, cur, 1, wm, wn, lane, false, d, nullptr, nullptr, cur, wu);
+        slice<T, NW>(f0, acc, f1, cur, 1, wm, wn, lane, false, d, nullptr, nullptr, cur, wu);
         if (k + 1 < ktiles) {
           wait_vmcnt0();
           __syncthreads();
         }
-        if (k + 2 < ktiles && k + 2 >= kfull) tail_fill<T>(p, m0, n0, (k + 2) * BK, cur, wu, lane);
+        if (k + 2 < ktiles && k + 2 >= kfull) tail_fill<T, NW>(p, m0, n0, (k + 2) * BK, cur, wu, lane);
         const bool copy = k + 2 < kfull;
         const void* ab = a_base<T>(p, m0, (k + 2) * BK);
         const void* bb = b_base<T>(p, n0, (k + 2) * BK);
-        slice<T>(f1, acc, f0, nxt, 0, wm, wn, lane, copy, d, ab, bb, cur, wu);
+        slice<T, NW>(f1, acc, f0, nxt, 0, wm, wn, lane, copy, d, ab, bb, cur, wu);
       }
     }
   }
@@ -317,8 +357,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm16_kernel(GemmParams p) {
   const T* bias = (const T*)p.bias;
   TO* Y = (TO*)p.Y;
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int n = n0 + wn * 128 + 16 * t + 4 * b;
+  for (int t = 0; t < G::NT; ++t) {
+    const int n = n0 + wn * G::WN + 16 * t + 4 * b;
     if (n >= p.N) continue;
     const int valid = min(4, p.N - n);
     f32x4 bv = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -327,7 +367,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm16_kernel(GemmParams p) {
       for (int r = 0; r < 4; ++r) bv[r] = r < valid ? to_f32(bias[n + r]) : 0.f;
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < G::MT; ++s) {
       const int m = m0 + wm * 128 + 16 * s + q;
       if (m < p.M) {
         f32x4 v = acc[t][s];
@@ -339,13 +379,18 @@ __global__ __launch_bounds__(THREADS, 1) void gemm16_kernel(GemmParams p) {
   }
 }
 
+#ifndef GEMM16_WAVES
+#define GEMM16_WAVES 8
+#endif
+
 template <typename T, typename TO, int ACT>
 hipError_t launch_typed(GemmParams p, hipStream_t stream) {
-  dim3 grid(p.tiles_m * p.tiles_n), block(THREADS);
+  constexpr int NW = GEMM16_WAVES;
+  dim3 grid(p.tiles_m * p.tiles_n), block(Geo<NW>::THREADS);
   if (p.bias)
-    hipLaunchKernelGGL((gemm16_kernel<T, TO, ACT, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((gemm16_kernel<T, TO, ACT, true, NW>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm16_kernel<T, TO, ACT, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((gemm16_kernel<T, TO, ACT, false, NW>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

@@ -27,10 +27,14 @@ __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// A tile: BM rows of 32 floats (8 chunks of 4); chunk c of row m at slot c ^ (m & 7).
-// B tile: 32 rows of BN floats (BN / 4 chunks); chunk c of row k at slot c ^ 4 ((k >> 2) & 1).
-__device__ __forceinline__ int swzA(int m) { return m & 7; }
-__device__ __forceinline__ int swzB(int k) { return ((k >> 2) & 1) << 2; }
+// A tile: BM rows of 32 floats (8 chunks of 4); chunk c of row m at slot
+// c ^ swzA(m): a 128-bit read by 16 lanes (16 rows, one chunk) hits 16
+// distinct 16-byte slots of a 256-byte window (8 of a 128-byte one).
+// B tile: 32 rows of BN floats (BN / 4 chunks); chunk c of row k at slot
+// c ^ 4 ((k >> 2) & 3): the 32-bit reads of one MFMA (rows k, k+4, k+8, k+12,
+// 16 consecutive n each) land in 4 disjoint 64-byte segments.
+__device__ __forceinline__ int swzA(int m) { return ((m >> 1) & 7) ^ ((m & 1) << 2); }
+__device__ __forceinline__ int swzB(int k) { return ((k >> 2) & 3) << 2; }
 
 template <int BM, int BN>
 struct Cfg {

@@ -29,12 +29,12 @@ struct MlpParams {
   const void* W[8];
   int64_t ldx, ldo;
   int M;
-  int num_tiles;  // row tiles of 64 rows
+  int num_tiles;  // row tiles (set by the launcher)
 };
 // Widths all equal to D (64 or 128), L layers (1..8 for 64, 1..4 for 128).
-hipError_t launch_mlp(const MlpParams& p, int D, int L, int hidden_act, int num_workgroups, hipStream_t stream);
-int mlp_tile_rows();
-int mlp_waves_per_workgroup();
+// num_workgroups <= 0: min(#CUs x occupancy, workgroups with work).
+hipError_t launch_mlp(const MlpParams& p, int D, int L, int hidden_act, int num_workgroups, int num_cus,
+                      hipStream_t stream);
 
 hipError_t launch_bias_add(const void* X, int64_t ldx, const void* bias, void* Y, int64_t ldy, int M, int N,
                            DType xt, DType bt, DType yt, hipStream_t stream, int num_cus);
