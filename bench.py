@@ -25,6 +25,7 @@ All inputs are synthetic and seeded (datagen).
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import os
 import sys
@@ -129,20 +130,28 @@ def main():
 
     # ----------------------------------------------------------------- timing
     def timed_steps(fn, steps, warmup):
-        """K back-to-back steps; wall time and per-launch event durations."""
+        """K back-to-back steps: wall time per step, and the average launch
+        duration from one pair of HIP events around the K launches on the
+        launch stream (no per-launch event records between the kernels)."""
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        t0 = time.perf_counter()
-        for a, b in ev:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        # a full collection of the Python heap inside the region stalls the
+        # launching thread for tens of ms while the GPU runs dry
+        gc.collect()
+        gc.disable()
+        try:
+            t0 = time.perf_counter()
             a.record(stream)
-            fn()
+            for _ in range(steps):
+                fn()
             b.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        kern = [a.elapsed_time(b) for a, b in ev]
-        return wall * 1e3 / steps, float(np.mean(kern)), kern
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
+        finally:
+            gc.enable()
+        return wall * 1e3 / steps, a.elapsed_time(b) / steps
 
     def pages_harness(fn):
         """>= warmup_ms of continuous GPU work, then N x {flush, event, fn, event}; median."""
@@ -158,12 +167,17 @@ def main():
             reps = min(reps * 2, 256)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(args.harness_iters)]
-        for a, b in ev:
-            flush()
-            a.record(stream)
-            fn()
-            b.record(stream)
-        torch.cuda.synchronize()
+        gc.collect()
+        gc.disable()
+        try:
+            for a, b in ev:
+                flush()
+                a.record(stream)
+                fn()
+                b.record(stream)
+            torch.cuda.synchronize()
+        finally:
+            gc.enable()
         t = np.array([a.elapsed_time(b) for a, b in ev])
         return {"median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
                 "p90_ms": float(np.percentile(t, 90)), "iters": int(args.harness_iters)}
@@ -193,7 +207,7 @@ def main():
     # -------------------------------------------------------- primary workload
     print("bench: generating %s" % prim.name, file=sys.stderr, flush=True)
     fused, unfused = (mlp_case if is_mlp else gemm_case)(prim)
-    ms_step, mean_kernel_ms, _ = timed_steps(fused, args.steps, args.warmup)
+    ms_step, mean_kernel_ms = timed_steps(fused, args.steps, args.warmup)
     if is_mlp:
         value = prim.M / (ms_step * 1e-3)
         unit, dtype = "rows/s", "f16"
@@ -230,7 +244,8 @@ def main():
                 continue
             print("bench: %s" % w.name, file=sys.stderr, flush=True)
             f, u = mlp_case(w)
-            ms, mk_ms, _ = timed_steps(f, max(10, args.steps // 2), 5)
+            # warm-up long enough for the clocks to settle under this load
+            ms, mk_ms = timed_steps(f, max(20, args.steps), max(10, int(200.0 / 0.15)))
             mlp_res[w.name] = {"rows_per_s": round(w.M / (ms * 1e-3), 1), "ms_per_call": round(ms, 5),
                                "roofline": roofline_mlp(w, mk_ms)}
             if not args.no_harness:

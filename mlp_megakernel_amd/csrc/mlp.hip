@@ -8,7 +8,7 @@
 // Design for gfx950, widths D of 64 or 128:
 //   * a workgroup copies every W_l into LDS once (L * D * D fp16: 96 KB for
 //     3 x 128, 40 KB for 5 x 64) and reuses it for all of its row tiles;
-//   * a wave owns a tile of 32 (D = 128) or 64 (D = 64) rows; tiles go to
+//   * a wave owns a tile of 32 rows; tiles go to
 //     waves round-robin, so every row goes through the same instruction
 //     sequence whatever the grid size (results are bit-identical for any
 //     grid);
@@ -24,8 +24,17 @@
 //     (layer_k_slot below);
 //   * activation in fp32 on the accumulators, rounded to fp16 only as the
 //     next layer's operand; the last layer stores fp16 directly;
-//   * at most 128 VGPRs, so 4 waves share a SIMD: one wave's global loads
-//     and activations overlap the others' MFMAs.
+//   * software pipeline inside a layer: the MFMAs of output sub-tile t are
+//     interleaved, instruction by instruction, with the activation of
+//     sub-tile t - 1, so the matrix core and the vector ALU work at the same
+//     time even within one wave; the x of a wave's next row tile is loaded
+//     when the current one starts, into a third register buffer;
+//   * the output of two neighbouring 16-unit sub-tiles is exchanged between
+//     lane groups (v_permlane16_swap) so that every lane stores 16 bytes and
+//     each store instruction writes 64 contiguous bytes per row;
+//   * the activation is VALU-bound (two transcendentals per element), so
+//     the softplus guard is taken out of the per-element path: see
+//     softplus_b2_fast and the check at the end of mlp_kernel.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -33,23 +42,69 @@ namespace coalesce {
 namespace {
 
 // Per-width geometry.  A wave owns a tile of 16 * MT rows; a workgroup has
-// WAVES waves.  Width 128: 32-row tiles and 16-wave workgroups, so one
-// workgroup (its 96 KB of weights fill the LDS) still gives 4 waves per SIMD
-// within 128 VGPRs.  Width 64: 64-row tiles, 8-wave workgroups, two per CU.
+// WAVES waves, and the kernel is held to the VGPR budget of MINW waves per
+// SIMD (the second launch-bounds argument).  Both widths use 32-row tiles:
+// one 128-bit weight read from LDS then feeds two MFMAs, which keeps the LDS
+// port below its limit, and the activations of a tile take 2 x 16 (D = 128)
+// or 2 x 8 (D = 64) VGPRs.
+//   D = 128: 12 waves, one workgroup per CU (its 96 KB of weights fill the
+//            LDS), 3 waves per SIMD within 168 VGPRs;
+//   D = 64:  16 waves, 4 waves per SIMD within 128 VGPRs.
+// The macros exist for tuning sweeps; the defaults are the measured best.
+#ifndef MLP128_MT
+#define MLP128_MT 2
+#endif
+#ifndef MLP128_WAVES
+#define MLP128_WAVES 12
+#endif
+#ifndef MLP128_MINW
+#define MLP128_MINW 3
+#endif
+#ifndef MLP64_MT
+#define MLP64_MT 2
+#endif
+#ifndef MLP64_WAVES
+#define MLP64_WAVES 16
+#endif
+#ifndef MLP64_MINW
+#define MLP64_MINW 4
+#endif
+#ifndef MLP_INTERLEAVE
+#define MLP_INTERLEAVE 1
+#endif
 template <int D>
 struct MlpCfg;
 template <>
 struct MlpCfg<128> {
-  static constexpr int MT = 2, WAVES = 16;
+  static constexpr int MT = MLP128_MT, WAVES = MLP128_WAVES, MINW = MLP128_MINW;
 };
 template <>
 struct MlpCfg<64> {
-  static constexpr int MT = 4, WAVES = 8;
+  static constexpr int MT = MLP64_MT, WAVES = MLP64_WAVES, MINW = MLP64_MINW;
 };
+
 template <int D>
-constexpr int tile_rows() { return 16 * MlpCfg<D>::MT; }
+struct Geo {
+  static constexpr int MT = MlpCfg<D>::MT;       // 16-row sub-tiles per wave tile
+  static constexpr int WAVES = MlpCfg<D>::WAVES;  // waves per workgroup
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int TR = 16 * MT;  // rows per wave tile
+  static constexpr int KS = D / 32;   // 32-deep k steps per layer
+  static constexpr int NT = D / 16;   // 16-unit output sub-tiles per layer
+};
+
+// Activations of one row tile in MFMA B-operand form: v[s][ks] holds, for
+// rows 16 s .. 16 s + 15, the 8 fp16 inputs of k step ks that this lane feeds
+// (two per dword).
 template <int D>
-constexpr int threads() { return 64 * MlpCfg<D>::WAVES; }
+struct HTile {
+  u32x4 v[Geo<D>::MT][Geo<D>::KS];
+};
+
+// Two fp32 values rounded to nearest-even fp16 and packed into one dword.
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
 
 // LDS position (within a row of W^T) of logical input unit k for layers fed
 // by a previous layer's registers.  Lane group g of the B operand holds, for
@@ -65,6 +120,7 @@ __device__ __forceinline__ int layer_k_slot(int k) {
 // chunk); the swizzle puts those 16 reads in 16 distinct 16-byte slots of a
 // 256-byte bank window (and any 8 consecutive rows in 8 distinct slots of a
 // 128-byte one).  Rows are 256 B (16 chunks) for D = 128 and 128 B for D = 64.
+// wswz(16 t + q) = wswz(q): the swizzle repeats every 16 rows.
 template <int D>
 __device__ __forceinline__ int wswz(int n) {
   if constexpr (D == 128)
@@ -78,43 +134,98 @@ __device__ __forceinline__ int w_offset(int l, int n, int slot) {
   return (l * D + n) * D + ((((slot >> 3) ^ wswz<D>(n))) << 3) + (slot & 7);
 }
 
+// Logical input unit k that sits at LDS slot `slot` (inverse of
+// layer_k_slot): slot = 32 a + 8 b + 4 c + d holds k = 32 a + 16 c + 4 b + d.
+__device__ __forceinline__ int layer_slot_k(int slot) {
+  return (slot & ~31) | (((slot >> 2) & 1) << 4) | (((slot >> 3) & 3) << 2) | (slot & 3);
+}
+
+// Copy every W_l into LDS in the layout above.  One work item fills the
+// 16-byte chunk cb of the 8 W^T rows n = 8 nb .. 8 nb + 7: it loads the 8
+// rows of W_l (16 bytes each) whose units land in that chunk, transposes the
+// 8 x 8 block in registers and writes 8 chunks of 16 bytes.
 template <int D, int L>
 __device__ __forceinline__ void stage_weights(const MlpParams& p, _Float16* sW) {
-  constexpr int CHUNKS = D / 8;  // 16-byte chunks per weight row
-  for (int idx = threadIdx.x; idx < L * D * CHUNKS; idx += threads<D>()) {
-    const int l = idx / (D * CHUNKS);
-    const int rem = idx - l * D * CHUNKS;
-    const int k = rem / CHUNKS;
-    const int c = rem - k * CHUNKS;
-    const f16x8 v = *(const f16x8*)((const _Float16*)p.W[l] + (int64_t)k * D + c * 8);
-    const int slot = l == 0 ? k : layer_k_slot(k);
+  constexpr int NB = D / 8;  // 8-row blocks (and 16-byte chunks) per layer
+  for (int idx = threadIdx.x; idx < L * NB * NB; idx += Geo<D>::THREADS) {
+    const int l = idx / (NB * NB);
+    const int rem = idx - l * NB * NB;
+    const int nb = rem / NB;
+    const int cb = rem - nb * NB;
+    const _Float16* Wl = (const _Float16*)p.W[l];
+    f16x8 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) sW[w_offset<D>(l, c * 8 + i, slot)] = v[i];
+    for (int j = 0; j < 8; ++j) {
+      const int slot = 8 * cb + j;
+      const int k = l == 0 ? slot : layer_slot_k(slot);
+      v[j] = *(const f16x8*)(Wl + (int64_t)k * D + 8 * nb);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f16x8 o = (f16x8){v[0][i], v[1][i], v[2][i], v[3][i], v[4][i], v[5][i], v[6][i], v[7][i]};
+      *(f16x8*)(sW + w_offset<D>(l, 8 * nb + i, 8 * cb)) = o;
+    }
   }
 }
 
-// Uniform (SGPR) base of a row tile: per-lane offsets from it fit in 32 bits
-// (at most 64 rows x a pitch the host limits), which keeps 64-bit address arithmetic
-// out of the loop.
-__device__ __forceinline__ const char* tile_base(const void* p, int64_t first_row, int64_t ld) {
-  const uint64_t v = (uint64_t)(uintptr_t)((const char*)p + first_row * ld * 2);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const char*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+// Per-lane constants of a wave.
+template <int D>
+struct Lane {
+  uint32_t wk[Geo<D>::KS];  // LDS byte address of the lane's W^T fragment: layer 0, sub-tile 0, k step ks
+  uint32_t xoff;            // byte offset of the lane's first x element in a 16-row sub-tile
+  uint32_t ooff;            // byte offset of the lane's 16-byte output piece of sub-tiles 0 and 1 (see last_layer)
+};
+
+template <int D>
+__device__ __forceinline__ Lane<D> lane_setup(const MlpParams& p, const _Float16* sW, int lane) {
+  Lane<D> c;
+  const int q = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < Geo<D>::KS; ++ks) c.wk[ks] = lds_addr(sW) + 2u * (uint32_t)w_offset<D>(0, q, 32 * ks + 8 * g);
+  const uint32_t xrow = (uint32_t)p.ldx * 2u, orow = (uint32_t)p.ldo * 2u;
+  c.xoff = (uint32_t)q * xrow + 16u * (uint32_t)g;
+  c.ooff = (uint32_t)q * orow + 32u * (uint32_t)(g & 1) + 16u * (uint32_t)(g >> 1);
+  return c;
+}
+
+__device__ __forceinline__ i16x8 lds_read128(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) i16x8*)(uintptr_t)addr;
+}
+
+// A value the compiler cannot see through.  The weight-fragment addresses of
+// every layer of every tile pass through it, so that neither the fragments
+// nor per-layer addresses are hoisted out of the tile loop into registers
+// (they do not fit next to the activations); constant offsets added
+// afterwards stay in the instructions' immediate fields.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Buffer resource over 16-row sub-tile s of row tile `tile` of a row-major
+// fp16 matrix with pitch ld (elements) and M rows.  All arguments are
+// wave-uniform.  The resource covers only the sub-tile's rows that exist:
+// accesses at byte offsets at or beyond its size are dropped by the hardware
+// (stores) or read as zero (loads), so the ragged last tile needs no branch.
+// The host bounds the pitch by 2^24 elements, so 16 rows span less than 2^32
+// bytes.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sub_rsrc(const void* base, int M, int tile, int s, int64_t ld) {
+  const int64_t first = (int64_t)tile * Geo<D>::TR + 16 * s;
+  const int64_t rows = min((int64_t)16, max((int64_t)0, (int64_t)M - first));
+  char* p = (char*)base + first * ld * 2;
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)((uint32_t)rows * (uint32_t)(ld * 2)), 0x00020000);
 }
 
 template <int D>
-__device__ __forceinline__ void load_x(const MlpParams& p, int tile, int lane,
-                                       i16x8 (&h)[MlpCfg<D>::MT][D / 32]) {
-  const char* base = tile_base(p.x, (int64_t)tile * tile_rows<D>(), p.ldx);
-  const int q = lane & 15, g = lane >> 4;
-  const int rows_left = p.M - 1 - tile * tile_rows<D>();  // last valid row within the tile
+__device__ __forceinline__ void load_x(const MlpParams& p, const Lane<D>& c, int tile, HTile<D>& h) {
+  const uint32_t xoff = opaque(c.xoff);  // keeps the k-step offsets in the instructions' immediate field
 #pragma unroll
-  for (int s = 0; s < MlpCfg<D>::MT; ++s) {
-    const uint32_t r = (uint32_t)min(16 * s + q, rows_left);
-    const uint32_t off = r * (uint32_t)(p.ldx * 2) + (uint32_t)(16 * g);
+  for (int s = 0; s < Geo<D>::MT; ++s) {
+    const __amdgpu_buffer_rsrc_t rs = sub_rsrc<D>(p.x, p.M, tile, s, p.ldx);
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) h[s][ks] = *(const i16x8*)(base + off + 64 * ks);
+    for (int ks = 0; ks < Geo<D>::KS; ++ks)
+      h.v[s][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, xoff + 64u * ks, 0, 0);
   }
 }
 
@@ -123,113 +234,306 @@ __device__ __forceinline__ void load_x(const MlpParams& p, int tile, int lane,
 // is a = g W = z / ln 2 = z log2(e), exactly the argument the hardware
 // exponential (2^x) wants, and
 //   g' = softplus(z') / ln 2 = log2(1 + 2^a')
-// costs exp2, add, log2 and the page's threshold (z > 20, i.e. a > 20 log2 e,
-// passes a through), with no base-change multiplies.  The first layer, whose
-// input x is in natural units, scales its accumulator by log2(e) once; the
-// last layer scales its output by ln 2 once.  In exact arithmetic nothing
-// changes; the fp16 operand is g rather than h (the same relative rounding).
+// costs exp2, add and log2, with no base-change multiplies.  The first
+// layer, whose input x is in natural units, scales its accumulator by log2(e)
+// once; the last layer scales its output by ln 2 once.  In exact arithmetic
+// nothing changes; the fp16 operand is g rather than h (the same relative
+// rounding).
+//
+// The page's guard (z > 20 passes z through) reads a > 20 log2(e) here.
+// Below that threshold the guarded form is log2(1 + 2^a) exactly, so the
+// per-element path computes only that (softplus_b2_fast) and keeps the
+// maximum fp16 output of each lane.  log2(1 + 2^a) >= a, so an argument
+// above the threshold (or +inf) shows as an output of at least 28 (a bound
+// below the threshold that the rounding of exp2, log2 and fp16 cannot cross);
+// a wave that sees one recomputes its tiles from x with the guarded form
+// (softplus_b2).  Both forms execute the same exp2/add/log2 instructions, so
+// every result equals what the guarded form gives.  NaN arguments give NaN
+// in both forms and are ignored by the maximum.
+constexpr float SP_THRESHOLD_B2 = 28.853900817779268f;  // 20 log2(e)
+constexpr unsigned short SP_FLAG_B2_F16 = 0x4F00;  // 28.0 in fp16
+
+__device__ __forceinline__ float softplus_b2_fast(float a) {
+  return __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(a));
+}
 __device__ __forceinline__ float softplus_b2(float a) {
-  const float s = __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(a));
-  return a > 28.853900817779268f ? a : s;
+  const float s = softplus_b2_fast(a);
+  return a > SP_THRESHOLD_B2 ? a : s;
 }
 
-template <int ACT, bool IN_B2>
-__device__ __forceinline__ float hidden_act(float acc) {
-  if constexpr (ACT == ACT_SOFTPLUS) {
-    if constexpr (IN_B2)
-      return softplus_b2(acc);
-    else
-      return softplus_b2(acc * 1.44269504088896341f);
-  } else {
-    return acc;
+// Issue order of one pipeline step: NM MFMAs, each followed by VPM VALU
+// instructions (transcendentals included), a DS read after every DS_EVERY-th
+// MFMA when DS is set, and a buffer store after every ST_EVERY-th MFMA when
+// ST is set.
+template <int NM, int VPM, bool DS, int DS_EVERY, bool ST, int ST_EVERY>
+__device__ __forceinline__ void interleave() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (DS && i % DS_EVERY == DS_EVERY - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (ST && i % ST_EVERY == ST_EVERY - 1) __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, VPM, 0);
   }
 }
 
-template <int ACT, bool IN_B2>
-__device__ __forceinline__ f16x4 act_to_f16(f32x4 v) {
-  return (f16x4){(_Float16)hidden_act<ACT, IN_B2>(v[0]), (_Float16)hidden_act<ACT, IN_B2>(v[1]),
-                 (_Float16)hidden_act<ACT, IN_B2>(v[2]), (_Float16)hidden_act<ACT, IN_B2>(v[3])};
-}
-
-// One layer for one row tile.  Output sub-tile t (16 units) is finished
-// before t + 1 starts, so its activation overlaps the next sub-tile's MFMAs.
-template <int D, int L, int l, int ACT>
-__device__ __forceinline__ void layer(const MlpParams& p, const _Float16* sW, int tile, int lane,
-                                      const i16x8 (&hin)[MlpCfg<D>::MT][D / 32],
-                                      i16x8 (&hout)[MlpCfg<D>::MT][D / 32]) {
-  constexpr int NT = D / 16, KS = D / 32, MT = MlpCfg<D>::MT;
-  // does this layer's input arrive in base-2 units (see softplus_b2)?
-  constexpr bool IN_B2 = ACT == ACT_SOFTPLUS && l > 0;
-  const int q = lane & 15, g = lane >> 4;
+// Hidden layer l for one row tile: hout = act(hin W_l), in the step pipeline
+// described at the top, with the unguarded softplus; the largest output is
+// folded into mx.
+template <int D, int l, int ACT>
+__device__ __forceinline__ void hidden_layer(const Lane<D>& c, const HTile<D>& hin, HTile<D>& hout,
+                                             u16x2& mx) {
+  using G = Geo<D>;
+  constexpr bool SP = ACT == ACT_SOFTPLUS;
+  constexpr bool IN_B2 = SP && l > 0;  // does the accumulator arrive in base-2 units?
+  // twice the VALU instructions per element: [scale] exp2 add log2, 1/2 pack
+  constexpr int VPE2 = SP ? (IN_B2 ? 7 : 9) : 1;
+  constexpr int VPM = (G::MT * 4 * VPE2 / 2 + G::KS * G::MT - 1) / (G::KS * G::MT);
+  uint32_t wk[G::KS];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    f32x4 acc[MT];
+  for (int ks = 0; ks < G::KS; ++ks) wk[ks] = opaque(c.wk[ks]) + 2u * (uint32_t)(l * D * D);
+  i16x8 wa[G::KS];
+  f32x4 acc[G::MT], prv[G::MT];
 #pragma unroll
-    for (int s = 0; s < MT; ++s) acc[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
-    const int n = 16 * t + q;
+  for (int ks = 0; ks < G::KS; ++ks) wa[ks] = lds_read128(wk[ks]);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const i16x8 a = *(const i16x8*)(sW + w_offset<D>(l, n, 32 * ks + 8 * g));
+  for (int t = 0; t <= G::NT; ++t) {
+    if (t < G::NT) {
 #pragma unroll
-      for (int s = 0; s < MT; ++s) acc[s] = mfma16x16x32(a, hin[s][ks], acc[s], _Float16());
-    }
-    if constexpr (l + 1 < L) {
+      for (int s = 0; s < G::MT; ++s) acc[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < MT; ++s) {
-        const f16x4 o = act_to_f16<ACT, IN_B2>(acc[s]);
-        const i16x4 ob = __builtin_bit_cast(i16x4, o);
+      for (int ks = 0; ks < G::KS; ++ks) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) hout[s][t >> 1][(t & 1) * 4 + r] = ob[r];
+        for (int s = 0; s < G::MT; ++s) acc[s] = mfma16x16x32(wa[ks], __builtin_bit_cast(i16x8, hin.v[s][ks]), acc[s], _Float16());
+        if (t + 1 < G::NT) wa[ks] = lds_read128(wk[ks] + 2u * (uint32_t)(16 * D * (t + 1)));
       }
-    } else {
-      char* obase = (char*)tile_base(p.out, (int64_t)tile * tile_rows<D>(), p.ldo);
-      const int rows_left = p.M - tile * tile_rows<D>();
+    }
+    if (t > 0) {
+      const int u = t - 1;
 #pragma unroll
-      for (int s = 0; s < MT; ++s) {
-        const int r = 16 * s + q;
-        if (r < rows_left) {
-          const float sc = IN_B2 ? 0.693147180559945309f : 1.0f;
-          const f16x4 o = (f16x4){(_Float16)(acc[s][0] * sc), (_Float16)(acc[s][1] * sc), (_Float16)(acc[s][2] * sc),
-                                  (_Float16)(acc[s][3] * sc)};
-          *(f16x4*)(obase + (uint32_t)r * (uint32_t)(p.ldo * 2) + (uint32_t)(32 * t + 8 * g)) = o;
+      for (int s = 0; s < G::MT; ++s) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float a = prv[s][r];
+          if constexpr (SP) {
+            if constexpr (!IN_B2) a *= 1.44269504088896341f;
+            v[r] = softplus_b2_fast(a);
+          } else {
+            v[r] = a;
+          }
         }
+        hout.v[s][u >> 1][(u & 1) * 2] = pack_f16(v[0], v[1]);
+        hout.v[s][u >> 1][(u & 1) * 2 + 1] = pack_f16(v[2], v[3]);
       }
+    }
+    if (MLP_INTERLEAVE && t > 0 && t < G::NT) interleave<G::KS * G::MT, VPM, true, G::MT, false, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < G::MT; ++s) prv[s] = acc[s];
+  }
+  if constexpr (SP) {
+    // running maximum of the layer's fp16 outputs as unsigned 16-bit
+    // integers, two at a time: the outputs are >= +0 or NaN, and for those
+    // the integer order of the bit patterns is the numeric order with every
+    // NaN above +inf
+#pragma unroll
+    for (int s = 0; s < G::MT; ++s)
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) {
+        const u16x2x4 h = __builtin_bit_cast(u16x2x4, hout.v[s][ks]);  // one dword = two fp16
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_max(mx, h.v[i]);
+      }
+    // here, not later: deferring the maximum would keep every layer's
+    // outputs alive until the end of the tile
+    asm volatile("" : "+v"(mx));
+  }
+}
+
+// Output of two neighbouring 16-unit sub-tiles u (even) and u + 1 of one
+// 16-row sub-tile, fp16.  Lane group g (lanes 16 g .. 16 g + 15, one row
+// each) holds 8 bytes of each: units 16 u + 4 g .. + 3 in a and
+// 16 (u + 1) + 4 g .. + 3 in b.  One v_permlane16_swap per dword exchanges
+// b of groups 0 and 2 with a of groups 1 and 3; then group g holds 16
+// contiguous bytes, at unit 16 u + 16 (g & 1) + 8 (g >> 1), and the four
+// groups cover 64 contiguous bytes of their row: one 16-byte store per lane
+// instead of two 8-byte ones with 32 contiguous bytes per row.
+__device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x2 a, u32x2 b) {
+  const auto s0 = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  __builtin_amdgcn_raw_buffer_store_b128((u32x4){s0[0], s1[0], s0[1], s1[1]}, rs, off, 0, 0);
+}
+
+// Last layer l = L - 1 for one row tile: out = hin W_L (times ln 2 when hin
+// is in base-2 units), fp16, stored through a buffer resource that drops the
+// rows beyond M.
+template <int D, int l, int ACT>
+__device__ __forceinline__ void last_layer(const MlpParams& p, const Lane<D>& c, const HTile<D>& hin,
+                                           int tile) {
+  using G = Geo<D>;
+  constexpr bool IN_B2 = ACT == ACT_SOFTPLUS && l > 0;
+  constexpr int VPM = (G::MT * 4 * (IN_B2 ? 3 : 1) / 2 + G::KS * G::MT - 1) / (G::KS * G::MT);
+  constexpr int ST_EVERY = G::KS;  // MT stores per step (every other step) over KS * MT MFMAs
+  __amdgpu_buffer_rsrc_t rs[G::MT];
+#pragma unroll
+  for (int s = 0; s < G::MT; ++s) rs[s] = sub_rsrc<D>(p.out, p.M, tile, s, p.ldo);
+  const uint32_t ooff = opaque(c.ooff);  // keeps the sub-tile offsets in the instructions' immediate field
+  uint32_t wk[G::KS];
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) wk[ks] = opaque(c.wk[ks]) + 2u * (uint32_t)(l * D * D);
+  i16x8 wa[G::KS];
+  f32x4 acc[G::MT], prv[G::MT];
+  u32x2 ev[G::MT];  // packed output of the even sub-tile of a pair
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) wa[ks] = lds_read128(wk[ks]);
+#pragma unroll
+  for (int t = 0; t <= G::NT; ++t) {
+    if (t < G::NT) {
+#pragma unroll
+      for (int s = 0; s < G::MT; ++s) acc[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) {
+#pragma unroll
+        for (int s = 0; s < G::MT; ++s) acc[s] = mfma16x16x32(wa[ks], __builtin_bit_cast(i16x8, hin.v[s][ks]), acc[s], _Float16());
+        if (t + 1 < G::NT) wa[ks] = lds_read128(wk[ks] + 2u * (uint32_t)(16 * D * (t + 1)));
+      }
+    }
+    if (t > 0) {
+      const int u = t - 1;
+#pragma unroll
+      for (int s = 0; s < G::MT; ++s) {
+        const float sc = IN_B2 ? 0.693147180559945309f : 1.0f;
+        const u32x2 o = (u32x2){pack_f16(prv[s][0] * sc, prv[s][1] * sc), pack_f16(prv[s][2] * sc, prv[s][3] * sc)};
+        if (u % 2 == 0)
+          ev[s] = o;
+        else
+          store_pair(rs[s], ooff + 32u * (uint32_t)(u - 1), ev[s], o);
+      }
+    }
+    if (MLP_INTERLEAVE && t > 0 && t < G::NT) interleave<G::KS * G::MT, VPM, true, G::MT, true, ST_EVERY>();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < G::MT; ++s) prv[s] = acc[s];
+  }
+}
+
+// One row tile with the guarded softplus, one 16-row sub-tile at a time and
+// without the step pipeline: the rarely taken path, kept small in registers.
+// Per element it executes the same MFMA accumulation order and the same
+// exp2/add/log2/pack instructions as the pipelined path, so it reproduces
+// that path's bits wherever the guard does not apply.
+template <int D, int L, int ACT>
+__device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& c, int tile) {
+  using G = Geo<D>;
+  constexpr bool SP = ACT == ACT_SOFTPLUS;
+#pragma unroll 1
+  for (int s = 0; s < G::MT; ++s) {
+    const __amdgpu_buffer_rsrc_t rx = sub_rsrc<D>(p.x, p.M, tile, s, p.ldx);
+    const __amdgpu_buffer_rsrc_t ro = sub_rsrc<D>(p.out, p.M, tile, s, p.ldo);
+    const uint32_t xoff = opaque(c.xoff), ooff = opaque(c.ooff);
+    u32x4 h[G::KS], hn[G::KS];
+    u32x2 ev;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) h[ks] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + 64u * ks, 0, 0);
+#pragma unroll 1
+    for (int l = 0; l < L; ++l) {
+      const bool in_b2 = SP && l > 0;
+#pragma unroll
+      for (int t = 0; t < G::NT; ++t) {
+        f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < G::KS; ++ks) {
+          const i16x8 wa = lds_read128(opaque(c.wk[ks]) + 2u * (uint32_t)(l * D * D + 16 * D * t));
+          acc = mfma16x16x32(wa, __builtin_bit_cast(i16x8, h[ks]), acc, _Float16());
+        }
+        if (l + 1 < L) {
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float a = acc[r];
+            if (SP) {
+              if (!in_b2) a *= 1.44269504088896341f;
+              v[r] = softplus_b2(a);
+            } else {
+              v[r] = a;
+            }
+          }
+          hn[t >> 1][(t & 1) * 2] = pack_f16(v[0], v[1]);
+          hn[t >> 1][(t & 1) * 2 + 1] = pack_f16(v[2], v[3]);
+        } else {
+          const float sc = in_b2 ? 0.693147180559945309f : 1.0f;
+          const u32x2 o = (u32x2){pack_f16(acc[0] * sc, acc[1] * sc), pack_f16(acc[2] * sc, acc[3] * sc)};
+          if (t % 2 == 0)
+            ev = o;
+          else
+            store_pair(ro, ooff + 32u * (uint32_t)(t - 1), ev, o);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int ks = 0; ks < G::KS; ++ks) h[ks] = hn[ks];
     }
   }
 }
 
+// One row tile, layers l .. L-1.  hin holds the layer-l input; hfree is free.
+// mx collects the largest unguarded softplus output.
 template <int D, int L, int l, int ACT>
-__device__ __forceinline__ void run_layers(const MlpParams& p, const _Float16* sW, int tile, int lane,
-                                           i16x8 (&h0)[MlpCfg<D>::MT][D / 32],
-                                           i16x8 (&h1)[MlpCfg<D>::MT][D / 32]) {
-  if constexpr (l % 2 == 0)
-    layer<D, L, l, ACT>(p, sW, tile, lane, h0, h1);
-  else
-    layer<D, L, l, ACT>(p, sW, tile, lane, h1, h0);
-  if constexpr (l + 1 < L) run_layers<D, L, l + 1, ACT>(p, sW, tile, lane, h0, h1);
+__device__ __forceinline__ void tile_chain(const MlpParams& p, const Lane<D>& c, int tile, HTile<D>& hin,
+                                           HTile<D>& hfree, u16x2& mx) {
+  if constexpr (l < L - 1) {
+    hidden_layer<D, l, ACT>(c, hin, hfree, mx);
+    tile_chain<D, L, l + 1, ACT>(p, c, tile, hfree, hin, mx);
+  } else {
+    last_layer<D, l, ACT>(p, c, hin, tile);
+  }
 }
 
-// Every configuration is held to 128 VGPRs (at least 4 waves per SIMD, the
-// second launch-bounds argument) so that memory latency and the activation
-// chains of some waves hide behind the MFMAs of others.
+// Several waves per SIMD (MlpCfg::MINW) so that memory latency and the
+// dependent activation chains of some waves hide behind the work of others.
 template <int D, int L, int ACT>
-__global__ __launch_bounds__(threads<D>(), 4) void mlp_kernel(MlpParams p) {
+__global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(MlpParams p) {
+  using G = Geo<D>;
   __shared__ __attribute__((aligned(16))) _Float16 sW[L * D * D];
   stage_weights<D, L>(p, sW);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * MlpCfg<D>::WAVES + (threadIdx.x >> 6);
-  const int nwaves = gridDim.x * MlpCfg<D>::WAVES;
-  i16x8 h0[MlpCfg<D>::MT][D / 32], h1[MlpCfg<D>::MT][D / 32];
-  for (int tile = wave; tile < p.num_tiles; tile += nwaves) {
-    // An offset the compiler cannot see through: the weight fragments are
-    // re-read from LDS for every tile instead of being hoisted into
-    // registers (they do not fit next to the activations).
-    int woff = 0;
-    asm volatile("" : "+v"(woff));
-    load_x<D>(p, tile, lane, h0);
-    run_layers<D, L, 0, ACT>(p, sW + woff, tile, lane, h0, h1);
+  const int wave = blockIdx.x * G::WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwaves = gridDim.x * G::WAVES;
+  const Lane<D> c = lane_setup<D>(p, sW, lane);
+  u16x2 mx = (u16x2){0, 0};
+  int tile = wave;
+  // Three activation buffers in rotation: the x of the next tile is loaded
+  // into the third one when a tile starts, a whole tile ahead of its use.
+  HTile<D> ha, hb, hc;
+  if (tile < p.num_tiles) load_x<D>(p, c, tile, ha);
+  while (tile < p.num_tiles) {
+    int next = tile + nwaves;
+    if (next < p.num_tiles) load_x<D>(p, c, next, hc);
+    tile_chain<D, L, 0, ACT>(p, c, tile, ha, hb, mx);
+    tile = next;
+    if (tile >= p.num_tiles) break;
+    next = tile + nwaves;
+    if (next < p.num_tiles) load_x<D>(p, c, next, hb);
+    tile_chain<D, L, 0, ACT>(p, c, tile, hc, ha, mx);
+    tile = next;
+    if (tile >= p.num_tiles) break;
+    next = tile + nwaves;
+    if (next < p.num_tiles) load_x<D>(p, c, next, ha);
+    tile_chain<D, L, 0, ACT>(p, c, tile, hb, hc, mx);
+    tile = next;
+  }
+  if constexpr (ACT == ACT_SOFTPLUS && L > 1) {
+    // Some softplus argument of this wave's tiles may have exceeded the
+    // guard threshold: recompute all of the wave's tiles with the guarded
+    // form.  Tiles without such an argument get the same bits again; the
+    // others are corrected.  The first results are complete in memory before
+    // they are overwritten.
+    if (__builtin_amdgcn_ballot_w64(max(mx[0], mx[1]) >= SP_FLAG_B2_F16) != 0) {
+      wait_vmcnt0();
+      for (int t = wave; t < p.num_tiles; t += nwaves) tile_guarded<D, L, ACT>(p, c, t);
+    }
   }
 }
 
@@ -238,22 +542,23 @@ __global__ __launch_bounds__(threads<D>(), 4) void mlp_kernel(MlpParams p) {
 // the runtime for the compiled kernel (its VGPR and LDS use) and is cached.
 template <int D, int L, int ACT>
 hipError_t launch_dl(MlpParams p, int num_workgroups, int num_cus, hipStream_t stream) {
-  p.num_tiles = (int)(((int64_t)p.M + tile_rows<D>() - 1) / tile_rows<D>());
+  using G = Geo<D>;
+  p.num_tiles = (int)(((int64_t)p.M + G::TR - 1) / G::TR);
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mlp_kernel<D, L, ACT>, threads<D>(), 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mlp_kernel<D, L, ACT>, G::THREADS, 0);
     if (e != hipSuccess) return e;
     per_cu = n > 0 ? n : 1;
   }
   int nwg = num_workgroups;
   if (nwg <= 0) {
-    const int need = (p.num_tiles + MlpCfg<D>::WAVES - 1) / MlpCfg<D>::WAVES;
+    const int need = (p.num_tiles + G::WAVES - 1) / G::WAVES;
     const long cap = (long)num_cus * per_cu;
     nwg = need < cap ? need : (int)cap;
     if (nwg < 1) nwg = 1;
   }
-  hipLaunchKernelGGL((mlp_kernel<D, L, ACT>), dim3(nwg), dim3(threads<D>()), 0, stream, p);
+  hipLaunchKernelGGL((mlp_kernel<D, L, ACT>), dim3(nwg), dim3(G::THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -282,7 +587,6 @@ hipError_t launch_d(const MlpParams& p, int L, int nwg, int cus, hipStream_t str
 }
 
 }  // namespace
-
 
 hipError_t launch_mlp(const MlpParams& p, int D, int L, int act, int num_workgroups, int num_cus, hipStream_t stream) {
   if (D == 128) {

@@ -91,6 +91,29 @@ def test_grid_size_and_row_order_invariance(D, L):
     assert torch.equal(outp.view(torch.int16), outs[0][perm].view(torch.int16))
 
 
+@pytest.mark.parametrize("D,L", [(64, 5), (128, 3), (128, 2)])
+def test_guard_recompute_mixed_rows(D, L):
+    # A few rows with large inputs push softplus arguments past the guard at
+    # z = 20 and past the fp32 range of exp (z > 88.7); the waves that own
+    # them recompute their tiles with the guarded form.  Results must match
+    # the oracle, and be bit-identical whichever wave and grid gets the rows.
+    w = datagen.MLP3 if D == 128 else datagen.MLP5
+    M = 64 * 150 + 5
+    x, Ws = datagen.mlp_inputs(w, M=M, dims=(D,) * (L + 1))
+    big = [3, 700, 4001, M - 1]
+    x[big] = (40.0 * torch.sign(x[big].float())).to(torch.float16)
+    xg, Wg = to_gpu(x), [t.to("cuda") for t in Ws]
+    out = mk.mlp_forward(xg, Wg).cpu()
+    ref = oracle.mlp_forward(f64(x), [f64(t) for t in Ws])
+    assert_close(f64(out), ref, 2e-2, "mixed large rows D=%d L=%d" % (D, L))
+    for g in (1, 5, mk.device_cu_count()):
+        o = mk.mlp_forward(xg, Wg, num_workgroups=g).cpu()
+        assert torch.equal(o.view(torch.int16), out.view(torch.int16)), g
+    perm = torch.from_numpy(np.random.default_rng(11).permutation(M))
+    outp = mk.mlp_forward(to_gpu(x[perm]), Wg).cpu()
+    assert torch.equal(outp.view(torch.int16), out[perm].view(torch.int16))
+
+
 def test_unfused_baseline_matches_oracle():
     # per-layer GEMM (fp16 out) + separate softplus kernel: the unfused chain
     D, L, M = 128, 3, 3000
