@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--no-harness", action="store_true", help="skip the flushed median-of-100 sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mlp", action="store_true")
+    ap.add_argument("--prewarm-ms", type=float, default=500.0,
+                    help="untimed back-to-back running before the warmup steps of each timed case")
     ap.add_argument("--harness-iters", type=int, default=100)
     ap.add_argument("--harness-warmup-ms", type=float, default=1000.0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -129,10 +131,20 @@ def main():
         return fused, unfused
 
     # ----------------------------------------------------------------- timing
+    def prewarm(fn):
+        """Untimed: run fn back to back for --prewarm-ms so that the clocks
+        have settled under this load before the warmup steps."""
+        t0 = time.perf_counter()
+        while (time.perf_counter() - t0) * 1e3 < args.prewarm_ms:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
+
     def timed_steps(fn, steps, warmup):
         """K back-to-back steps: wall time per step, and the average launch
         duration from one pair of HIP events around the K launches on the
         launch stream (no per-launch event records between the kernels)."""
+        prewarm(fn)
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -244,8 +256,7 @@ def main():
                 continue
             print("bench: %s" % w.name, file=sys.stderr, flush=True)
             f, u = mlp_case(w)
-            # warm-up long enough for the clocks to settle under this load
-            ms, mk_ms = timed_steps(f, max(20, args.steps), max(10, int(200.0 / 0.15)))
+            ms, mk_ms = timed_steps(f, max(20, args.steps), 10)
             mlp_res[w.name] = {"rows_per_s": round(w.M / (ms * 1e-3), 1), "ms_per_call": round(ms, 5),
                                "roofline": roofline_mlp(w, mk_ms)}
             if not args.no_harness:

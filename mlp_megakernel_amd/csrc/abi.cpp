@@ -141,7 +141,7 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
     e = launch_gemm32(p, act_code(act), (hipStream_t)stream, cus);
   else
     e = launch_gemm16(p, in_dtype == COALESCE_BF16 ? DT_BF16 : DT_F16, out_dtype == COALESCE_F32 ? DT_F32 : (in_dtype == COALESCE_BF16 ? DT_BF16 : DT_F16),
-                      act_code(act), (hipStream_t)stream);
+                      act_code(act), (hipStream_t)stream, cus);
   if (e != hipSuccess) return device_fail(e, "GEMM launch");
   return ok();
 }

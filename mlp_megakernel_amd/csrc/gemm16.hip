@@ -2,29 +2,32 @@
 //
 // Y = act(A . B + bias) ("Coalesce" README, "Fusion study"): the bias add and
 // the activation run on the fp32 accumulators in registers and Y is written
-// once.  Tile plan (hand-budgeted against the 512 registers a lane has when
-// one wave runs per SIMD):
-//   * workgroup tile 256 (m) x 256 (n), K step 64, 4 waves in a 2 x 2 grid,
-//     each wave owning a 128 x 128 block of Y;
+// once.  Tile plan (hand-budgeted against the 256 registers a lane has when
+// two waves share a SIMD):
+//   * workgroup tile 256 (m) x 256 (n), K step 64, 8 waves in a 2 x 4 grid,
+//     each wave owning a 128 (m) x 64 (n) block of Y;
 //   * the wave computes Y^T blocks with v_mfma_f32_16x16x32 -- A operand =
 //     B^T (rows n), B operand = A^T (columns m) -- so every lane ends up with
-//     4 consecutive n of one row m, which makes bias loads and Y stores
-//     contiguous;
-//   * accumulators: 8 x 8 sub-tiles x 4 fp32 = 256 registers (AGPRs); operand
-//     fragments for one 32-deep k slice: 8 + 8 x 4 = 64 registers, double
+//     4 consecutive n of one row m, which makes bias loads contiguous;
+//   * accumulators: 4 x 8 sub-tiles x 4 fp32 = 128 registers; operand
+//     fragments for one 32-deep k slice: 4 + 8 x 4 = 48 registers, double
 //     buffered;
 //   * global -> LDS copies are 16-byte direct-to-LDS loads (no VGPR staging)
-//     addressed as an SGPR base plus a per-lane 32-bit offset fixed for the
-//     whole tile; two LDS stages of 64 KB; K step k + 2 is copied while step
-//     k + 1 is consumed;
+//     addressed as an SGPR base plus a per-lane 32-bit offset; two LDS stages
+//     of 64 KB; K step k + 2 is copied while step k + 1 is consumed;
 //   * B is K x N with n contiguous, so its MFMA fragments (8 consecutive k of
 //     one n) come from the transposing LDS read ds_read_b64_tr_b16;
 //   * LDS rows are XOR-swizzled in 16-byte chunks so that fragment reads
 //     spread over the banks;
-//   * each 32-deep slice is issued as 8 groups of {2 copies, 3 fragment reads
-//     of the next slice, 8 MFMAs}, fenced so the compiler keeps that
+//   * each 32-deep slice is issued as 4 groups of {2 copies, 8 MFMAs, the
+//     fragment reads of the next slice}, fenced so the compiler keeps that
 //     interleave: the copies never arrive as a burst that stalls the wave's
-//     in-order issue, and the MFMA pipe is fed between them.
+//     in-order issue, and the MFMA pipe is fed between them;
+//   * the epilogue stages each wave's block in the (then free) LDS and stores
+//     whole 128-byte lines of Y;
+//   * the kernel is persistent (one workgroup per CU walking its tiles), and
+//     the next tile's first copies are issued while the current tile's
+//     stores drain.
 // The last, partial K step (K not a multiple of 64) goes through masked
 // register loads that zero every element past K.  Rows past M read a
 // clamped (valid) row and are never stored; columns past N are masked.
@@ -72,41 +75,43 @@ struct Stage {
   T* b;
 };
 
-// Per-lane byte offsets of the 16 direct copies of one K step, relative to
-// the tile's A base (A + m0 * lda + k0) and B base (B + n0 + k0 * ldb).
-// Copy j < 8 fills A rows 64 w + 8 j .. + 7 (one 1 KB LDS block, lane l's 16
-// bytes at slot l); copy 8 + j fills B rows 16 w + 2 j, + 1.
+// Direct copies of one K step: copy j < CA fills A rows 8 (w CA + j) .. + 7
+// (one 1 KB LDS block, lane l's 16 bytes at slot l); copy CA + j fills B rows
+// 2 (w CB + j), + 1.  The per-lane byte offsets, relative to the tile's A base
+// (A + m0 * lda + k0) and B base (B + n0 + k0 * ldb), are recomputed at each
+// copy from the lane index (a few VALU operations) rather than held in
+// registers across the K loop.
 template <int NW>
 struct DmaPlan {
-  uint32_t a[Geo<NW>::CA];
-  uint32_t b[Geo<NW>::CB];
+  const GemmParams* p;
+  int m0, n0, w, lane;
 };
 
 template <typename T, int NW>
 __device__ __forceinline__ DmaPlan<NW> make_plan(const GemmParams& p, int m0, int n0, int w, int lane) {
+  return DmaPlan<NW>{&p, m0, n0, w, lane};
+}
+
+template <typename T, int NW>
+__device__ __forceinline__ uint32_t dma_offset(const DmaPlan<NW>& d, int j) {
   typedef Geo<NW> G;
-  DmaPlan<NW> d;
-  const int rsub = lane >> 3;
-  const int nlast = ((p.N - 1) >> 3) << 3;
+  const GemmParams& p = *d.p;
   // 32-bit arithmetic is exact here: the host checks 256 * lda and 64 * ldb
   // bytes fit in 32 bits.
-  const uint32_t lda_b = (uint32_t)p.lda * (uint32_t)sizeof(T);
-  const uint32_t ldb_b = (uint32_t)p.ldb * (uint32_t)sizeof(T);
-#pragma unroll
-  for (int j = 0; j < G::CA; ++j) {
-    const int row = (w * G::CA + j) * 8 + rsub;
-    const int cA = (lane & 7) ^ swzA(row);
-    const int gm = min(m0 + row, p.M - 1);
-    d.a[j] = (uint32_t)(gm - m0) * lda_b + (uint32_t)(cA * 8 * (int)sizeof(T));
+  if (j < G::CA) {
+    const uint32_t lda_b = (uint32_t)p.lda * (uint32_t)sizeof(T);
+    const int row = (d.w * G::CA + j) * 8 + (d.lane >> 3);
+    const int cA = (d.lane & 7) ^ swzA(row);
+    const int gm = min(d.m0 + row, p.M - 1);
+    return (uint32_t)(gm - d.m0) * lda_b + (uint32_t)(cA * 8 * (int)sizeof(T));
+  } else {
+    const uint32_t ldb_b = (uint32_t)p.ldb * (uint32_t)sizeof(T);
+    const int nlast = ((p.N - 1) >> 3) << 3;
+    const int row = (d.w * G::CB + j - G::CA) * 2 + (d.lane >> 5);
+    const int cB = (d.lane & 31) ^ swzB(row);
+    const int gn = min(d.n0 + cB * 8, nlast);
+    return (uint32_t)row * ldb_b + (uint32_t)((gn - d.n0) * (int)sizeof(T));
   }
-#pragma unroll
-  for (int j = 0; j < G::CB; ++j) {
-    const int row = (w * G::CB + j) * 2 + (lane >> 5);
-    const int cB = (lane & 31) ^ swzB(row);
-    const int gn = min(n0 + cB * 8, nlast);
-    d.b[j] = (uint32_t)row * ldb_b + (uint32_t)((gn - n0) * (int)sizeof(T));
-  }
-  return d;
 }
 
 // Uniform (SGPR) 64-bit base for a direct copy.
@@ -134,9 +139,9 @@ __device__ __forceinline__ void dma_copy(int j, const DmaPlan<NW>& d, const void
                                          Stage<T> st, int wu) {
   typedef Geo<NW> G;
   if (j < G::CA)
-    dma16_off(abase, d.a[j], lds_addr(st.a) + (uint32_t)((wu * G::CA + j) * 8) * (BK * (int)sizeof(T)));
+    dma16_off(abase, dma_offset<T, NW>(d, j), lds_addr(st.a) + (uint32_t)((wu * G::CA + j) * 8) * (BK * (int)sizeof(T)));
   else
-    dma16_off(bbase, d.b[j - G::CA],
+    dma16_off(bbase, dma_offset<T, NW>(d, j),
               lds_addr(st.b) + (uint32_t)((wu * G::CB + j - G::CA) * 2) * (BN * (int)sizeof(T)));
 }
 
@@ -224,8 +229,8 @@ __device__ __forceinline__ i16x4 read_af_half(Stage<T> st, int ks, int wn, int t
 }
 
 // One slice: NT groups of {2 copies of K step k + 2 when `copy` (a uniform
-// branch around the copies only), the next slice's fragment reads for
-// sub-tile t (and MT / NT of the m sub-tiles), the MT MFMAs of sub-tile t}.
+// branch around the copies only), the MT MFMAs of sub-tile t, the next
+// slice's fragment reads for sub-tile t (and MT / NT of the m sub-tiles)}.
 // A scheduling fence closes every group.  The MFMAs never sit inside a
 // branch, so the accumulators stay in AGPRs.  On the last K step the "next"
 // reads fetch stale but in-bounds LDS and are unused.
@@ -241,13 +246,16 @@ __device__ __forceinline__ void slice(const Frags<NW>& cur, f32x4 (&acc)[Geo<NW>
       dma_copy<T, NW>(2 * t, d, ab, bb, cst, wu);
       dma_copy<T, NW>(2 * t + 1, d, ab, bb, cst, wu);
     }
+#pragma unroll
+    for (int s = 0; s < G::MT; ++s) acc[t][s] = mfma16x16x32(cur.a[t], cur.b[s], acc[t][s], T());
+    // The reads after the MFMAs: nxt.a[t] then takes the registers of
+    // cur.a[t], which the MFMAs above were its last use of.
+    __builtin_amdgcn_sched_barrier(0);
     const i16x4 lo = read_af_half<T, NW>(rst, rks, wn, t, 0, lane);
     const i16x4 hi = read_af_half<T, NW>(rst, rks, wn, t, 1, lane);
     nxt.a[t] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
     for (int i = 0; i < BPG; ++i) nxt.b[t * BPG + i] = read_bf<T>(rst, rks, wm, t * BPG + i, lane);
-#pragma unroll
-    for (int s = 0; s < G::MT; ++s) acc[t][s] = mfma16x16x32(cur.a[t], cur.b[s], acc[t][s], T());
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -283,6 +291,77 @@ __device__ __forceinline__ void store4(TO* dst, f32x4 v, int valid) {
   }
 }
 
+// Epilogue through LDS for a wave's full 128 x WN block of a 16-bit Y.  The
+// accumulator layout gives each lane 4 consecutive n of one row (8 bytes),
+// 32 contiguous bytes per row per store instruction; instead the wave writes
+// act(acc + bias), rounded, into its own LDS region (row-major, 16-byte
+// chunks XOR-swizzled by row so that both the 8-byte writes and the 16-byte
+// reads are free of bank conflicts) and reads it back row-contiguously:
+// every store instruction then writes whole 128-byte lines of Y (8 rows of
+// 128 bytes, or 4 of 256).  Only the wave's own region is touched, so no
+// workgroup barrier is needed between the write and the read-back.
+template <int ROWB>
+__device__ __forceinline__ int stage_swz(int row) {
+  if constexpr (ROWB == 128)
+    return (row >> 1) & 7;
+  else
+    return row & 15;
+}
+
+template <typename T, typename TO, int ACT, bool HAS_BIAS, int NW>
+__device__ __forceinline__ void epilogue_staged(const GemmParams& p, const f32x4 (&acc)[Geo<NW>::NT][Geo<NW>::MT],
+                                                char* region, int wr0, int wc0, int lane) {
+  typedef Geo<NW> G;
+  constexpr int ROWB = G::WN * 2;      // bytes per staged row
+  constexpr int CPR = ROWB / 16;       // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;        // rows per 1 KB read-back
+  static_assert(ROWB == 128 || ROWB == 256, "staging swizzle assumes 128- or 256-byte rows");
+  const int q = lane & 15, b = lane >> 4;
+  const T* bias = (const T*)p.bias;
+  typedef TO to4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int t = 0; t < G::NT; ++t) {
+    f32x4 bv = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if constexpr (HAS_BIAS) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bv[r] = to_f32(bias[wc0 + 16 * t + 4 * b + r]);
+    }
+    const int chunk = 2 * t + (b >> 1);
+#pragma unroll
+    for (int s = 0; s < G::MT; ++s) {
+      const int row = 16 * s + q;
+      to4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = from_f32<TO>(apply_act<ACT>(acc[t][s][r] + bv[r]));
+      *(to4*)(region + row * ROWB + ((chunk ^ stage_swz<ROWB>(row)) << 4) + ((b & 1) << 3)) = o;
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  TO* Y = (TO*)p.Y;
+  const int rsub = lane / CPR, c = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 128 / RPI; ++i) {
+    const int row = RPI * i + rsub;
+    const u32x4 v = *(const u32x4*)(region + row * ROWB + ((c ^ stage_swz<ROWB>(row)) << 4));
+    *(u32x4*)(Y + (int64_t)(wr0 + row) * p.ldy + wc0 + 8 * c) = v;
+  }
+}
+
+// Workgroup barrier for LDS reuse: the wave's own LDS accesses are complete
+// (lgkmcnt 0) but its global stores and direct copies may still be in
+// flight (no vmcnt wait, unlike __syncthreads' fence); the "memory" clobber
+// keeps the compiler from moving memory accesses across it.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+#pragma clang diagnostic pop
+
+// Persistent kernel: one workgroup per CU (the two LDS stages take 128 KB)
+// walks the tiles v = blockIdx.x, + gridDim.x, ...  Once a tile's Y stores
+// are issued, the next tile's first two K steps are copied in without
+// waiting for them, so the copies' latency and the stores' drain overlap.
+// With gridDim.x a multiple of 8 a workgroup stays on one XCD, which is what
+// tile_coords assumes.
 template <typename T, typename TO, int ACT, bool HAS_BIAS, int NW>
 __global__ __launch_bounds__(Geo<NW>::THREADS, 1) void gemm16_kernel(GemmParams p) {
   typedef Geo<NW> G;
@@ -293,89 +372,140 @@ __global__ __launch_bounds__(Geo<NW>::THREADS, 1) void gemm16_kernel(GemmParams 
   __shared__ __attribute__((aligned(1024))) T sB[2][BK * BN];
   const Stage<T> st0{sA[0], sB[0]}, st1{sA[1], sB[1]};
 
-  int tm, tn;
-  tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int total = p.tiles_m * p.tiles_n;
+  int v = blockIdx.x;
+  if (v >= total) return;
+  const int lane0 = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int wm = w & 1, wn = w >> 1;
-
-  f32x4 acc[G::NT][G::MT];
-#pragma unroll
-  for (int t = 0; t < G::NT; ++t)
-#pragma unroll
-    for (int s = 0; s < G::MT; ++s) acc[t][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
   const int kfull = p.K / BK;
   const int ktiles = (p.K + BK - 1) / BK;
-  const DmaPlan<NW> d = make_plan<T, NW>(p, m0, n0, wu, lane);
-  Frags<NW> f0, f1;
-  if (ktiles > 0) {
-    if (kfull > 0)
-      dma_all<T, NW>(p, d, m0, n0, 0, st0, wu);
-    else
-      tail_fill<T, NW>(p, m0, n0, 0, st0, wu, lane);
-    wait_vmcnt0();
-    __syncthreads();
+
+  // Steps 0 and 1 of the tile at (m0, n0) into the two stages.
+  auto prologue = [&](int m0, int n0, const DmaPlan<NW>& d, int lane) {
+    if (ktiles > 0) {
+      if (kfull > 0)
+        dma_all<T, NW>(p, d, m0, n0, 0, st0, wu);
+      else
+        tail_fill<T, NW>(p, m0, n0, 0, st0, wu, lane);
+    }
     if (ktiles > 1) {
       if (kfull > 1)
         dma_all<T, NW>(p, d, m0, n0, BK, st1, wu);
       else
         tail_fill<T, NW>(p, m0, n0, BK, st1, wu, lane);
     }
-    read_all<T, NW>(f0, st0, 0, wm, wn, lane);
-  }
-  // Per K step k (stage cur; the other stage holds step k + 1 or is filling):
-  //   slice 0: MFMAs on f0 while f1 (slice 1 of cur) is read;
-  //   barrier: every wave has its fragments of cur, so cur is free, and the
-  //            copies of step k + 1 have landed;
-  //   slice 1: MFMAs on f1 while step k + 2 is copied into cur and f0
-  //            (slice 0 of step k + 1) is read.
-  for (int kt = 0; kt < ktiles; kt += 2) {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int k = kt + half;
-      if (k < ktiles) {
-        const Stage<T> cur = half ? st1 : st0;
-        const Stage<T> nxt = half ? st0 : st1;
-        slice<T, NW>(f0, acc, f1, cur, 1, wm, wn, lane, false, d, nullptr, nullptr, cur, wu);
-        if (k + 1 < ktiles) {
-          wait_vmcnt0();
-          __syncthreads();
-        }
-        if (k + 2 < ktiles && k + 2 >= kfull) tail_fill<T, NW>(p, m0, n0, (k + 2) * BK, cur, wu, lane);
-        const bool copy = k + 2 < kfull;
-        const void* ab = a_base<T>(p, m0, (k + 2) * BK);
-        const void* bb = b_base<T>(p, n0, (k + 2) * BK);
-        slice<T, NW>(f1, acc, f0, nxt, 0, wm, wn, lane, copy, d, ab, bb, cur, wu);
-      }
-    }
-  }
+  };
 
-  // Epilogue: + bias, activation, one rounding, one store.
-  const int q = lane & 15, b = lane >> 4;
-  const T* bias = (const T*)p.bias;
-  TO* Y = (TO*)p.Y;
+  int tm, tn;
+  tile_coords(v, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+  int m0 = tm * BM, n0 = tn * BN;
+  DmaPlan<NW> d = make_plan<T, NW>(p, m0, n0, wu, lane0);
+  prologue(m0, n0, d, lane0);
+
+  while (true) {
+    // The lane index through an opaque copy: everything derived from it
+    // (fragment and epilogue addresses) is recomputed per tile instead of
+    // being hoisted out of the tile loop and held in registers across the
+    // K loop, where there are none to spare.
+    int lane = lane0;
+    asm volatile("" : "+v"(lane));
+    const int q = lane & 15, b = lane >> 4;
+    f32x4 acc[G::NT][G::MT];
 #pragma unroll
-  for (int t = 0; t < G::NT; ++t) {
-    const int n = n0 + wn * G::WN + 16 * t + 4 * b;
-    if (n >= p.N) continue;
-    const int valid = min(4, p.N - n);
-    f32x4 bv = (f32x4){0.f, 0.f, 0.f, 0.f};
-    if constexpr (HAS_BIAS) {
+    for (int t = 0; t < G::NT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) bv[r] = r < valid ? to_f32(bias[n + r]) : 0.f;
+      for (int s = 0; s < G::MT; ++s) acc[t][s] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    Frags<NW> f0, f1;
+    if (ktiles > 0) {
+      wait_vmcnt0();
+      __syncthreads();
+      read_all<T, NW>(f0, st0, 0, wm, wn, lane);
     }
+    // Per K step k (stage cur; the other stage holds step k + 1 or is filling):
+    //   slice 0: MFMAs on f0 while f1 (slice 1 of cur) is read;
+    //   barrier: every wave has its fragments of cur, so cur is free, and the
+    //            copies of step k + 1 have landed;
+    //   slice 1: MFMAs on f1 while step k + 2 is copied into cur and f0
+    //            (slice 0 of step k + 1) is read.
+    for (int kt = 0; kt < ktiles; kt += 2) {
 #pragma unroll
-    for (int s = 0; s < G::MT; ++s) {
-      const int m = m0 + wm * 128 + 16 * s + q;
-      if (m < p.M) {
-        f32x4 v = acc[t][s];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = apply_act<ACT>(v[r] + bv[r]);
-        store4<TO>(Y + (int64_t)m * p.ldy + n, v, valid);
+      for (int half = 0; half < 2; ++half) {
+        const int k = kt + half;
+        if (k < ktiles) {
+          const Stage<T> cur = half ? st1 : st0;
+          const Stage<T> nxt = half ? st0 : st1;
+          slice<T, NW>(f0, acc, f1, cur, 1, wm, wn, lane, false, d, nullptr, nullptr, cur, wu);
+          if (k + 1 < ktiles) {
+            wait_vmcnt0();
+            __syncthreads();
+          }
+          if (k + 2 < ktiles && k + 2 >= kfull) tail_fill<T, NW>(p, m0, n0, (k + 2) * BK, cur, wu, lane);
+          const bool copy = k + 2 < kfull;
+          const void* ab = a_base<T>(p, m0, (k + 2) * BK);
+          const void* bb = b_base<T>(p, n0, (k + 2) * BK);
+          slice<T, NW>(f1, acc, f0, nxt, 0, wm, wn, lane, copy, d, ab, bb, cur, wu);
+        }
       }
     }
+
+    // Epilogue: + bias, activation, one rounding, one store.  A wave whose
+    // whole 128 x WN block lies inside a 16-bit Y stages it in LDS (the
+    // stages are free once every wave is past its last fragment read) and
+    // keeps it in registers as full rows.
+    const int wr0 = m0 + wm * 128, wc0 = n0 + wn * G::WN;
+    constexpr bool STAGE = sizeof(TO) == 2;
+    const bool staged = STAGE && wr0 + 128 <= p.M && wc0 + G::WN <= p.N;
+    __syncthreads();
+    if (staged) {
+      if constexpr (STAGE) {
+        // waves 0 .. NW/2 - 1 stage in the A stages, the others in the B
+        // stages (each 64 KB, NW/2 regions of 128 x WN x 2 bytes)
+        constexpr int RB = 128 * G::WN * 2;
+        static_assert((NW / 2) * RB <= (int)sizeof(sA), "staging regions exceed the stage buffers");
+        char* region = wu < NW / 2 ? (char*)sA + wu * RB : (char*)sB + (wu - NW / 2) * RB;
+        epilogue_staged<T, TO, ACT, HAS_BIAS, NW>(p, acc, region, wr0, wc0, lane);
+      }
+    } else {
+      // edge block (or 32-bit Y): element stores straight from the
+      // accumulators
+      const T* bias = (const T*)p.bias;
+      TO* Y = (TO*)p.Y;
+#pragma unroll
+      for (int t = 0; t < G::NT; ++t) {
+        const int n = n0 + wn * G::WN + 16 * t + 4 * b;
+        if (n >= p.N) continue;
+        const int valid = min(4, p.N - n);
+        f32x4 bv = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if constexpr (HAS_BIAS) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) bv[r] = r < valid ? to_f32(bias[n + r]) : 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < G::MT; ++s) {
+          const int m = m0 + wm * 128 + 16 * s + q;
+          if (m < p.M) {
+            f32x4 o = acc[t][s];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = apply_act<ACT>(o[r] + bv[r]);
+            store4<TO>(Y + (int64_t)m * p.ldy + n, o, valid);
+          }
+        }
+      }
+    }
+    // Every wave is done with the LDS (its stores may still be in flight):
+    // copy the next tile's first two K steps in while they drain.
+    lds_barrier();
+    const int vn = v + (int)gridDim.x;
+    if (vn < total) {
+      tile_coords(vn, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
+      m0 = tm * BM;
+      n0 = tn * BN;
+      d = make_plan<T, NW>(p, m0, n0, wu, lane);
+      prologue(m0, n0, d, lane);
+    }
+    if (vn >= total) break;
+    v = vn;
   }
 }
 
@@ -383,38 +513,53 @@ __global__ __launch_bounds__(Geo<NW>::THREADS, 1) void gemm16_kernel(GemmParams 
 #define GEMM16_WAVES 8
 #endif
 
-template <typename T, typename TO, int ACT>
-hipError_t launch_typed(GemmParams p, hipStream_t stream) {
+// Grid: min(#tiles, #CUs x workgroups per CU), the per-CU count from the
+// runtime for the compiled kernel, cached per instantiation.
+template <typename T, typename TO, int ACT, bool HAS_BIAS>
+hipError_t launch_bias(const GemmParams& p, hipStream_t stream, int num_cus) {
   constexpr int NW = GEMM16_WAVES;
-  dim3 grid(p.tiles_m * p.tiles_n), block(Geo<NW>::THREADS);
-  if (p.bias)
-    hipLaunchKernelGGL((gemm16_kernel<T, TO, ACT, true, NW>), grid, block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((gemm16_kernel<T, TO, ACT, false, NW>), grid, block, 0, stream, p);
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm16_kernel<T, TO, ACT, HAS_BIAS, NW>,
+                                                                Geo<NW>::THREADS, 0);
+    if (e != hipSuccess) return e;
+    per_cu = n > 0 ? n : 1;
+  }
+  const long total = (long)p.tiles_m * p.tiles_n;
+  const long cap = (long)num_cus * per_cu;
+  const int grid = (int)(total < cap ? total : cap);
+  hipLaunchKernelGGL((gemm16_kernel<T, TO, ACT, HAS_BIAS, NW>), dim3(grid), dim3(Geo<NW>::THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
+template <typename T, typename TO, int ACT>
+hipError_t launch_typed(GemmParams p, hipStream_t stream, int num_cus) {
+  if (p.bias) return launch_bias<T, TO, ACT, true>(p, stream, num_cus);
+  return launch_bias<T, TO, ACT, false>(p, stream, num_cus);
+}
+
 template <typename T, typename TO>
-hipError_t launch_act(GemmParams p, int act, hipStream_t stream) {
+hipError_t launch_act(GemmParams p, int act, hipStream_t stream, int num_cus) {
   switch (act) {
-    case ACT_GELU: return launch_typed<T, TO, ACT_GELU>(p, stream);
-    case ACT_SOFTPLUS: return launch_typed<T, TO, ACT_SOFTPLUS>(p, stream);
-    default: return launch_typed<T, TO, ACT_NONE>(p, stream);
+    case ACT_GELU: return launch_typed<T, TO, ACT_GELU>(p, stream, num_cus);
+    case ACT_SOFTPLUS: return launch_typed<T, TO, ACT_SOFTPLUS>(p, stream, num_cus);
+    default: return launch_typed<T, TO, ACT_NONE>(p, stream, num_cus);
   }
 }
 
 }  // namespace
 
-hipError_t launch_gemm16(GemmParams p, DType in, DType out, int act, hipStream_t stream) {
+hipError_t launch_gemm16(GemmParams p, DType in, DType out, int act, hipStream_t stream, int num_cus) {
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   p.group_m = 8;
   if (in == DT_BF16) {
-    if (out == DT_F32) return launch_act<__bf16, float>(p, act, stream);
-    return launch_act<__bf16, __bf16>(p, act, stream);
+    if (out == DT_F32) return launch_act<__bf16, float>(p, act, stream, num_cus);
+    return launch_act<__bf16, __bf16>(p, act, stream, num_cus);
   }
-  if (out == DT_F32) return launch_act<_Float16, float>(p, act, stream);
-  return launch_act<_Float16, _Float16>(p, act, stream);
+  if (out == DT_F32) return launch_act<_Float16, float>(p, act, stream, num_cus);
+  return launch_act<_Float16, _Float16>(p, act, stream, num_cus);
 }
 
 }  // namespace coalesce

@@ -20,7 +20,7 @@ struct GemmParams {
 
 // Each launcher picks its tile configuration, fills tiles_* and launches on
 // `stream`; it returns the hipError_t of the launch.
-hipError_t launch_gemm16(GemmParams p, DType in, DType out, int act, hipStream_t stream);
+hipError_t launch_gemm16(GemmParams p, DType in, DType out, int act, hipStream_t stream, int num_cus);
 hipError_t launch_gemm32(GemmParams p, int act, hipStream_t stream, int num_cus);
 
 struct MlpParams {
