@@ -50,7 +50,8 @@ typedef enum { COALESCE_F32 = 0, COALESCE_F16 = 1, COALESCE_BF16 = 2 } coalesce_
 typedef enum {
   COALESCE_ACT_NONE = 0,
   COALESCE_ACT_GELU_ERF = 1, /* 0.5 z (1 + erf(z / sqrt 2)) */
-  COALESCE_ACT_SOFTPLUS = 2  /* ln(1 + e^z), evaluated as z above 20 */
+  COALESCE_ACT_SOFTPLUS = 2, /* ln(1 + e^z), evaluated as z above 20 */
+  COALESCE_ACT_RELU = 3      /* z > 0 ? z : 0 (the matmul-relu of the "Coalesce" README's MLIR pipeline) */
 } coalesce_act;
 
 /*
@@ -92,7 +93,7 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
  *         dense row-major (the x @ W orientation)
  *   dims  HOST array of L + 1 widths
  *   out   device, M x dims[L] fp16, leading dimension ldo >= dims[L] (written)
- * Supported: dtype F16; hidden_act SOFTPLUS (or NONE: a linear chain); all
+ * Supported: dtype F16; hidden_act SOFTPLUS, RELU or NONE (a linear chain); all
  * widths equal to 64 (L = 1..8) or to 128 (L = 1..4).  M == 0 is a no-op.
  */
 coalesce_status coalesce_mlp_forward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims, int32_t L,

@@ -20,11 +20,11 @@ LIB_PATH = os.path.join(_HERE, "libcoalesce.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_DEVICE = 0, 1, 2, 3
 F32, F16, BF16 = 0, 1, 2
-ACT_NONE, ACT_GELU_ERF, ACT_SOFTPLUS = 0, 1, 2
+ACT_NONE, ACT_GELU_ERF, ACT_SOFTPLUS, ACT_RELU = 0, 1, 2, 3
 
 _DTYPES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 _ACTS = {"none": ACT_NONE, None: ACT_NONE, "gelu": ACT_GELU_ERF, "gelu_erf": ACT_GELU_ERF,
-         "softplus": ACT_SOFTPLUS}
+         "softplus": ACT_SOFTPLUS, "relu": ACT_RELU}
 
 # Every exported entry point of include/coalesce.h with its ctypes signature.
 _i64, _i32, _p, _sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t

@@ -57,7 +57,9 @@ coalesce_status current_cus(int* out) {
 }
 
 bool valid_dtype(int d) { return d == COALESCE_F32 || d == COALESCE_F16 || d == COALESCE_BF16; }
-bool valid_act(int a) { return a == COALESCE_ACT_NONE || a == COALESCE_ACT_GELU_ERF || a == COALESCE_ACT_SOFTPLUS; }
+bool valid_act(int a) {
+  return a == COALESCE_ACT_NONE || a == COALESCE_ACT_GELU_ERF || a == COALESCE_ACT_SOFTPLUS || a == COALESCE_ACT_RELU;
+}
 int64_t dsize(int d) { return d == COALESCE_F32 ? 4 : 2; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 const int64_t kMaxExtent = (int64_t)INT32_MAX;
@@ -74,7 +76,10 @@ Range span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t es) {
 bool overlap(Range a, Range b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
 
 int act_code(coalesce_act a) {
-  return a == COALESCE_ACT_GELU_ERF ? ACT_GELU : a == COALESCE_ACT_SOFTPLUS ? ACT_SOFTPLUS : ACT_NONE;
+  return a == COALESCE_ACT_GELU_ERF ? ACT_GELU
+         : a == COALESCE_ACT_SOFTPLUS ? ACT_SOFTPLUS
+         : a == COALESCE_ACT_RELU     ? ACT_RELU
+                                      : ACT_NONE;
 }
 
 }  // namespace
@@ -159,7 +164,7 @@ coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void
     if (dims[l] <= 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dims[%d] = %lld is not positive", l, (long long)dims[l]);
   if (dtype != COALESCE_F16) return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel takes fp16 only");
   if (hidden_act == COALESCE_ACT_GELU_ERF)
-    return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel supports softplus or no hidden activation");
+    return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel supports softplus, relu or no hidden activation");
   const int64_t D = dims[0];
   for (int l = 1; l <= L; ++l)
     if (dims[l] != D) return fail(COALESCE_ERR_UNSUPPORTED, "all MLP widths must be equal");

@@ -75,10 +75,15 @@ __device__ __forceinline__ float softplus_guarded(float z) {
   return z > 20.0f ? z : s;
 }
 
+// relu(z) = z > 0 ? z : 0; v_max_f32 against +0 (a NaN z gives 0, as the
+// comparison does).
+__device__ __forceinline__ float relu(float z) { return __builtin_fmaxf(z, 0.0f); }
+
 template <int ACT>
 __device__ __forceinline__ float apply_act(float z) {
   if constexpr (ACT == ACT_GELU) return gelu_erf(z);
   else if constexpr (ACT == ACT_SOFTPLUS) return softplus_guarded(z);
+  else if constexpr (ACT == ACT_RELU) return relu(z);
   else return z;
 }
 

@@ -122,6 +122,7 @@ hipError_t act_dispatch(const void* X, int64_t ldx, void* Y, int64_t ldy, int M,
   switch (act) {
     case ACT_GELU: return act_t<T, ACT_GELU>(X, ldx, Y, ldy, M, N, stream, num_cus);
     case ACT_SOFTPLUS: return act_t<T, ACT_SOFTPLUS>(X, ldx, Y, ldy, M, N, stream, num_cus);
+    case ACT_RELU: return act_t<T, ACT_RELU>(X, ldx, Y, ldy, M, N, stream, num_cus);
     default: return act_t<T, ACT_NONE>(X, ldx, Y, ldy, M, N, stream, num_cus);
   }
 }

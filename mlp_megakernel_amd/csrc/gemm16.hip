@@ -544,6 +544,7 @@ hipError_t launch_act(GemmParams p, int act, hipStream_t stream, int num_cus) {
   switch (act) {
     case ACT_GELU: return launch_typed<T, TO, ACT_GELU>(p, stream, num_cus);
     case ACT_SOFTPLUS: return launch_typed<T, TO, ACT_SOFTPLUS>(p, stream, num_cus);
+    case ACT_RELU: return launch_typed<T, TO, ACT_RELU>(p, stream, num_cus);
     default: return launch_typed<T, TO, ACT_NONE>(p, stream, num_cus);
   }
 }

@@ -241,6 +241,7 @@ hipError_t launch_act(GemmParams p, int act, hipStream_t stream) {
   switch (act) {
     case ACT_GELU: return launch_cfg<BM, BN, ACT_GELU>(p, stream);
     case ACT_SOFTPLUS: return launch_cfg<BM, BN, ACT_SOFTPLUS>(p, stream);
+    case ACT_RELU: return launch_cfg<BM, BN, ACT_RELU>(p, stream);
     default: return launch_cfg<BM, BN, ACT_NONE>(p, stream);
   }
 }

@@ -6,7 +6,7 @@
 namespace coalesce {
 
 enum DType { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
-enum Act { ACT_NONE = 0, ACT_GELU = 1, ACT_SOFTPLUS = 2 };
+enum Act { ACT_NONE = 0, ACT_GELU = 1, ACT_SOFTPLUS = 2, ACT_RELU = 3 };
 
 struct GemmParams {
   const void* A;

@@ -318,6 +318,8 @@ __device__ __forceinline__ void hidden_layer(const Lane<D>& c, const HTile<D>& h
           if constexpr (SP) {
             if constexpr (!IN_B2) a *= 1.44269504088896341f;
             v[r] = softplus_b2_fast(a);
+          } else if constexpr (ACT == ACT_RELU) {
+            v[r] = relu(a);
           } else {
             v[r] = a;
           }
@@ -591,9 +593,11 @@ hipError_t launch_d(const MlpParams& p, int L, int nwg, int cus, hipStream_t str
 hipError_t launch_mlp(const MlpParams& p, int D, int L, int act, int num_workgroups, int num_cus, hipStream_t stream) {
   if (D == 128) {
     if (act == ACT_NONE) return launch_d<128, ACT_NONE>(p, L, num_workgroups, num_cus, stream);
+    if (act == ACT_RELU) return launch_d<128, ACT_RELU>(p, L, num_workgroups, num_cus, stream);
     return launch_d<128, ACT_SOFTPLUS>(p, L, num_workgroups, num_cus, stream);
   }
   if (act == ACT_NONE) return launch_d<64, ACT_NONE>(p, L, num_workgroups, num_cus, stream);
+  if (act == ACT_RELU) return launch_d<64, ACT_RELU>(p, L, num_workgroups, num_cus, stream);
   return launch_d<64, ACT_SOFTPLUS>(p, L, num_workgroups, num_cus, stream);
 }
 

@@ -26,8 +26,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "coalesce_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
-ACT_NONE, ACT_GELU_ERF, ACT_SOFTPLUS = 0, 1, 2
-_ACTS = {"none": ACT_NONE, "gelu": ACT_GELU_ERF, "gelu_erf": ACT_GELU_ERF, "softplus": ACT_SOFTPLUS}
+ACT_NONE, ACT_GELU_ERF, ACT_SOFTPLUS, ACT_RELU = 0, 1, 2, 3
+_ACTS = {"none": ACT_NONE, "gelu": ACT_GELU_ERF, "gelu_erf": ACT_GELU_ERF, "softplus": ACT_SOFTPLUS, "relu": ACT_RELU}
 
 _lib = None
 

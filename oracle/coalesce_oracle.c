@@ -38,7 +38,7 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_ACT_NONE = 0, ORACLE_ACT_GELU_ERF = 1, ORACLE_ACT_SOFTPLUS = 2 };
+enum { ORACLE_ACT_NONE = 0, ORACLE_ACT_GELU_ERF = 1, ORACLE_ACT_SOFTPLUS = 2, ORACLE_ACT_RELU = 3 };
 
 /* GELU, erf form ("Coalesce" README, notes: use erf, not tanh). */
 double oracle_gelu(double z) { return 0.5 * z * (1.0 + erf(z / sqrt(2.0))); }
@@ -56,6 +56,7 @@ double oracle_softplus(double z) {
 static double apply_act(double z, int act) {
   if (act == ORACLE_ACT_GELU_ERF) return oracle_gelu(z);
   if (act == ORACLE_ACT_SOFTPLUS) return oracle_softplus(z);
+  if (act == ORACLE_ACT_RELU) return z > 0.0 ? z : 0.0; /* the matmul-relu of the "Coalesce" README */
   return z;
 }
 

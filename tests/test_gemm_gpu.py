@@ -49,8 +49,19 @@ def test_integer_inputs_bit_exact(in_dt, out_dt):
                            ref_t.view(torch.int32 if out_dt == "f32" else torch.int16)), (M, N, K)
 
 
+@pytest.mark.parametrize("in_dt,out_dt", [("f32", "f32"), ("bf16", "f32"), ("f16", "f32")])
+def test_integer_inputs_relu_bit_exact(in_dt, out_dt):
+    # relu of an exact integer sum is exact
+    for (M, N, K) in [(1, 1, 1), (17, 33, 65), (257, 129, 127), (300, 520, 260)]:
+        progress("exact relu %s->%s M=%d N=%d K=%d" % (in_dt, out_dt, M, N, K))
+        A, B, bias = _integer_inputs(M, N, K, in_dt)
+        ref = oracle.gemm_bias_act(f64(A), f64(B), f64(bias), act="relu")
+        Y = mk.gemm_bias_act(to_gpu(A), to_gpu(B), bias.to("cuda"), act="relu", out_dtype=DT[out_dt])
+        assert np.array_equal(f64(Y), ref), (M, N, K)
+
+
 @pytest.mark.parametrize("in_dt,out_dt", [("f32", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32")])
-@pytest.mark.parametrize("act", ["gelu", "softplus", "none"])
+@pytest.mark.parametrize("act", ["gelu", "softplus", "relu", "none"])
 def test_random_parity(in_dt, out_dt, act):
     shapes = [(100, 70, 50), (300, 520, 260), (513, 300, 1000)]
     for (M, N, K) in shapes:

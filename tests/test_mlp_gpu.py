@@ -37,6 +37,23 @@ def test_linear_chain_signed_permutations_exact(D, L):
     assert np.array_equal(f64(out), ref), (D, L)
 
 
+@pytest.mark.parametrize("D,L", [(64, 3), (64, 5), (128, 2), (128, 3)])
+def test_relu_chains(D, L):
+    # signed-permutation weights and integer x: every layer is exact in fp16
+    M = 200
+    x = datagen.integer_matrix((M, D), 3, 7, 17, 8, "f16")
+    Ws = [_signed_perm(D, 300 * L + l) for l in range(L)]
+    out = mk.mlp_forward(to_gpu(x), [w.to("cuda") for w in Ws], hidden_act="relu")
+    ref = oracle.mlp_forward(f64(x), [f64(w) for w in Ws], hidden_act="relu")
+    assert np.array_equal(f64(out), ref), (D, L)
+    # random inputs, ragged rows, the 2e-2 gate
+    w = datagen.MLP3 if D == 128 else datagen.MLP5
+    x, Ws = datagen.mlp_inputs(w, M=1000, dims=(D,) * (L + 1))
+    out = mk.mlp_forward(to_gpu(x), [t.to("cuda") for t in Ws], hidden_act="relu")
+    ref = oracle.mlp_forward(f64(x), [f64(t) for t in Ws], hidden_act="relu")
+    assert_close(f64(out), ref, 2e-2, "relu D=%d L=%d" % (D, L))
+
+
 @pytest.mark.parametrize("D,L", CASES)
 def test_random_parity_ragged_rows(D, L):
     w = datagen.MLP3 if D == 128 else datagen.MLP5

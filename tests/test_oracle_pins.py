@@ -165,6 +165,7 @@ def test_gemm_pages_fill_patterns_exact_rational():
 
 @pytest.mark.parametrize("act,f", [("gelu", lambda b: b * scipy.special.ndtr(b)),
                                    ("softplus", lambda b: np.logaddexp(0.0, b)),
+                                   ("relu", lambda b: np.where(b > 0, b, 0.0)),
                                    ("none", lambda b: b)])
 def test_gemm_k0_is_act_of_bias_per_column(act, f):
     M, N = 4, 6
@@ -278,6 +279,28 @@ def test_mlp_rows_permute_and_subset():
     perm = np.random.default_rng(0).permutation(50)
     assert np.array_equal(oracle.mlp_forward(x[perm], Ws), full[perm])
     assert np.array_equal(oracle.mlp_forward(x, Ws, rows=perm[:9]), full[perm[:9]])
+
+
+def test_relu_chain_by_hand_and_identity_closed_form():
+    # 1 row, widths 2 -> 2 -> 1, relu between layers, evaluated by hand:
+    # z1 = [1*1 + 2*0.25, 1*(-1) + 2*(-0.5)] = [1.5, -2], h1 = [1.5, 0],
+    # out = 1.5*3 + 0*(-1) = 4.5
+    x = np.array([[1.0, 2.0]])
+    W1 = np.array([[1.0, -1.0], [0.25, -0.5]])
+    W2 = np.array([[3.0], [-1.0]])
+    assert oracle.mlp_forward(x, [W1, W2], hidden_act="relu")[0, 0] == 4.5
+    # relu is idempotent: identity weights give out = relu(x) for any L >= 2
+    xs = np.linspace(-3, 3, 24).reshape(3, 8)
+    I = np.eye(8)
+    for L in (2, 3, 5):
+        got = oracle.mlp_forward(xs, [I] * L, hidden_act="relu")
+        assert np.array_equal(got, np.where(xs > 0, xs, 0.0))
+    # GEMM epilogue: relu(z) - relu(-z) = z, and relu(z) >= 0
+    A = np.linspace(-2, 2, 15).reshape(5, 3)
+    B = np.array([[1.0, -0.5], [2.0, 0.0], [-1.0, 3.0]])
+    pos = oracle.gemm_bias_act(A, B, None, act="relu")
+    neg = oracle.gemm_bias_act(-A, B, None, act="relu")
+    assert np.all(pos >= 0) and np.allclose(pos - neg, oracle.gemm_bias_act(A, B, None, act="none"), atol=1e-15)
 
 
 def test_mlp_small_chain_by_hand():
