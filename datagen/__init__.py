@@ -13,7 +13,8 @@ Recipe (the same everywhere):
     deviation, so pre-activations come out at about unit scale);
   * values are drawn in float64, rounded to float32 (round to nearest even),
     then to bf16/fp16 (round to nearest even) when the input type is 16-bit;
-  * tensor ids: A = 1, B = 2, bias = 3, x = 10, W_l = 10 + l (l = 1..L).
+  * tensor ids: A = 1, B = 2, bias = 3, x = 10, W_l = 10 + l (l = 1..L),
+    the upstream gradient dout of the MLP backward = 30.
 
 Workloads (``WORKLOADS``) carry the shapes and value distributions of the
 pages' problems: the FP32 square GEMM + bias + GELU shapes of the "Coalesce"
@@ -29,6 +30,7 @@ import numpy as np
 import torch
 
 TENSOR_A, TENSOR_B, TENSOR_BIAS, TENSOR_X = 1, 2, 3, 10
+TENSOR_DOUT = 30
 
 
 def tensor_w(layer: int) -> int:
@@ -189,6 +191,14 @@ def mlp_inputs(w: MlpWorkload, M: Optional[int] = None, dims: Optional[Sequence[
     Ws = [normal(w.seed_id, tensor_w(l + 1), (dims[l], dims[l + 1]), 1.0 / np.sqrt(dims[l]), w.dtype)
           for l in range(len(dims) - 1)]
     return x, Ws
+
+
+def mlp_grad_output(w: MlpWorkload, M: Optional[int] = None, dims: Optional[Sequence[int]] = None):
+    """dout (M x d_L, the MLP's dtype) ~ N(0, 1): the upstream gradient fed to
+    the backward (a unit-scale stand-in for dL/d(out) of a training loss)."""
+    M = w.M if M is None else M
+    dims = tuple(w.dims if dims is None else dims)
+    return normal(w.seed_id, TENSOR_DOUT, (M, dims[-1]), 1.0, w.dtype)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

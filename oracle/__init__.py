@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle for the fused GEMM epilogue and the softplus MLP chain.
+"""Plain fp64 CPU oracle for the fused GEMM epilogue and the softplus MLP chain
+(forward, and the training pair: forward with stored activations, backward).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this package.  The HIP library
@@ -64,6 +65,12 @@ def _load():
     lib.oracle_gemm_bias_act_at.argtypes = [p, p, p, p, p, i64, p, i64, i64, i64, i32, i32]
     lib.oracle_mlp_forward.restype = i32
     lib.oracle_mlp_forward.argtypes = [p, p, p, i32, p, p, i64, i64, i32, i32]
+    lib.oracle_act_deriv.restype = d
+    lib.oracle_act_deriv.argtypes = [d, i32]
+    lib.oracle_mlp_forward_train.restype = i32
+    lib.oracle_mlp_forward_train.argtypes = [p, p, p, i32, p, p, i64, i32, i32]
+    lib.oracle_mlp_backward.restype = i32
+    lib.oracle_mlp_backward.argtypes = [p, p, p, i32, p, p, p, i64, i32, i32]
     _lib = lib
     return lib
 
@@ -189,3 +196,70 @@ def mlp_forward(x, weights: Sequence, rows: Optional[Sequence[int]] = None, hidd
     if rc != 0:
         raise ValueError("oracle_mlp_forward rejected its arguments")
     return out
+
+
+def _chain(x, weights):
+    x = _f64(x)
+    Ws = [_f64(w) for w in weights]
+    if len(Ws) < 1:
+        raise ValueError("need at least one layer")
+    if len(Ws) > 8:
+        raise ValueError("at most 8 layers")
+    M, d0 = x.shape
+    dims = [d0]
+    for w in Ws:
+        if w.shape[0] != dims[-1]:
+            raise ValueError("layer widths do not chain")
+        dims.append(w.shape[1])
+    return x, Ws, M, dims
+
+
+def act_deriv(z, act="softplus") -> np.ndarray:
+    """d act / dz: the logistic sigmoid for softplus, the step for relu, 1 for none."""
+    lib = _load()
+    z = np.asarray(z, dtype=np.float64)
+    a = _act(act)
+    return np.vectorize(lambda v: lib.oracle_act_deriv(v, a), otypes=[np.float64])(z)
+
+
+def mlp_forward_train(x, weights: Sequence, hidden_act="softplus", nthreads: int = 0):
+    """(out, [h_1 .. h_{L-1}]): the forward chain and the hidden activations
+    h_l = act(z_l) that the training forward stores for the backward
+    ("MLP Megakernel" README, "Key ideas")."""
+    lib = _load()
+    x, Ws, M, dims = _chain(x, weights)
+    L = len(Ws)
+    out = np.empty((M, dims[-1]), dtype=np.float64)
+    acts = [np.empty((M, dims[l]), dtype=np.float64) for l in range(1, L)]
+    wptrs = (ctypes.c_void_p * L)(*[w.ctypes.data for w in Ws])
+    aptrs = (ctypes.c_void_p * max(1, L - 1))(*[a.ctypes.data for a in acts])
+    dims_arr = np.asarray(dims, dtype=np.int64)
+    rc = lib.oracle_mlp_forward_train(_ptr(x), ctypes.cast(wptrs, ctypes.c_void_p), _ptr(dims_arr), L, _ptr(out),
+                                      ctypes.cast(aptrs, ctypes.c_void_p) if L > 1 else None, M,
+                                      _act(hidden_act), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_mlp_forward_train rejected its arguments")
+    return out, acts
+
+
+def mlp_backward(x, weights: Sequence, dout, hidden_act="softplus", want_dx: bool = True, nthreads: int = 0):
+    """([dW_1 .. dW_L], dx or None): gradients of sum(dout * out) with respect
+    to every weight and to x, by the chain rule in fp64, the forward
+    recomputed from x and W ("MLP Megakernel" README, "Key ideas"; the
+    backward multiplies by softplus' derivative, the logistic sigmoid)."""
+    lib = _load()
+    x, Ws, M, dims = _chain(x, weights)
+    L = len(Ws)
+    g = _f64(dout)
+    if g.shape != (M, dims[-1]):
+        raise ValueError("dout must be M x dims[L]")
+    dWs = [np.empty((dims[l], dims[l + 1]), dtype=np.float64) for l in range(L)]
+    dx = np.empty((M, dims[0]), dtype=np.float64) if want_dx else None
+    wptrs = (ctypes.c_void_p * L)(*[w.ctypes.data for w in Ws])
+    gptrs = (ctypes.c_void_p * L)(*[w.ctypes.data for w in dWs])
+    dims_arr = np.asarray(dims, dtype=np.int64)
+    rc = lib.oracle_mlp_backward(_ptr(x), ctypes.cast(wptrs, ctypes.c_void_p), _ptr(dims_arr), L, _ptr(g),
+                                 ctypes.cast(gptrs, ctypes.c_void_p), _ptr(dx), M, _act(hidden_act), nthreads)
+    if rc != 0:
+        raise ValueError("oracle_mlp_backward rejected its arguments")
+    return dWs, dx

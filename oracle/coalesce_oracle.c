@@ -20,6 +20,10 @@
  *  - same README, "Ablation Study / Key findings": softplus(x) = log(1 + e^x)
  *    (the page's guarded form switches to x above 20; the oracle instead
  *    evaluates the exact function in fp64, see oracle_softplus).
+ *  - same README, "Key ideas" (training: the forward keeps the hidden
+ *    activations, the backward multiplies by the derivative of softplus) and
+ *    the quick start's out.sum().backward(): the gradients of the chain with
+ *    respect to every W_l and to x, given dL/d(out), by the chain rule.
  *
  * Everything is computed in double precision from inputs that the caller has
  * already widened exactly to double (bf16/fp16/fp32 -> fp64 is exact).  The
@@ -182,5 +186,171 @@ int oracle_mlp_forward(const double* x, const double* const* W, const int64_t* d
     free(h);
     free(z);
   }
+  return bad ? -1 : 0;
+}
+
+/* Derivative of the hidden activation at z.  softplus: d/dz ln(1 + e^z) =
+ * e^z / (1 + e^z), the logistic sigmoid, evaluated without overflow on either
+ * side.  relu: 1 for z > 0, else 0 (0 at the kink z = 0 itself).  none: 1. */
+double oracle_act_deriv(double z, int act) {
+  if (act == ORACLE_ACT_SOFTPLUS) {
+    if (z >= 0.0) return 1.0 / (1.0 + exp(-z));
+    double e = exp(z);
+    return e / (1.0 + e);
+  }
+  if (act == ORACLE_ACT_RELU) return z > 0.0 ? 1.0 : 0.0;
+  return 1.0;
+}
+
+static int check_chain(const double* const* W, const int64_t* dims, int L, int64_t* maxw) {
+  if (L < 1 || !dims || !W) return -1;
+  int64_t m = 0;
+  for (int l = 0; l <= L; ++l) {
+    if (dims[l] < 0) return -1;
+    if (dims[l] > m) m = dims[l];
+  }
+  for (int l = 0; l < L; ++l)
+    if (dims[l] > 0 && dims[l + 1] > 0 && !W[l]) return -1;
+  *maxw = m;
+  return 0;
+}
+
+/* z = h W for one row: z[j] = sum_k h[k] W[k][j], k in order. */
+static void row_times_w(const double* h, const double* w, int64_t din, int64_t dout, double* z) {
+  for (int64_t j = 0; j < dout; ++j) {
+    double acc = 0.0;
+    for (int64_t k = 0; k < din; ++k) acc += h[k] * w[k * dout + j];
+    z[j] = acc;
+  }
+}
+
+/* g = d W^T for one row: g[k] = sum_j d[j] W[k][j], j in order. */
+static void row_times_wt(const double* d, const double* w, int64_t din, int64_t dout, double* g) {
+  for (int64_t k = 0; k < din; ++k) {
+    double acc = 0.0;
+    for (int64_t j = 0; j < dout; ++j) acc += d[j] * w[k * dout + j];
+    g[k] = acc;
+  }
+}
+
+/*
+ * Training forward: the chain of oracle_mlp_forward over all M rows, and
+ * acts[l - 1] (l = 1..L-1, each M x dims[l], dense) receives the hidden
+ * activation h_l = act(z_l) that the backward consumes.  acts may be NULL
+ * when L == 1.
+ */
+int oracle_mlp_forward_train(const double* x, const double* const* W, const int64_t* dims, int L, double* out,
+                             double* const* acts, int64_t M, int hidden_act, int nthreads) {
+  int64_t maxw = 0;
+  if (M < 0 || check_chain(W, dims, L, &maxw)) return -1;
+  if (M > 0 && (!x || !out || (L > 1 && !acts))) return -1;
+  for (int l = 1; l < L; ++l)
+    if (M > 0 && dims[l] > 0 && !acts[l - 1]) return -1;
+  if (nthreads <= 0) nthreads = oracle_max_threads();
+  int bad = 0;
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+  {
+    double* h = (double*)malloc((size_t)(maxw > 0 ? maxw : 1) * sizeof(double));
+    double* z = (double*)malloc((size_t)(maxw > 0 ? maxw : 1) * sizeof(double));
+    if (!h || !z) bad = 1;
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t r = 0; r < M; ++r) {
+      if (!h || !z) continue;
+      memcpy(h, x + r * dims[0], (size_t)dims[0] * sizeof(double));
+      for (int l = 0; l < L; ++l) {
+        row_times_w(h, W[l], dims[l], dims[l + 1], z);
+        if (l == L - 1) {
+          memcpy(out + r * dims[L], z, (size_t)dims[L] * sizeof(double));
+        } else {
+          for (int64_t j = 0; j < dims[l + 1]; ++j) h[j] = apply_act(z[j], hidden_act);
+          memcpy(acts[l] + r * dims[l + 1], h, (size_t)dims[l + 1] * sizeof(double));
+        }
+      }
+    }
+    free(h);
+    free(z);
+  }
+  return bad ? -1 : 0;
+}
+
+/*
+ * Backward of the chain by the chain rule, all in fp64.  With W[l] mapping
+ * width dims[l] to dims[l + 1] (layer l + 1 of the page), h_0 = x,
+ * z_{l+1} = h_l W[l], h_l = act(z_l) (0 < l < L), out = z_L and the upstream
+ * gradient dz_L = dout (M x dims[L]):
+ *   dW[l]  = h_l^T dz_{l+1}                       (dims[l] x dims[l+1])
+ *   dh_l   = dz_{l+1} W[l]^T
+ *   dz_l   = dh_l * act'(z_l)   elementwise, 0 < l < L
+ *   dx     = dh_0                                  (M x dims[0]; skipped when dx is NULL)
+ * The forward is recomputed here from x and W (the oracle takes no stored
+ * activations).  Every dW element sums its row terms for r = 0, 1, ..., M-1
+ * in that order, so the result does not depend on the thread count; rows
+ * are processed in blocks to bound the memory.  Returns 0, or -1 on a bad
+ * argument.
+ */
+int oracle_mlp_backward(const double* x, const double* const* W, const int64_t* dims, int L, const double* dout,
+                        double* const* dW, double* dx, int64_t M, int hidden_act, int nthreads) {
+  int64_t maxw = 0;
+  if (M < 0 || check_chain(W, dims, L, &maxw) || !dW) return -1;
+  for (int l = 0; l < L; ++l)
+    if (dims[l] > 0 && dims[l + 1] > 0 && !dW[l]) return -1;
+  if (M > 0 && (!x || !dout)) return -1;
+  if (nthreads <= 0) nthreads = oracle_max_threads();
+  for (int l = 0; l < L; ++l) memset(dW[l], 0, (size_t)(dims[l] * dims[l + 1]) * sizeof(double));
+  if (M == 0) return 0;
+  /* per-row record: h_0..h_{L-1}, then dz_1..dz_L, then z_1..z_{L-1} */
+  int64_t hoff[9], doff[9], zoff[9], S = 0;
+  if (L > 8) return -1;
+  for (int l = 0; l < L; ++l) { hoff[l] = S; S += dims[l]; }
+  for (int l = 1; l <= L; ++l) { doff[l] = S; S += dims[l]; }
+  for (int l = 1; l < L; ++l) { zoff[l] = S; S += dims[l]; }
+  const int64_t BR = 2048;
+  double* buf = (double*)malloc((size_t)(BR * (S > 0 ? S : 1)) * sizeof(double));
+  if (!buf) return -1;
+  int bad = 0;
+  for (int64_t r0 = 0; r0 < M; r0 += BR) {
+    const int64_t nb = M - r0 < BR ? M - r0 : BR;
+#pragma omp parallel num_threads(nthreads) reduction(| : bad)
+    {
+      double* g = (double*)malloc((size_t)(maxw > 0 ? maxw : 1) * sizeof(double));
+      if (!g) bad = 1;
+#pragma omp for schedule(dynamic, 16)
+      for (int64_t b = 0; b < nb; ++b) {
+        if (!g) continue;
+        const int64_t r = r0 + b;
+        double* rec = buf + b * S;
+        memcpy(rec + hoff[0], x + r * dims[0], (size_t)dims[0] * sizeof(double));
+        for (int l = 0; l < L - 1; ++l) {
+          double* z = rec + zoff[l + 1];
+          row_times_w(rec + hoff[l], W[l], dims[l], dims[l + 1], z);
+          for (int64_t j = 0; j < dims[l + 1]; ++j) rec[hoff[l + 1] + j] = apply_act(z[j], hidden_act);
+        }
+        memcpy(rec + doff[L], dout + r * dims[L], (size_t)dims[L] * sizeof(double));
+        for (int l = L - 1; l >= 0; --l) {
+          row_times_wt(rec + doff[l + 1], W[l], dims[l], dims[l + 1], g);
+          if (l > 0) {
+            for (int64_t k = 0; k < dims[l]; ++k)
+              rec[doff[l] + k] = g[k] * oracle_act_deriv(rec[zoff[l] + k], hidden_act);
+          } else if (dx) {
+            memcpy(dx + r * dims[0], g, (size_t)dims[0] * sizeof(double));
+          }
+        }
+      }
+      free(g);
+    }
+    /* dW[l][k][n] += h_l[r][k] dz_{l+1}[r][n] for the block's rows in order */
+    for (int l = 0; l < L; ++l) {
+      const int64_t din = dims[l], dn = dims[l + 1];
+      double* dw = dW[l];
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+      for (int64_t k = 0; k < din; ++k)
+        for (int64_t b = 0; b < nb; ++b) {
+          const double a = buf[b * S + hoff[l] + k];
+          const double* d = buf + b * S + doff[l + 1];
+          for (int64_t n = 0; n < dn; ++n) dw[k * dn + n] += a * d[n];
+        }
+    }
+  }
+  free(buf);
   return bad ? -1 : 0;
 }
