@@ -111,6 +111,71 @@ coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void
                                           coalesce_act hidden_act, int64_t num_workgroups, void* stream);
 
 /*
+ * Training forward ("MLP Megakernel" README, "Key ideas": for training, the
+ * forward keeps the hidden activations in fp32 so that the backward's
+ * softplus derivative loses nothing).  Computes out exactly as
+ * coalesce_mlp_forward does (the same bits) and also writes, for
+ * l = 0 .. L-2,
+ *   acts[l] = h_{l+1} = act(z_{l+1})
+ * in fp32: the activation as computed on the fp32 accumulators, before its
+ * rounding to the next layer's fp16 operand.
+ *   acts  HOST array of L - 1 device pointers, each M x dims[l+1] fp32 with
+ *         leading dimension lda (D <= lda <= 2^24, 16-byte aligned rows),
+ *         not overlapping x, out, the weights or each other; may be NULL
+ *         when L == 1.
+ * Other arguments, support and errors as coalesce_mlp_forward.
+ */
+coalesce_status coalesce_mlp_forward_train(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                           int32_t L, void* out, int64_t ldo, float* const* acts, int64_t lda,
+                                           int64_t M, coalesce_dtype dtype, coalesce_act hidden_act, void* stream);
+
+/*
+ * Device workspace in bytes that coalesce_mlp_backward needs for this chain
+ * on the current device (one partial weight gradient per compute unit).
+ * Returns 0 for an unsupported width or depth or a failed device query.
+ */
+size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L);
+
+/*
+ * Backward of the MLP chain ("MLP Megakernel" README, "Key ideas": the
+ * backward reads the fp32 activations stored by the training forward,
+ * multiplies by the derivative of softplus, and casts to fp16 only for the
+ * matrix-core operands; the weight gradients come out of one fused kernel).
+ * With h_0 = x, h_l = acts[l-1], the upstream gradient dz_L = dout and
+ * 0-based layers l = L-1 .. 0:
+ *   dW[l] = h_l^T dz_{l+1}               (fp32, summed over all M rows)
+ *   dz_l  = (dz_{l+1} W_l^T) * act'(z_l)  (l > 0)
+ *   dx    = dz_1 W_0^T                    (when dx is not NULL)
+ * act'(z_l) is recovered from h_l: softplus -> 1 - exp(-h_l) (the logistic
+ * sigmoid of z_l), relu -> 1 where h_l > 0 else 0, none -> 1.  h_l and
+ * dz_l are rounded to fp16 (nearest even) as MFMA operands; products
+ * accumulate in fp32.
+ *   x         device, M x D fp16 (ldx)          the forward's input
+ *   W, dims   as coalesce_mlp_forward
+ *   acts      HOST array of L - 1 device pointers, M x D fp32 (lda), as
+ *             written by coalesce_mlp_forward_train; may be NULL when L == 1
+ *   dout      device, M x D fp16 (ldd)          dLoss/d(out)
+ *   dW        HOST array of L device pointers, each D x D fp32, dense
+ *             row-major (the x @ W orientation of W[l]), overwritten
+ *   dx        device, M x D fp16 (ldq), written; or NULL to skip it
+ *   workspace device, at least coalesce_mlp_backward_workspace_size(dims, L)
+ *             bytes, 16-byte aligned; its contents on entry are ignored
+ * Pitches obey D <= ld <= 2^24 with 16-byte aligned rows.  Two kernels run
+ * on `stream`: the fused backward (one persistent workgroup per compute
+ * unit; each sums its rows' weight-gradient terms in registers) and a
+ * reduction that adds the per-workgroup sums in a fixed order, so repeated
+ * calls give identical bits.  M == 0 gives dW = 0.  Supported chains as
+ * coalesce_mlp_forward.  Outputs must not overlap the inputs, each other or
+ * the workspace.  Calls that share a workspace must be ordered on one
+ * stream.
+ */
+coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                      int32_t L, const float* const* acts, int64_t lda, const void* dout,
+                                      int64_t ldd, float* const* dW, void* dx, int64_t ldq, int64_t M,
+                                      coalesce_dtype dtype, coalesce_act hidden_act, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
  * Unfused baseline, step 2: Y = X + bias (bias broadcast over rows), each
  * element converted to fp32, added, and rounded once to y_dtype.  The
  * elementwise-kernel design of the "Fuse Elementwise Ops" page (vectorised

@@ -32,6 +32,10 @@ SIGNATURES = {
     "coalesce_gemm_bias_act": (_i32, [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
     "coalesce_mlp_forward": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _i64, _i32, _i32, _p]),
     "coalesce_mlp_forward_grid": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _i64, _i32, _i32, _i64, _p]),
+    "coalesce_mlp_forward_train": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _p, _i64, _i64, _i32, _i32, _p]),
+    "coalesce_mlp_backward_workspace_size": (_sz, [_p, _i32]),
+    "coalesce_mlp_backward": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _p, _i64, _p, _p, _i64, _i64, _i32, _i32,
+                                     _p, _sz, _p]),
     "coalesce_bias_add": (_i32, [_p, _i64, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
     "coalesce_activation": (_i32, [_p, _i64, _p, _i64, _i64, _i64, _i32, _i32, _p]),
     "coalesce_flush_caches": (_i32, [_p, _sz, _p, _p]),
@@ -137,12 +141,8 @@ def gemm_bias_act(A: torch.Tensor, B: torch.Tensor, bias: Optional[torch.Tensor]
     return out
 
 
-def mlp_forward(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_act="softplus",
-                out: Optional[torch.Tensor] = None, num_workgroups: int = 0, stream=None):
-    """out = W_L(... softplus(softplus(x W_1) W_2) ...) in one persistent launch."""
-    lib = load_library()
+def _chain_dims(x: torch.Tensor, weights: Sequence[torch.Tensor]):
     M, D0, ldx = _matrix(x, "x")
-    L = len(weights)
     dims = [D0]
     for i, w in enumerate(weights):
         if w.dim() != 2 or not w.is_contiguous() or w.dtype != x.dtype or not w.is_cuda:
@@ -150,6 +150,19 @@ def mlp_forward(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_act="so
         if w.shape[0] != dims[-1]:
             raise ValueError("layer widths do not chain")
         dims.append(w.shape[1])
+    return M, ldx, dims
+
+
+def _ptr_array(ts):
+    return ctypes.cast((ctypes.c_void_p * max(len(ts), 1))(*[t.data_ptr() for t in ts]), ctypes.c_void_p)
+
+
+def mlp_forward(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_act="softplus",
+                out: Optional[torch.Tensor] = None, num_workgroups: int = 0, stream=None):
+    """out = W_L(... softplus(softplus(x W_1) W_2) ...) in one persistent launch."""
+    lib = load_library()
+    M, ldx, dims = _chain_dims(x, weights)
+    L = len(weights)
     if out is None:
         out = aligned_empty(M, dims[-1], x.dtype, x.device)
     Mo, Do, ldo = _matrix(out, "out")
@@ -161,6 +174,96 @@ def mlp_forward(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_act="so
                                          ctypes.cast(dp, ctypes.c_void_p), L, _ptr(out), ldo, M,
                                          _DTYPES[x.dtype], _ACTS[hidden_act], int(num_workgroups), _stream(stream)))
     return out
+
+
+def _acts_pitch(acts: Sequence[torch.Tensor], M: int, dims):
+    lda = None
+    for i, a in enumerate(acts):
+        r, c, ld = _matrix(a, "acts[%d]" % i)
+        if (r, c) != (M, dims[i + 1]) or a.dtype != torch.float32:
+            raise ValueError("acts[%d] must be M x dims[%d] float32" % (i, i + 1))
+        if lda is not None and ld != lda:
+            raise ValueError("every acts[l] must share one leading dimension")
+        lda = ld
+    return lda or dims[0]
+
+
+def mlp_forward_train(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_act="softplus",
+                      out: Optional[torch.Tensor] = None, acts: Optional[Sequence[torch.Tensor]] = None,
+                      stream=None):
+    """(out, acts): the forward of mlp_forward (same bits) plus the fp32
+    hidden activations h_1 .. h_{L-1} the backward needs
+    (coalesce_mlp_forward_train)."""
+    lib = load_library()
+    M, ldx, dims = _chain_dims(x, weights)
+    L = len(weights)
+    if out is None:
+        out = aligned_empty(M, dims[-1], x.dtype, x.device)
+    Mo, Do, ldo = _matrix(out, "out")
+    if (Mo, Do) != (M, dims[-1]):
+        raise ValueError("out must be M x dims[L]")
+    if acts is None:
+        pitch = max(4, (dims[0] + 3) // 4 * 4)
+        acts = [torch.empty((M, pitch), dtype=torch.float32, device=x.device)[:, :dims[l]] for l in range(1, L)]
+    if len(acts) != L - 1:
+        raise ValueError("need L - 1 activation buffers")
+    lda = _acts_pitch(acts, M, dims)
+    dp = (ctypes.c_int64 * (L + 1))(*dims)
+    _check(lib.coalesce_mlp_forward_train(_ptr(x), ldx, _ptr_array(weights), ctypes.cast(dp, ctypes.c_void_p), L,
+                                          _ptr(out), ldo, _ptr_array(acts) if L > 1 else None, lda, M,
+                                          _DTYPES[x.dtype], _ACTS[hidden_act], _stream(stream)))
+    return out, list(acts)
+
+
+def mlp_backward_workspace_size(dims: Sequence[int]) -> int:
+    """Bytes of workspace coalesce_mlp_backward needs for this chain here."""
+    L = len(dims) - 1
+    dp = (ctypes.c_int64 * (L + 1))(*dims)
+    n = int(load_library().coalesce_mlp_backward_workspace_size(ctypes.cast(dp, ctypes.c_void_p), L))
+    if n == 0:
+        raise CoalesceError(ERR_UNSUPPORTED, "no backward for dims %s on this device" % (list(dims),))
+    return n
+
+
+def mlp_backward(x: torch.Tensor, weights: Sequence[torch.Tensor], acts: Sequence[torch.Tensor],
+                 dout: torch.Tensor, hidden_act="softplus", want_dx: bool = True,
+                 dW: Optional[Sequence[torch.Tensor]] = None, dx: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """(dW list (fp32), dx or None): the backward of the chain from the
+    stored activations, one fused kernel plus a fixed-order reduction
+    (coalesce_mlp_backward)."""
+    lib = load_library()
+    M, ldx, dims = _chain_dims(x, weights)
+    L = len(weights)
+    Md, Dd, ldd = _matrix(dout, "dout")
+    if (Md, Dd) != (M, dims[-1]) or dout.dtype != x.dtype:
+        raise ValueError("dout must be M x dims[L] of x's dtype")
+    if len(acts) != L - 1:
+        raise ValueError("need the L - 1 stored activations")
+    lda = _acts_pitch(acts, M, dims)
+    if dW is None:
+        dW = [torch.empty((dims[l], dims[l + 1]), dtype=torch.float32, device=x.device) for l in range(L)]
+    for l, g in enumerate(dW):
+        if g.shape != (dims[l], dims[l + 1]) or g.dtype != torch.float32 or not g.is_contiguous():
+            raise ValueError("dW[%d] must be a contiguous dims[l] x dims[l+1] float32 tensor" % l)
+    ldq = 0
+    if want_dx:
+        if dx is None:
+            dx = aligned_empty(M, dims[0], x.dtype, x.device)
+        Mq, Dq, ldq = _matrix(dx, "dx")
+        if (Mq, Dq) != (M, dims[0]) or dx.dtype != x.dtype:
+            raise ValueError("dx must be M x dims[0] of x's dtype")
+    else:
+        dx = None
+    need = mlp_backward_workspace_size(dims)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    dp = (ctypes.c_int64 * (L + 1))(*dims)
+    _check(lib.coalesce_mlp_backward(_ptr(x), ldx, _ptr_array(weights), ctypes.cast(dp, ctypes.c_void_p), L,
+                                     _ptr_array(acts) if L > 1 else None, lda, _ptr(dout), ldd, _ptr_array(dW),
+                                     _ptr(dx), ldq, M, _DTYPES[x.dtype], _ACTS[hidden_act], _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)))
+    return list(dW), dx
 
 
 def bias_add(X: torch.Tensor, bias: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
@@ -205,22 +308,54 @@ def version() -> int:
     return int(load_library().coalesce_version())
 
 
-class FusedMLPSoftplus(torch.nn.Module):
-    """Inference module with the page's constructor shape (D, H, out_features).
+class _FusedMLPFunction(torch.autograd.Function):
+    """Training pair as one autograd node: forward = the training megakernel
+    (which stores the fp32 hidden activations), backward = the fused backward.
+    Weight gradients are computed in fp32 and returned in the weights' dtype."""
 
-    Holds L weight matrices in the x @ W orientation (fp16) and runs the whole
-    chain in one megakernel launch.  Forward only.
+    @staticmethod
+    def forward(ctx, x, hidden_act, *weights):
+        out, acts = mlp_forward_train(x, list(weights), hidden_act=hidden_act)
+        ctx.hidden_act = hidden_act
+        ctx.save_for_backward(x, *weights, *acts)
+        ctx.L = len(weights)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        saved = ctx.saved_tensors
+        L = ctx.L
+        x, weights, acts = saved[0], list(saved[1:1 + L]), list(saved[1 + L:])
+        if dout.dim() != 2 or dout.stride(-1) != 1 or (dout.data_ptr() % 16) or (dout.stride(0) * 2) % 16:
+            dout = aligned_copy(dout.to(x.dtype), dout.device)
+        dW, dx = mlp_backward(x, weights, acts, dout.to(x.dtype), hidden_act=ctx.hidden_act,
+                              want_dx=ctx.needs_input_grad[0])
+        return (dx, None) + tuple(g.to(w.dtype) for g, w in zip(dW, weights))
+
+
+class FusedMLPSoftplus(torch.nn.Module):
+    """Module with the page's constructor shape (D, H, out_features).
+
+    Holds L weight matrices in the x @ W orientation (fp16).  Without
+    gradients the forward is the inference megakernel; when a weight requires
+    a gradient (or x does) it runs the training forward and its backward is
+    the fused backward kernel.
     """
 
     def __init__(self, D: int = 128, H: int = 128, out_features: int = 128, layers: int = 3,
-                 device="cuda", dtype=torch.float16):
+                 device="cuda", dtype=torch.float16, hidden_act="softplus", requires_grad: bool = True):
         super().__init__()
         dims = [D] + [H] * (layers - 1) + [out_features]
+        self.hidden_act = hidden_act
         self.weights = torch.nn.ParameterList(
-            [torch.nn.Parameter(torch.empty(dims[i], dims[i + 1], device=device, dtype=dtype), requires_grad=False)
-             for i in range(layers)])
-        for w in self.weights:
-            torch.nn.init.normal_(w, std=w.shape[0] ** -0.5)
+            [torch.nn.Parameter(torch.empty(dims[i], dims[i + 1], device=device, dtype=dtype),
+                                requires_grad=requires_grad) for i in range(layers)])
+        with torch.no_grad():
+            for w in self.weights:
+                torch.nn.init.normal_(w, std=w.shape[0] ** -0.5)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        return mlp_forward(x, [w for w in self.weights])
+        ws = [w for w in self.weights]
+        if torch.is_grad_enabled() and (x.requires_grad or any(w.requires_grad for w in ws)):
+            return _FusedMLPFunction.apply(x, self.hidden_act, *ws)
+        return mlp_forward(x, ws, hidden_act=self.hidden_act)

@@ -151,55 +151,196 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
   return ok();
 }
 
-coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
-                                          int32_t L, void* out, int64_t ldo, int64_t M, coalesce_dtype dtype,
-                                          coalesce_act hidden_act, int64_t num_workgroups, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared checks of the MLP entry points: the chain's widths (all equal to 64
+// or 128), depth, dtype, activation and weights.  Fills D and p_W.
+coalesce_status check_mlp_chain(const void* const* W, const int64_t* dims, int32_t L, int64_t M,
+                                coalesce_dtype dtype, coalesce_act hidden_act, int64_t* D_out) {
   if (L < 1) return fail(COALESCE_ERR_INVALID_ARGUMENT, "L must be at least 1 (got %d)", (int)L);
   if (!W || !dims) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W or dims is NULL");
   if (M < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative M");
-  if (num_workgroups < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative workgroup count");
   if (!valid_dtype(dtype)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown dtype");
   if (!valid_act(hidden_act)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown activation");
-  for (int l = 0; l <= L; ++l)
+  for (int l = 0; l <= L && l <= 8; ++l)
     if (dims[l] <= 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dims[%d] = %lld is not positive", l, (long long)dims[l]);
   if (dtype != COALESCE_F16) return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel takes fp16 only");
   if (hidden_act == COALESCE_ACT_GELU_ERF)
     return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel supports softplus, relu or no hidden activation");
   const int64_t D = dims[0];
-  for (int l = 1; l <= L; ++l)
-    if (dims[l] != D) return fail(COALESCE_ERR_UNSUPPORTED, "all MLP widths must be equal");
   if (D != 64 && D != 128) return fail(COALESCE_ERR_UNSUPPORTED, "MLP width %lld not supported (64 or 128)", (long long)D);
   if ((D == 128 && L > 4) || (D == 64 && L > 8))
     return fail(COALESCE_ERR_UNSUPPORTED, "%d layers of width %lld do not fit in LDS", (int)L, (long long)D);
-  if (M > kMaxExtent - 64) return fail(COALESCE_ERR_UNSUPPORTED, "M must be below 2^31 - 64");
+  for (int l = 1; l <= L; ++l)
+    if (dims[l] != D) return fail(COALESCE_ERR_UNSUPPORTED, "all MLP widths must be equal");
+  if (M > kMaxExtent - 256) return fail(COALESCE_ERR_UNSUPPORTED, "M must be below 2^31 - 256");
+  for (int l = 0; l < L; ++l) {
+    if (!W[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W[%d] is NULL", l);
+    if (!aligned16(W[l])) return fail(COALESCE_ERR_UNSUPPORTED, "W[%d] must be 16-byte aligned", l);
+  }
+  *D_out = D;
+  return COALESCE_OK;
+}
+
+// An fp16 row-major M x D operand: present, pitch at least D and at most
+// 2^24 (16-row tiles are addressed with 32-bit byte offsets), 16-byte
+// aligned rows.
+coalesce_status check_rows(const void* t, int64_t ld, int64_t D, int64_t es, const char* name) {
+  if (!t) return fail(COALESCE_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (ld < D) return fail(COALESCE_ERR_INVALID_ARGUMENT, "the pitch of %s is shorter than the row", name);
+  if (ld > (int64_t(1) << 24)) return fail(COALESCE_ERR_UNSUPPORTED, "the pitch of %s must be at most 2^24", name);
+  if (!aligned16(t) || (ld * es) % 16)
+    return fail(COALESCE_ERR_UNSUPPORTED, "%s must be 16-byte aligned with a 16-byte row pitch", name);
+  return COALESCE_OK;
+}
+
+coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* W, const int64_t* dims, int32_t L,
+                                 void* out, int64_t ldo, float* const* acts, int64_t lda, int64_t M,
+                                 coalesce_dtype dtype, coalesce_act hidden_act, int64_t num_workgroups, bool train,
+                                 void* stream) {
+  int64_t D = 0;
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &D);
+  if (s != COALESCE_OK) return s;
+  if (num_workgroups < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative workgroup count");
+  if (num_workgroups > (int64_t)INT32_MAX) return fail(COALESCE_ERR_UNSUPPORTED, "workgroup count too large");
   if (M == 0) return ok();
-  if (!x || !out) return fail(COALESCE_ERR_INVALID_ARGUMENT, "x or out is NULL");
-  if (ldx < D || ldo < D) return fail(COALESCE_ERR_INVALID_ARGUMENT, "ldx/ldo shorter than the row");
-  // a 64-row tile is addressed with 32-bit byte offsets
-  if (ldx > (int64_t(1) << 24) || ldo > (int64_t(1) << 24))
-    return fail(COALESCE_ERR_UNSUPPORTED, "ldx and ldo must be at most 2^24");
-  if (!aligned16(x) || !aligned16(out) || (ldx * 2) % 16 || (ldo * 2) % 16)
-    return fail(COALESCE_ERR_UNSUPPORTED, "x and out must be 16-byte aligned with 16-byte row pitch");
+  if ((s = check_rows(x, ldx, D, 2, "x")) != COALESCE_OK) return s;
+  if ((s = check_rows(out, ldo, D, 2, "out")) != COALESCE_OK) return s;
   const Range ro = span(out, M, D, ldo, 2);
   if (overlap(ro, span(x, M, D, ldx, 2))) return fail(COALESCE_ERR_INVALID_ARGUMENT, "out overlaps x");
   MlpParams p{};
   for (int l = 0; l < L; ++l) {
-    if (!W[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W[%d] is NULL", l);
-    if (!aligned16(W[l])) return fail(COALESCE_ERR_UNSUPPORTED, "W[%d] must be 16-byte aligned", l);
     if (overlap(ro, span(W[l], D, D, D, 2))) return fail(COALESCE_ERR_INVALID_ARGUMENT, "out overlaps W[%d]", l);
     p.W[l] = W[l];
   }
+  if (train && L > 1) {
+    if (!acts) return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts is NULL");
+    for (int l = 0; l + 1 < L; ++l) {
+      char name[16];
+      snprintf(name, sizeof(name), "acts[%d]", l);
+      if ((s = check_rows(acts[l], lda, D, 4, name)) != COALESCE_OK) return s;
+      const Range ra = span(acts[l], M, D, lda, 4);
+      if (overlap(ra, span(x, M, D, ldx, 2)) || overlap(ra, ro))
+        return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts[%d] overlaps x or out", l);
+      for (int j = 0; j < L; ++j)
+        if (overlap(ra, span(W[j], D, D, D, 2))) return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts[%d] overlaps W[%d]", l, j);
+      for (int j = 0; j < l; ++j)
+        if (overlap(ra, span(acts[j], M, D, lda, 4)))
+          return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts[%d] overlaps acts[%d]", l, j);
+      p.acts[l] = acts[l];
+    }
+  }
   int cus = 0;
-  coalesce_status s = current_cus(&cus);
+  s = current_cus(&cus);
   if (s != COALESCE_OK) return s;
   p.x = x;
   p.out = out;
   p.ldx = ldx;
   p.ldo = ldo;
+  p.lda = train ? lda : 0;
   p.M = (int)M;
-  if (num_workgroups > (int64_t)INT32_MAX) return fail(COALESCE_ERR_UNSUPPORTED, "workgroup count too large");
-  hipError_t e = launch_mlp(p, (int)D, (int)L, act_code(hidden_act), (int)num_workgroups, cus, (hipStream_t)stream);
+  hipError_t e = launch_mlp(p, (int)D, (int)L, act_code(hidden_act), train && L > 1, (int)num_workgroups, cus,
+                            (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "MLP launch");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                          int32_t L, void* out, int64_t ldo, int64_t M, coalesce_dtype dtype,
+                                          coalesce_act hidden_act, int64_t num_workgroups, void* stream) {
+  return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, num_workgroups, false,
+                          stream);
+}
+
+coalesce_status coalesce_mlp_forward_train(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                           int32_t L, void* out, int64_t ldo, float* const* acts, int64_t lda,
+                                           int64_t M, coalesce_dtype dtype, coalesce_act hidden_act, void* stream) {
+  return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, acts, lda, M, dtype, hidden_act, 0, true, stream);
+}
+
+size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L) {
+  if (!dims || L < 1 || L > 8) return 0;
+  const int64_t D = dims[0];
+  if (D != 64 && D != 128) return 0;
+  if (D == 128 && L > 4) return 0;
+  for (int l = 1; l <= L; ++l)
+    if (dims[l] != D) return 0;
+  int cus = 0;
+  if (current_cus(&cus) != COALESCE_OK) return 0;
+  return mlp_backward_workspace((int)D, (int)L, cus);
+}
+
+coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                      int32_t L, const float* const* acts, int64_t lda, const void* dout,
+                                      int64_t ldd, float* const* dW, void* dx, int64_t ldq, int64_t M,
+                                      coalesce_dtype dtype, coalesce_act hidden_act, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  int64_t D = 0;
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &D);
+  if (s != COALESCE_OK) return s;
+  if (!dW) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW is NULL");
+  MlpBwdParams p{};
+  for (int l = 0; l < L; ++l) {
+    if (!dW[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW[%d] is NULL", l);
+    if (((uintptr_t)dW[l]) & 3u) return fail(COALESCE_ERR_UNSUPPORTED, "dW[%d] must be 4-byte aligned", l);
+    p.W[l] = W[l];
+    p.dW[l] = dW[l];
+  }
+  if (M > 0) {
+    if ((s = check_rows(x, ldx, D, 2, "x")) != COALESCE_OK) return s;
+    if ((s = check_rows(dout, ldd, D, 2, "dout")) != COALESCE_OK) return s;
+    if (L > 1) {
+      if (!acts) return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts is NULL");
+      for (int l = 0; l + 1 < L; ++l) {
+        char name[16];
+        snprintf(name, sizeof(name), "acts[%d]", l);
+        if ((s = check_rows(acts[l], lda, D, 4, name)) != COALESCE_OK) return s;
+        p.acts[l] = acts[l];
+      }
+    }
+    if (dx) {
+      if ((s = check_rows(dx, ldq, D, 2, "dx")) != COALESCE_OK) return s;
+      const Range rq = span(dx, M, D, ldq, 2);
+      bool bad = overlap(rq, span(x, M, D, ldx, 2)) || overlap(rq, span(dout, M, D, ldd, 2));
+      for (int l = 0; l < L; ++l) bad = bad || overlap(rq, span(W[l], D, D, D, 2)) || overlap(rq, span(dW[l], D, D, D, 4));
+      for (int l = 0; l + 1 < L; ++l) bad = bad || overlap(rq, span(acts[l], M, D, lda, 4));
+      if (bad) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dx overlaps an input or a weight gradient");
+    }
+  }
+  int cus = 0;
+  s = current_cus(&cus);
+  if (s != COALESCE_OK) return s;
+  const size_t need = mlp_backward_workspace((int)D, (int)L, cus);
+  if (!workspace) return fail(COALESCE_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(COALESCE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(COALESCE_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes,
+                need);
+  const Range rw = {(uintptr_t)workspace, (uintptr_t)workspace + need};
+  for (int l = 0; l < L; ++l) {
+    const Range rg = span(dW[l], D, D, D, 4);
+    if (overlap(rg, rw)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW[%d] overlaps the workspace", l);
+    for (int j = 0; j < L; ++j)
+      if ((j != l && overlap(rg, span(dW[j], D, D, D, 4))) || overlap(rg, span(W[j], D, D, D, 2)))
+        return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW[%d] overlaps another weight or gradient", l);
+  }
+  p.x = x;
+  p.dout = dout;
+  p.dx = M > 0 ? dx : nullptr;
+  p.partial = (float*)workspace;
+  p.ldx = ldx;
+  p.ldd = ldd;
+  p.lda = lda;
+  p.ldq = ldq;
+  p.M = (int)M;
+  hipError_t e = launch_mlp_backward(p, (int)D, (int)L, act_code(hidden_act), cus, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "MLP backward launch");
   return ok();
 }
 

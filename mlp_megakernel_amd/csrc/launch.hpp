@@ -27,14 +27,35 @@ struct MlpParams {
   const void* x;
   void* out;
   const void* W[8];
-  int64_t ldx, ldo;
+  float* acts[8];  // training forward: acts[l] receives h_{l+1} (fp32, M x D, pitch lda), l = 0..L-2
+  int64_t ldx, ldo, lda;
   int M;
   int num_tiles;  // row tiles (set by the launcher)
 };
 // Widths all equal to D (64 or 128), L layers (1..8 for 64, 1..4 for 128).
 // num_workgroups <= 0: min(#CUs x occupancy, workgroups with work).
-hipError_t launch_mlp(const MlpParams& p, int D, int L, int hidden_act, int num_workgroups, int num_cus,
-                      hipStream_t stream);
+// store_acts: also write the hidden activations to p.acts (training forward).
+hipError_t launch_mlp(const MlpParams& p, int D, int L, int hidden_act, bool store_acts, int num_workgroups,
+                      int num_cus, hipStream_t stream);
+
+struct MlpBwdParams {
+  const void* x;        // M x D fp16, pitch ldx
+  const void* dout;     // M x D fp16, pitch ldd: dL/d(out)
+  const void* W[8];     // D x D fp16, dense
+  const float* acts[8]; // acts[l] = h_{l+1}, M x D fp32, pitch lda (l = 0..L-2)
+  void* dx;             // M x D fp16, pitch ldq, or nullptr
+  float* partial;       // grid x L x D x D fp32 per-workgroup weight-gradient sums
+  float* dW[8];         // D x D fp32, dense: the reduced weight gradients
+  int64_t ldx, ldd, lda, ldq;
+  int M;
+  int num_tiles;        // row tiles (set by the launcher)
+};
+// Weight-gradient workspace (bytes) the backward needs on a device with
+// num_cus compute units.
+size_t mlp_backward_workspace(int D, int L, int num_cus);
+// Backward of the MLP chain: fills p.dW (and p.dx when set).  p.partial must
+// hold mlp_backward_workspace(D, L, num_cus) bytes.
+hipError_t launch_mlp_backward(MlpBwdParams p, int D, int L, int hidden_act, int num_cus, hipStream_t stream);
 
 hipError_t launch_bias_add(const void* X, int64_t ldx, const void* bias, void* Y, int64_t ldy, int M, int N,
                            DType xt, DType bt, DType yt, hipStream_t stream, int num_cus);

@@ -37,6 +37,7 @@
 //     softplus_b2_fast and the check at the end of mlp_kernel.
 #include "common.hpp"
 #include "launch.hpp"
+#include "mlp_common.hpp"
 
 namespace coalesce {
 namespace {
@@ -101,43 +102,9 @@ struct HTile {
   u32x4 v[Geo<D>::MT][Geo<D>::KS];
 };
 
-// Two fp32 values rounded to nearest-even fp16 and packed into one dword.
-__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
-}
-
-// LDS position (within a row of W^T) of logical input unit k for layers fed
-// by a previous layer's registers.  Lane group g of the B operand holds, for
-// k step ks, elements e = 0..7 = units 32 ks + 16 (e / 4) + 4 g + (e % 4); the
-// A operand lane group g reads 8 consecutive LDS elements starting at
-// 32 ks + 8 g, so unit k must sit at 32 ks + 8 g + e.
-__device__ __forceinline__ int layer_k_slot(int k) {
-  return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
-}
-
-// 16-byte chunk swizzle of W^T rows: chunk c of row n sits at c ^ wswz(n).  A
-// weight-fragment read is one 128-bit read by 16 lanes (rows n0..n0+15, one
-// chunk); the swizzle puts those 16 reads in 16 distinct 16-byte slots of a
-// 256-byte bank window (and any 8 consecutive rows in 8 distinct slots of a
-// 128-byte one).  Rows are 256 B (16 chunks) for D = 128 and 128 B for D = 64.
-// wswz(16 t + q) = wswz(q): the swizzle repeats every 16 rows.
-template <int D>
-__device__ __forceinline__ int wswz(int n) {
-  if constexpr (D == 128)
-    return n & 15;
-  else
-    return ((n >> 1) & 7) ^ ((n & 1) << 2);
-}
-
 template <int D>
 __device__ __forceinline__ int w_offset(int l, int n, int slot) {
   return (l * D + n) * D + ((((slot >> 3) ^ wswz<D>(n))) << 3) + (slot & 7);
-}
-
-// Logical input unit k that sits at LDS slot `slot` (inverse of
-// layer_k_slot): slot = 32 a + 8 b + 4 c + d holds k = 32 a + 16 c + 4 b + d.
-__device__ __forceinline__ int layer_slot_k(int slot) {
-  return (slot & ~31) | (((slot >> 2) & 1) << 4) | (((slot >> 3) & 3) << 2) | (slot & 3);
 }
 
 // Copy every W_l into LDS in the layout above.  One work item fills the
@@ -174,6 +141,7 @@ struct Lane {
   uint32_t wk[Geo<D>::KS];  // LDS byte address of the lane's W^T fragment: layer 0, sub-tile 0, k step ks
   uint32_t xoff;            // byte offset of the lane's first x element in a 16-row sub-tile
   uint32_t ooff;            // byte offset of the lane's 16-byte output piece of sub-tiles 0 and 1 (see last_layer)
+  uint32_t aoff;            // byte offset of the lane's first fp32 activation in a 16-row sub-tile (training forward)
 };
 
 template <int D>
@@ -185,21 +153,8 @@ __device__ __forceinline__ Lane<D> lane_setup(const MlpParams& p, const _Float16
   const uint32_t xrow = (uint32_t)p.ldx * 2u, orow = (uint32_t)p.ldo * 2u;
   c.xoff = (uint32_t)q * xrow + 16u * (uint32_t)g;
   c.ooff = (uint32_t)q * orow + 32u * (uint32_t)(g & 1) + 16u * (uint32_t)(g >> 1);
+  c.aoff = (uint32_t)q * (uint32_t)p.lda * 4u + 16u * (uint32_t)g;
   return c;
-}
-
-__device__ __forceinline__ i16x8 lds_read128(uint32_t addr) {
-  return *(const __attribute__((address_space(3))) i16x8*)(uintptr_t)addr;
-}
-
-// A value the compiler cannot see through.  The weight-fragment addresses of
-// every layer of every tile pass through it, so that neither the fragments
-// nor per-layer addresses are hoisted out of the tile loop into registers
-// (they do not fit next to the activations); constant offsets added
-// afterwards stay in the instructions' immediate fields.
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
 }
 
 // Buffer resource over 16-row sub-tile s of row tile `tile` of a row-major
@@ -215,6 +170,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sub_rsrc(const void* base, int
   const int64_t rows = min((int64_t)16, max((int64_t)0, (int64_t)M - first));
   char* p = (char*)base + first * ld * 2;
   return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)((uint32_t)rows * (uint32_t)(ld * 2)), 0x00020000);
+}
+
+// As sub_rsrc, over the fp32 activation matrix acts[l] (pitch ld elements;
+// the host bounds it by 2^24).
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t act_rsrc(float* base, int M, int tile, int s, int64_t ld) {
+  const int64_t first = (int64_t)tile * Geo<D>::TR + 16 * s;
+  const int64_t rows = min((int64_t)16, max((int64_t)0, (int64_t)M - first));
+  char* p = (char*)base + first * ld * 4;
+  return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)((uint32_t)rows * (uint32_t)(ld * 4)), 0x00020000);
+}
+
+// Stored activation of the training forward: h = act(z) in fp32 and natural
+// units (the base-2 softplus output times ln 2), four consecutive units of
+// one row per lane.
+__device__ __forceinline__ void store_act(__amdgpu_buffer_rsrc_t rs, uint32_t off, float a0, float a1, float a2,
+                                          float a3) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (f32x4){a0, a1, a2, a3}), rs, off, 0, 0);
 }
 
 template <int D>
@@ -279,11 +252,18 @@ __device__ __forceinline__ void interleave() {
 // Hidden layer l for one row tile: hout = act(hin W_l), in the step pipeline
 // described at the top, with the unguarded softplus; the largest output is
 // folded into mx.
-template <int D, int l, int ACT>
-__device__ __forceinline__ void hidden_layer(const Lane<D>& c, const HTile<D>& hin, HTile<D>& hout,
-                                             u16x2& mx) {
+template <int D, int l, int ACT, bool ST>
+__device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& c, const HTile<D>& hin,
+                                             HTile<D>& hout, u16x2& mx, int tile) {
   using G = Geo<D>;
   constexpr bool SP = ACT == ACT_SOFTPLUS;
+  __amdgpu_buffer_rsrc_t ra[G::MT];
+  uint32_t aoff = 0;
+  if constexpr (ST) {
+#pragma unroll
+    for (int s = 0; s < G::MT; ++s) ra[s] = act_rsrc<D>(p.acts[l], p.M, tile, s, p.lda);
+    aoff = opaque(c.aoff);
+  }
   constexpr bool IN_B2 = SP && l > 0;  // does the accumulator arrive in base-2 units?
   // twice the VALU instructions per element: [scale] exp2 add log2, 1/2 pack
   constexpr int VPE2 = SP ? (IN_B2 ? 7 : 9) : 1;
@@ -326,9 +306,13 @@ __device__ __forceinline__ void hidden_layer(const Lane<D>& c, const HTile<D>& h
         }
         hout.v[s][u >> 1][(u & 1) * 2] = pack_f16(v[0], v[1]);
         hout.v[s][u >> 1][(u & 1) * 2 + 1] = pack_f16(v[2], v[3]);
+        if constexpr (ST) {
+          const float sc = SP ? 0.693147180559945309f : 1.0f;
+          store_act(ra[s], aoff + 64u * (uint32_t)u, v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
+        }
       }
     }
-    if (MLP_INTERLEAVE && t > 0 && t < G::NT) interleave<G::KS * G::MT, VPM, true, G::MT, false, 1>();
+    if (MLP_INTERLEAVE && t > 0 && t < G::NT) interleave<G::KS * G::MT, VPM, true, G::MT, ST, G::KS>();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int s = 0; s < G::MT; ++s) prv[s] = acc[s];
@@ -350,20 +334,6 @@ __device__ __forceinline__ void hidden_layer(const Lane<D>& c, const HTile<D>& h
     // outputs alive until the end of the tile
     asm volatile("" : "+v"(mx));
   }
-}
-
-// Output of two neighbouring 16-unit sub-tiles u (even) and u + 1 of one
-// 16-row sub-tile, fp16.  Lane group g (lanes 16 g .. 16 g + 15, one row
-// each) holds 8 bytes of each: units 16 u + 4 g .. + 3 in a and
-// 16 (u + 1) + 4 g .. + 3 in b.  One v_permlane16_swap per dword exchanges
-// b of groups 0 and 2 with a of groups 1 and 3; then group g holds 16
-// contiguous bytes, at unit 16 u + 16 (g & 1) + 8 (g >> 1), and the four
-// groups cover 64 contiguous bytes of their row: one 16-byte store per lane
-// instead of two 8-byte ones with 32 contiguous bytes per row.
-__device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t rs, uint32_t off, u32x2 a, u32x2 b) {
-  const auto s0 = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
-  const auto s1 = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
-  __builtin_amdgcn_raw_buffer_store_b128((u32x4){s0[0], s1[0], s0[1], s1[1]}, rs, off, 0, 0);
 }
 
 // Last layer l = L - 1 for one row tile: out = hin W_L (times ln 2 when hin
@@ -424,7 +394,7 @@ __device__ __forceinline__ void last_layer(const MlpParams& p, const Lane<D>& c,
 // Per element it executes the same MFMA accumulation order and the same
 // exp2/add/log2/pack instructions as the pipelined path, so it reproduces
 // that path's bits wherever the guard does not apply.
-template <int D, int L, int ACT>
+template <int D, int L, int ACT, bool ST>
 __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& c, int tile) {
   using G = Geo<D>;
   constexpr bool SP = ACT == ACT_SOFTPLUS;
@@ -462,6 +432,11 @@ __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& 
           }
           hn[t >> 1][(t & 1) * 2] = pack_f16(v[0], v[1]);
           hn[t >> 1][(t & 1) * 2 + 1] = pack_f16(v[2], v[3]);
+          if constexpr (ST) {
+            const float sc = SP ? 0.693147180559945309f : 1.0f;
+            store_act(act_rsrc<D>(p.acts[l], p.M, tile, s, p.lda), opaque(c.aoff) + 64u * (uint32_t)t, v[0] * sc,
+                      v[1] * sc, v[2] * sc, v[3] * sc);
+          }
         } else {
           const float sc = in_b2 ? 0.693147180559945309f : 1.0f;
           const u32x2 o = (u32x2){pack_f16(acc[0] * sc, acc[1] * sc), pack_f16(acc[2] * sc, acc[3] * sc)};
@@ -480,12 +455,12 @@ __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& 
 
 // One row tile, layers l .. L-1.  hin holds the layer-l input; hfree is free.
 // mx collects the largest unguarded softplus output.
-template <int D, int L, int l, int ACT>
+template <int D, int L, int l, int ACT, bool ST>
 __device__ __forceinline__ void tile_chain(const MlpParams& p, const Lane<D>& c, int tile, HTile<D>& hin,
                                            HTile<D>& hfree, u16x2& mx) {
   if constexpr (l < L - 1) {
-    hidden_layer<D, l, ACT>(c, hin, hfree, mx);
-    tile_chain<D, L, l + 1, ACT>(p, c, tile, hfree, hin, mx);
+    hidden_layer<D, l, ACT, ST>(p, c, hin, hfree, mx, tile);
+    tile_chain<D, L, l + 1, ACT, ST>(p, c, tile, hfree, hin, mx);
   } else {
     last_layer<D, l, ACT>(p, c, hin, tile);
   }
@@ -493,7 +468,7 @@ __device__ __forceinline__ void tile_chain(const MlpParams& p, const Lane<D>& c,
 
 // Several waves per SIMD (MlpCfg::MINW) so that memory latency and the
 // dependent activation chains of some waves hide behind the work of others.
-template <int D, int L, int ACT>
+template <int D, int L, int ACT, bool ST>
 __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(MlpParams p) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(16))) _Float16 sW[L * D * D];
@@ -513,17 +488,17 @@ __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(M
   while (tile < p.num_tiles) {
     int next = tile + nwaves;
     if (next < p.num_tiles) load_x<D>(p, c, next, hc);
-    tile_chain<D, L, 0, ACT>(p, c, tile, ha, hb, mx);
+    tile_chain<D, L, 0, ACT, ST>(p, c, tile, ha, hb, mx);
     tile = next;
     if (tile >= p.num_tiles) break;
     next = tile + nwaves;
     if (next < p.num_tiles) load_x<D>(p, c, next, hb);
-    tile_chain<D, L, 0, ACT>(p, c, tile, hc, ha, mx);
+    tile_chain<D, L, 0, ACT, ST>(p, c, tile, hc, ha, mx);
     tile = next;
     if (tile >= p.num_tiles) break;
     next = tile + nwaves;
     if (next < p.num_tiles) load_x<D>(p, c, next, ha);
-    tile_chain<D, L, 0, ACT>(p, c, tile, hb, hc, mx);
+    tile_chain<D, L, 0, ACT, ST>(p, c, tile, hb, hc, mx);
     tile = next;
   }
   if constexpr (ACT == ACT_SOFTPLUS && L > 1) {
@@ -534,7 +509,7 @@ __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(M
     // they are overwritten.
     if (__builtin_amdgcn_ballot_w64(max(mx[0], mx[1]) >= SP_FLAG_B2_F16) != 0) {
       wait_vmcnt0();
-      for (int t = wave; t < p.num_tiles; t += nwaves) tile_guarded<D, L, ACT>(p, c, t);
+      for (int t = wave; t < p.num_tiles; t += nwaves) tile_guarded<D, L, ACT, ST>(p, c, t);
     }
   }
 }
@@ -542,14 +517,14 @@ __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(M
 // Persistent grid: min(#CUs x workgroups that fit on a CU, #workgroups with
 // work), unless the caller fixed the count.  The per-CU occupancy comes from
 // the runtime for the compiled kernel (its VGPR and LDS use) and is cached.
-template <int D, int L, int ACT>
+template <int D, int L, int ACT, bool ST>
 hipError_t launch_dl(MlpParams p, int num_workgroups, int num_cus, hipStream_t stream) {
   using G = Geo<D>;
   p.num_tiles = (int)(((int64_t)p.M + G::TR - 1) / G::TR);
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mlp_kernel<D, L, ACT>, G::THREADS, 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mlp_kernel<D, L, ACT, ST>, G::THREADS, 0);
     if (e != hipSuccess) return e;
     per_cu = n > 0 ? n : 1;
   }
@@ -560,45 +535,50 @@ hipError_t launch_dl(MlpParams p, int num_workgroups, int num_cus, hipStream_t s
     nwg = need < cap ? need : (int)cap;
     if (nwg < 1) nwg = 1;
   }
-  hipLaunchKernelGGL((mlp_kernel<D, L, ACT>), dim3(nwg), dim3(G::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((mlp_kernel<D, L, ACT, ST>), dim3(nwg), dim3(G::THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int ACT>
+template <int D, int ACT, bool ST>
 hipError_t launch_d(const MlpParams& p, int L, int nwg, int cus, hipStream_t stream) {
   if constexpr (D == 128) {
     switch (L) {
-      case 1: return launch_dl<D, 1, ACT>(p, nwg, cus, stream);
-      case 2: return launch_dl<D, 2, ACT>(p, nwg, cus, stream);
-      case 3: return launch_dl<D, 3, ACT>(p, nwg, cus, stream);
-      case 4: return launch_dl<D, 4, ACT>(p, nwg, cus, stream);
+      case 1: return launch_dl<D, 1, ACT, ST>(p, nwg, cus, stream);
+      case 2: return launch_dl<D, 2, ACT, ST>(p, nwg, cus, stream);
+      case 3: return launch_dl<D, 3, ACT, ST>(p, nwg, cus, stream);
+      case 4: return launch_dl<D, 4, ACT, ST>(p, nwg, cus, stream);
     }
   } else {
     switch (L) {
-      case 1: return launch_dl<D, 1, ACT>(p, nwg, cus, stream);
-      case 2: return launch_dl<D, 2, ACT>(p, nwg, cus, stream);
-      case 3: return launch_dl<D, 3, ACT>(p, nwg, cus, stream);
-      case 4: return launch_dl<D, 4, ACT>(p, nwg, cus, stream);
-      case 5: return launch_dl<D, 5, ACT>(p, nwg, cus, stream);
-      case 6: return launch_dl<D, 6, ACT>(p, nwg, cus, stream);
-      case 7: return launch_dl<D, 7, ACT>(p, nwg, cus, stream);
-      case 8: return launch_dl<D, 8, ACT>(p, nwg, cus, stream);
+      case 1: return launch_dl<D, 1, ACT, ST>(p, nwg, cus, stream);
+      case 2: return launch_dl<D, 2, ACT, ST>(p, nwg, cus, stream);
+      case 3: return launch_dl<D, 3, ACT, ST>(p, nwg, cus, stream);
+      case 4: return launch_dl<D, 4, ACT, ST>(p, nwg, cus, stream);
+      case 5: return launch_dl<D, 5, ACT, ST>(p, nwg, cus, stream);
+      case 6: return launch_dl<D, 6, ACT, ST>(p, nwg, cus, stream);
+      case 7: return launch_dl<D, 7, ACT, ST>(p, nwg, cus, stream);
+      case 8: return launch_dl<D, 8, ACT, ST>(p, nwg, cus, stream);
     }
   }
   return hipErrorInvalidValue;
 }
 
+template <int D, bool ST>
+hipError_t launch_da(const MlpParams& p, int L, int act, int nwg, int cus, hipStream_t stream) {
+  if (act == ACT_NONE) return launch_d<D, ACT_NONE, ST>(p, L, nwg, cus, stream);
+  if (act == ACT_RELU) return launch_d<D, ACT_RELU, ST>(p, L, nwg, cus, stream);
+  return launch_d<D, ACT_SOFTPLUS, ST>(p, L, nwg, cus, stream);
+}
+
 }  // namespace
 
-hipError_t launch_mlp(const MlpParams& p, int D, int L, int act, int num_workgroups, int num_cus, hipStream_t stream) {
-  if (D == 128) {
-    if (act == ACT_NONE) return launch_d<128, ACT_NONE>(p, L, num_workgroups, num_cus, stream);
-    if (act == ACT_RELU) return launch_d<128, ACT_RELU>(p, L, num_workgroups, num_cus, stream);
-    return launch_d<128, ACT_SOFTPLUS>(p, L, num_workgroups, num_cus, stream);
-  }
-  if (act == ACT_NONE) return launch_d<64, ACT_NONE>(p, L, num_workgroups, num_cus, stream);
-  if (act == ACT_RELU) return launch_d<64, ACT_RELU>(p, L, num_workgroups, num_cus, stream);
-  return launch_d<64, ACT_SOFTPLUS>(p, L, num_workgroups, num_cus, stream);
+hipError_t launch_mlp(const MlpParams& p, int D, int L, int act, bool store_acts, int num_workgroups, int num_cus,
+                      hipStream_t stream) {
+  if (D == 128)
+    return store_acts ? launch_da<128, true>(p, L, act, num_workgroups, num_cus, stream)
+                      : launch_da<128, false>(p, L, act, num_workgroups, num_cus, stream);
+  return store_acts ? launch_da<64, true>(p, L, act, num_workgroups, num_cus, stream)
+                    : launch_da<64, false>(p, L, act, num_workgroups, num_cus, stream);
 }
 
 }  // namespace coalesce

@@ -105,3 +105,69 @@ def test_elementwise_and_flush_reject():
     assert lib.coalesce_flush_caches(P + 4, 1024, P, None) == UNS
     assert lib.coalesce_flush_caches(None, 1024, P, None) == INV
     assert lib.coalesce_flush_caches(None, 0, None, None) == mk.OK
+
+
+def mlp_train(D=128, L=3, **kw):
+    lib = mk.load_library()
+    dims = [D] * (L + 1)
+    W = (ctypes.c_void_p * L)(*[P * (16 + l) for l in range(L)])
+    d = (ctypes.c_int64 * len(dims))(*dims)
+    acts = kw.pop("acts", [P * (256 + 64 * l) for l in range(max(L - 1, 1))])
+    A = None if acts is None else ctypes.cast((ctypes.c_void_p * len(acts))(*acts), ctypes.c_void_p)
+    a = dict(x=P, ldx=D, out=P * 64, ldo=D, lda=D, M=100, dt=mk.F16, act=mk.ACT_SOFTPLUS)
+    a.update(kw)
+    return lib.coalesce_mlp_forward_train(a["x"], a["ldx"], ctypes.cast(W, ctypes.c_void_p),
+                                          ctypes.cast(d, ctypes.c_void_p), L, a["out"], a["ldo"], A, a["lda"],
+                                          a["M"], a["dt"], a["act"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(acts=None), INV), (dict(acts=[P * 256, None]), INV), (dict(lda=100), INV),
+    (dict(acts=[P * 256 + 4, P * 320]), UNS), (dict(lda=130), UNS), (dict(lda=(1 << 24) + 4), UNS),
+    (dict(acts=[P * 64, P * 320]), INV),        # acts[0] overlaps out
+    (dict(acts=[P * 256, P * 256 + 512]), INV),  # acts overlap each other
+    (dict(act=mk.ACT_GELU_ERF), UNS), (dict(D=128, L=5), UNS), (dict(x=None), INV),
+])
+def test_mlp_forward_train_rejects_before_launch(kw, status):
+    assert mlp_train(**kw) == status
+
+
+def test_mlp_forward_train_empty_and_single_layer_need_no_acts():
+    assert mlp_train(M=0, x=None, out=None, acts=None) == mk.OK
+
+
+def mlp_bwd(D=128, L=3, **kw):
+    lib = mk.load_library()
+    dims = [D] * (L + 1)
+    W = (ctypes.c_void_p * L)(*[P * (16 + l) for l in range(L)])
+    d = (ctypes.c_int64 * len(dims))(*dims)
+    acts = kw.pop("acts", [P * (256 + 64 * l) for l in range(max(L - 1, 1))])
+    dW = kw.pop("dW", [P * (1024 + 4 * l) for l in range(L)])
+    A = None if acts is None else ctypes.cast((ctypes.c_void_p * len(acts))(*acts), ctypes.c_void_p)
+    G = None if dW is None else ctypes.cast((ctypes.c_void_p * len(dW))(*dW), ctypes.c_void_p)
+    a = dict(x=P, ldx=D, lda=D, dout=P * 128, ldd=D, dx=P * 192, ldq=D, M=100, dt=mk.F16, act=mk.ACT_SOFTPLUS,
+             ws=P * 4096, wsb=1 << 30)
+    a.update(kw)
+    return lib.coalesce_mlp_backward(a["x"], a["ldx"], ctypes.cast(W, ctypes.c_void_p),
+                                     ctypes.cast(d, ctypes.c_void_p), L, A, a["lda"], a["dout"], a["ldd"], G,
+                                     a["dx"], a["ldq"], a["M"], a["dt"], a["act"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dW=None), INV), (dict(dW=[P * 1024, None, P * 1032]), INV), (dict(dW=[P * 1024 + 2, P * 1028, P * 1032]), UNS),
+    (dict(x=None), INV), (dict(dout=None), INV), (dict(acts=None), INV), (dict(ldd=100), INV), (dict(ldq=64), INV),
+    (dict(dout=P * 128 + 8), UNS), (dict(lda=129), UNS), (dict(dx=P + 64), INV),  # dx overlaps x
+    (dict(act=mk.ACT_GELU_ERF), UNS), (dict(dt=mk.F32), UNS), (dict(D=64, L=9), UNS), (dict(D=32), UNS),
+    (dict(L=0), INV), (dict(M=-5), INV), (dict(act=11), INV),
+])
+def test_mlp_backward_rejects_before_launch(kw, status):
+    assert mlp_bwd(**kw) == status
+    assert len(mk.load_library().coalesce_last_error()) > 0
+
+
+def test_mlp_backward_workspace_size_of_unsupported_chain_is_zero():
+    lib = mk.load_library()
+    for dims in ([96, 96], [128] * 6, [64] * 10):
+        d = (ctypes.c_int64 * len(dims))(*dims)
+        assert lib.coalesce_mlp_backward_workspace_size(ctypes.cast(d, ctypes.c_void_p), len(dims) - 1) == 0
+    assert lib.coalesce_mlp_backward_workspace_size(None, 3) == 0
