@@ -18,6 +18,10 @@ TFLOP/s.  The same line carries
     flush and bracketed by their own event pair, median / p10 / p90 -- for
     the fused kernel and for the unfused GEMM -> bias -> activation baseline
     (per-layer GEMM -> softplus for the MLPs);
+  * mlp_train: the training pair of both MLP workloads -- the training
+    forward (which also stores the fp32 hidden activations) and the fused
+    backward (weight gradients of every layer and dx) -- each timed the same
+    way, with its HBM roofline, and rows/s of one forward + backward step;
   * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
     sample of the primary workload.
 All inputs are synthetic and seeded (datagen).
@@ -51,6 +55,7 @@ def parse():
     ap.add_argument("--no-harness", action="store_true", help="skip the flushed median-of-100 sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mlp", action="store_true")
+    ap.add_argument("--no-train", action="store_true", help="skip the MLP training pair")
     ap.add_argument("--prewarm-ms", type=float, default=500.0,
                     help="untimed back-to-back running before the warmup steps of each timed case")
     ap.add_argument("--harness-iters", type=int, default=100)
@@ -129,6 +134,31 @@ def main():
                     h = hs2[l]
 
         return fused, unfused
+
+    def train_case(w):
+        x, Ws = datagen.mlp_inputs(w)
+        g = datagen.mlp_grad_output(w)
+        x, g = x.to(dev), g.to(dev)
+        Ws = [t.to(dev) for t in Ws]
+        out = torch.empty((w.M, w.dims[-1]), dtype=torch.float16, device=dev)
+        acts = [torch.empty((w.M, d), dtype=torch.float32, device=dev) for d in w.dims[1:-1]]
+        dW = [torch.empty((w.dims[l], w.dims[l + 1]), dtype=torch.float32, device=dev) for l in range(w.L)]
+        dx = torch.empty_like(x)
+        ws = torch.empty(mk.mlp_backward_workspace_size(w.dims), dtype=torch.uint8, device=dev)
+
+        def fwd():
+            mk.mlp_forward_train(x, Ws, out=out, acts=acts)
+
+        def bwd():
+            mk.mlp_backward(x, Ws, acts, g, dW=dW, dx=dx, workspace=ws)
+
+        def step():
+            fwd()
+            bwd()
+
+        fwd()
+        torch.cuda.synchronize()
+        return fwd, bwd, step, ws.numel()
 
     # ----------------------------------------------------------------- timing
     def prewarm(fn):
@@ -268,6 +298,38 @@ def main():
         result["mlp"] = mlp_res
         if datagen.MLP3.name in mlp_res:
             result["mlp_rows_per_sec"] = mlp_res[datagen.MLP3.name]["rows_per_s"]
+
+    # ------------------------------------------------------- MLP training pair
+    if not args.no_train:
+        train_res = {}
+        for w in (datagen.MLP3, datagen.MLP5):
+            print("bench: training pair %s" % w.name, file=sys.stderr, flush=True)
+            fwd, bwd, step, ws_bytes = train_case(w)
+            hidden = sum(w.dims[1:-1])
+            # algorithmic bytes per row: the training forward reads x and
+            # writes out and the fp32 activations; the backward reads x, dout
+            # and the activations and writes dx (the weights and dW are a few
+            # KB; the per-workgroup partial sums are reported separately)
+            fb = w.M * (2.0 * w.dims[0] + 2.0 * w.dims[-1] + 4.0 * hidden)
+            bb = w.M * (2.0 * w.dims[0] + 2.0 * w.dims[-1] + 4.0 * hidden + 2.0 * w.dims[0])
+            res = {}
+            for name, fn, by, kern in (("forward_train", fwd, fb, "mlp_kernel"),
+                                       ("backward", bwd, bb, "mlp_bwd_kernel + mlp_bwd_reduce")):
+                ms, ev_ms = timed_steps(fn, max(20, args.steps), 10)
+                ach = by / (ev_ms * 1e-3) / 1e9
+                res[name] = {"ms_per_call": round(ms, 5), "rows_per_s": round(w.M / (ms * 1e-3), 1),
+                             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                                          "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                                          "traffic": measured_traffic(name + "/" + w.name), "kernel": kern,
+                                          "algorithmic_bytes_per_launch": by, "mean_launch_ms": round(ev_ms, 5)}}
+            res["backward"]["workspace_bytes"] = ws_bytes
+            ms, _ = timed_steps(step, max(20, args.steps), 10)
+            res["step_ms"] = round(ms, 5)
+            res["step_rows_per_s"] = round(w.M / (ms * 1e-3), 1)
+            train_res[w.name] = res
+            del fwd, bwd, step
+            torch.cuda.empty_cache()
+        result["mlp_train"] = train_res
 
     # ------------------------------------------- the other GEMM workloads (harness)
     if not args.no_harness:

@@ -146,10 +146,10 @@ size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L);
  *   dW[l] = h_l^T dz_{l+1}               (fp32, summed over all M rows)
  *   dz_l  = (dz_{l+1} W_l^T) * act'(z_l)  (l > 0)
  *   dx    = dz_1 W_0^T                    (when dx is not NULL)
- * act'(z_l) is recovered from h_l: softplus -> 1 - exp(-h_l) (the logistic
- * sigmoid of z_l), relu -> 1 where h_l > 0 else 0, none -> 1.  h_l and
- * dz_l are rounded to fp16 (nearest even) as MFMA operands; products
- * accumulate in fp32.
+ * act'(z_l) is recovered from h_l in fp32: softplus -> 1 - exp(-h_l) (the
+ * logistic sigmoid of z_l; absolute error at most 2^-23), relu -> 1 where
+ * h_l > 0 else 0, none -> 1.  h_l and dz_l are rounded to fp16 (nearest
+ * even) as MFMA operands; products accumulate in fp32.
  *   x         device, M x D fp16 (ldx)          the forward's input
  *   W, dims   as coalesce_mlp_forward
  *   acts      HOST array of L - 1 device pointers, M x D fp32 (lda), as

@@ -11,9 +11,7 @@
 //   dz_l  = (dz_{l+1} W_l^T) * act'(z_l)      (l > 0; contraction over units)
 //   dx    =  dz_1 W_0^T                       (l = 0, optional)
 // act'(z_l) is recovered from the stored h_l = act(z_l):
-//   softplus: sigmoid(z) = 1 - exp(-h) (a four-term series below h = 2^-6,
-//             where the subtraction would cancel);
-//   relu: h > 0;  none: 1.
+//   softplus: sigmoid(z) = 1 - exp(-h);  relu: h > 0;  none: 1.
 //
 // Design for gfx950:
 //   * a workgroup of 4 waves (one per SIMD, 512 registers a lane) owns a
@@ -28,16 +26,18 @@
 //   * weight gradients: dW_l is split into four D/2 x D/2 blocks, one per
 //     wave, and accumulated in registers over all of the workgroup's tiles.
 //     The contraction runs over rows, so h_l and dz_{l+1} of the whole tile
-//     are staged in LDS as fp16 (row-major, 32-byte chunks XOR-swizzled by
+//     are staged in LDS as fp16 (row-major, 16-byte pieces XOR-swizzled by
 //     row) and read back with the transposing ds_read_b64_tr_b16, which
-//     hands every lane 4 consecutive rows of one column;
+//     hands every lane 4 rows of one column;
 //   * h_l comes from the fp32 activations loaded once per layer: the same
 //     registers give the fp16 staging copy and the derivative;
-//   * the loads of the next layer's activations (and of the next tile's
-//     dout) are issued a layer ahead, and the barriers around the staging
-//     buffers do not wait for them;
+//   * every input of a tile (dout, each activation layer, x) has its own
+//     register buffer that is reloaded with the next tile's rows as soon as
+//     the current rows are staged, so the loads run a whole tile ahead (the
+//     deepest chains keep one activation buffer, loaded a layer ahead); the
+//     barriers around the staging buffers do not wait for them;
 //   * at the end every workgroup writes its partial dW to a workspace and a
-//     second kernel sums the partials in workgroup order: the result is
+//     second kernel sums the partials in a fixed order: the result is
 //     deterministic for a given grid (the pages' design accumulates with
 //     atomics below 32K rows and calls GEMMs above).
 #include "common.hpp"
@@ -60,18 +60,24 @@ struct BGeo {
 };
 
 // Staging buffers sH (h_l) and sZ (dz_{l+1}): R rows x D fp16, rows of 2D
-// bytes, 32-byte chunk c (16 units) of row r at chunk position c ^ sfz(r).
-// Both access patterns then spread over all banks:
-//   * writes by 16 consecutive rows (one 8-byte piece each, lane groups
-//     side by side) hit every 32-byte position of a 256-byte window twice;
-//   * a transposing read by the 4 lane groups (rows 8 g + 4 h + 0..3 of a
-//     32-row chunk, one chunk each) hits every position twice.
+// bytes, 16-byte piece c (units 8 c .. 8 c + 7) of row r at piece position
+// c ^ sfz(r), where sfz depends on r mod 16 only.  The LDS serves 256 bytes
+// (64 four-byte banks) per pass, half a wave for 8-byte accesses and a
+// quarter for 16-byte ones; every pass below then touches each bank once:
+//   * 8-byte writes (4 units of one row per lane): a half-wave covers 16
+//     consecutive rows at one piece index;
+//   * 16-byte writes: a quarter-wave covers 16 consecutive rows at one piece;
+//   * transposing reads: a half-wave covers 8 consecutive rows, two pieces
+//     each.  The 32 rows of a weight-gradient contraction step are paired as
+//     kk = 8 g + 4 h + rho <-> row 16 h + 4 g + rho, so that the rows of one
+//     read are 8 consecutive ones and the second read is 16 rows further
+//     (sfz unchanged: the offset stays an immediate).
 template <int D>
 __device__ __forceinline__ int sfz(int r) {
   if constexpr (D == 128)
-    return (r & 3) | (((r >> 3) & 1) << 2);
+    return ((r & 7) << 1) | ((r >> 3) & 1);
   else
-    return ((r >> 1) & 1) | (((r >> 3) & 1) << 1);
+    return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
 }
 
 // Weights in LDS: W_l as D rows k of D fp16, 16-byte chunks swizzled by
@@ -122,10 +128,14 @@ __device__ __forceinline__ BLane<D> blane_setup(const MlpBwdParams& p, const _Fl
   for (int ks = 0; ks < G::KS; ++ks)
     c.wk[ks] = lds_addr(sW) + 2u * (uint32_t)(q * D + (((4 * ks + g) ^ wswz<D>(q)) << 3));
   const int r = 16 * G::MT * w + q;  // the lane's row in sub-tile 0 of its wave
-  c.st8 = (uint32_t)(r * 2 * D + (sfz<D>(r) << 5) + (g << 3));
-  c.st16 = (uint32_t)(r * 2 * D + (((g >> 1) ^ sfz<D>(r)) << 5) + ((g & 1) << 4));
-  const int rt = 8 * g + (q >> 2);  // row of the first transposing read in a 32-row chunk
-  c.trk = (uint32_t)(rt * 2 * D + (sfz<D>(rt) << 5) + ((q & 3) << 3));
+  // units 16 t + 4 g .. + 3 sit in piece 2 t + g / 2 (XOR t << 5 selects t)
+  c.st8 = (uint32_t)(r * 2 * D + (((g >> 1) ^ sfz<D>(r)) << 4) + ((g & 1) << 3));
+  // units 32 ks + 8 g .. + 7 are piece 4 ks + g (XOR ks << 6 selects ks)
+  c.st16 = (uint32_t)(r * 2 * D + ((g ^ sfz<D>(r)) << 4));
+  // transposing read: row 4 g + q / 4 of a 32-row chunk, units 16 b + 4 (q % 4)
+  // .. + 3, i.e. piece 2 b + (q % 4) / 2 (XOR b << 5 selects the block b)
+  const int rt = 4 * g + (q >> 2);
+  c.trk = (uint32_t)(rt * 2 * D + ((((q & 3) >> 1) ^ sfz<D>(rt)) << 4) + ((q & 1) << 3));
   c.boff = (uint32_t)q * (uint32_t)p.ldx * 2u + 16u * (uint32_t)g;  // x; dout uses its own pitch below
   c.aoff = (uint32_t)q * (uint32_t)p.lda * 4u + 16u * (uint32_t)g;
   c.qoff = (uint32_t)q * (uint32_t)p.ldq * 2u + 32u * (uint32_t)(g & 1) + 16u * (uint32_t)(g >> 1);
@@ -195,7 +205,7 @@ __device__ __forceinline__ void stage_b(uint32_t buf, const BLane<D>& c, const F
   for (int s = 0; s < BGeo<D>::MT; ++s)
 #pragma unroll
     for (int ks = 0; ks < BGeo<D>::KS; ++ks)
-      lds_write128((buf + c.st16 + 16u * 2 * D * s) ^ (uint32_t)(2 * ks << 5), f.v[s][ks]);
+      lds_write128((buf + c.st16 + 16u * 2 * D * s) ^ (uint32_t)(ks << 6), f.v[s][ks]);
 }
 
 // Stage the packed fp16 D-layout pieces held in B-operand form: unit block t
@@ -223,108 +233,164 @@ __device__ __forceinline__ void pack_rows(const RowsF32<D>& a, FragB<D>& f) {
     }
 }
 
-// Derivative of the hidden activation from its stored output h = act(z).
+// dz = g * act'(z) from the stored output h = act(z), in fp32:
+//   softplus: act'(z) = sigmoid(z) = 1 - e^{-h} (e^{-h} = 1 / (1 + e^z) for
+//     h = ln(1 + e^z)).  The hardware 2^x on -h log2(e) gives e^{-h} to about
+//     one ulp, and 1 - e^{-h} is then exact, so the derivative is off by at
+//     most 2^-23 in absolute terms: below the resolution of the fp16 dz it
+//     feeds wherever dz is a normal fp16 number;
+//   relu: g where h > 0, else 0 (a select, so an infinite g gives 0 there);
+//   none: g.
 template <int ACT>
-__device__ __forceinline__ float act_grad(float h) {
+__device__ __forceinline__ float apply_grad(float g, float h) {
   if constexpr (ACT == ACT_SOFTPLUS) {
-    // sigmoid(z) = 1 - e^{-h}; below h = 2^-6 the series
-    // h (1 - h (1/2 - h (1/6 - h / 24))) (truncation below 2^-25 relative)
-    const float big = 1.0f - __builtin_amdgcn_exp2f(h * -1.44269504088896341f);
-    const float small = h * __builtin_fmaf(-h, __builtin_fmaf(-h, __builtin_fmaf(-h, 0.0416666679f, 0.166666672f), 0.5f), 1.0f);
-    return h < 0.015625f ? small : big;
+    return g * (1.0f - __builtin_amdgcn_exp2f(h * -1.44269504088896341f));
   } else if constexpr (ACT == ACT_RELU) {
-    return h > 0.0f ? 1.0f : 0.0f;
+    return h > 0.0f ? g : 0.0f;
   } else {
-    return 1.0f;
+    return g;
   }
 }
 
-// dW_l(wave block) += sH^T sZ over the tile's R rows.
-template <int D>
-__device__ __forceinline__ void weight_grad(uint32_t sH, uint32_t sZ, const BLane<D>& c, int w,
-                                            f32x4 (&dw)[BGeo<D>::QB][BGeo<D>::QB]) {
-  using G = BGeo<D>;
-  const uint32_t kb0 = (uint32_t)(G::QB * (w >> 1)), nb0 = (uint32_t)(G::QB * (w & 1));
-  uint32_t ha[G::QB], zb[G::QB];
+// Issue order of one pipeline step (as in the forward megakernel): NM MFMAs,
+// each followed by VPM VALU instructions and, after every DS_EVERY-th one, a
+// DS read.
+template <int NM, int VPM, int DS_EVERY>
+__device__ __forceinline__ void interleave_bwd() {
 #pragma unroll
-  for (int b = 0; b < G::QB; ++b) {
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i % DS_EVERY == DS_EVERY - 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, VPM, 0);
+  }
+}
+
+// VALU issue slots per element of the derivative step (the transcendental
+// counted twice).
+template <int ACT>
+constexpr int act_grad_ops() {
+  return ACT == ACT_SOFTPLUS ? 5 : ACT == ACT_RELU ? 2 : 0;
+}
+
+// One layer's matrix work for the wave, software-pipelined over the NT
+// 16-unit output sub-tiles of the data-gradient product.  Step t (0..NT)
+// issues the MFMAs of sub-tile t (its W fragments were read one step ahead),
+// the derivative and packing of sub-tile t - 1 (on results that are already
+// complete), and a share of the weight-gradient MFMAs (their transposing
+// reads one step ahead), so the matrix core, the VALU and the LDS all work
+// within the one wave a SIMD holds.
+//   weight gradient: dW_l(wave block) += sH^T sZ over the tile's R rows.  The
+//     wave's block is QB x QB 16 x 16 tiles: k tiles QB (w / 2) + i, n tiles
+//     QB (w % 2) + k; MFMA m = (j QB + i) QB + k covers rows 32 j .. + 31.
+//   MODE 1: dz_l = (dz_{l+1} W_l^T) * act'(h_l) for the wave's rows, packed
+//     to fp16 in B-operand form into out;
+//   MODE 2: dx = dz_1 W_0^T, stored as fp16 in pairs of sub-tiles;
+//   MODE 0: weight gradient only.
+template <int D, int l, int ACT, int MODE>
+__device__ __forceinline__ void layer_grads(const MlpBwdParams& p, const BLane<D>& c, uint32_t sH, uint32_t sZ,
+                                            int w, int tile, f32x4 (&dw)[BGeo<D>::QB][BGeo<D>::QB],
+                                            const FragB<D>& dz, const RowsF32<D>& h, FragB<D>& out) {
+  using G = BGeo<D>;
+  constexpr int NT = G::NT, MT = G::MT, KS = G::KS, QB = G::QB, CH = G::CH;
+  constexpr int NWG = CH * QB * QB;       // weight-gradient MFMAs
+  constexpr int PER = (NWG + NT - 1) / NT;  // of them per step
+  constexpr int NDG = MODE ? KS * MT : 0;   // data-gradient MFMAs per step
+  constexpr int VPE = MODE == 1 ? act_grad_ops<ACT>() : 0;
+  constexpr int VPS = MT * (4 * VPE + 2) + (MODE == 2 ? 2 : 0);  // VALU per step
+  constexpr int NM = NDG + PER;
+  constexpr int VPM = (VPS + NM - 1) / NM;
+
+  // transposing-read addresses of the wave's k tiles (sH) and n tiles (sZ)
+  const uint32_t kb0 = (uint32_t)(QB * (w >> 1)), nb0 = (uint32_t)(QB * (w & 1));
+  uint32_t ha[QB], zb[QB];
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
     ha[b] = (sH + c.trk) ^ ((kb0 + b) << 5);
     zb[b] = (sZ + c.trk) ^ ((nb0 + b) << 5);
   }
+  i16x8 fa[CH][QB], fb[CH][QB];
+  auto tr8 = [](uint32_t addr, int j) {
+    const i16x4 x0 = lds_tr(addr + (uint32_t)(32 * j * 2 * D));
+    const i16x4 x1 = lds_tr(addr + (uint32_t)((32 * j + 16) * 2 * D));
+    return (i16x8){x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+  };
+  // fragments first used by the MFMAs of step u
+  auto load_frags = [&](int u) {
 #pragma unroll
-  for (int j = 0; j < G::CH; ++j) {
-    i16x8 a[G::QB], b[G::QB];
-#pragma unroll
-    for (int i = 0; i < G::QB; ++i) {
-      const uint32_t r0 = (uint32_t)(32 * j * 2 * D), r4 = (uint32_t)((32 * j + 4) * 2 * D);
-      const i16x4 a0 = lds_tr(ha[i] + r0), a1 = lds_tr(ha[i] + r4);
-      const i16x4 b0 = lds_tr(zb[i] + r0), b1 = lds_tr(zb[i] + r4);
-      a[i] = (i16x8){a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      b[i] = (i16x8){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+    for (int m = u * PER; m < (u + 1) * PER && m < NWG; ++m) {
+      const int j = m / (QB * QB), i = (m / QB) % QB, k = m % QB;
+      if (k == 0) fa[j][i] = tr8(ha[i], j);
+      if (i == 0) fb[j][k] = tr8(zb[k], j);
     }
-#pragma unroll
-    for (int i = 0; i < G::QB; ++i)
-#pragma unroll
-      for (int k = 0; k < G::QB; ++k) dw[i][k] = mfma16x16x32(a[i], b[k], dw[i][k], _Float16());
-  }
-}
+  };
 
-// dz_l = (dz_{l+1} W_l^T) * act'(h_l) for the wave's rows: B operand dz
-// (registers), A operand W_l (LDS), result packed to fp16 in B form.
-template <int D, int l, int ACT>
-__device__ __forceinline__ void data_grad(const BLane<D>& c, const FragB<D>& dz, const RowsF32<D>& h,
-                                          FragB<D>& out) {
-  using G = BGeo<D>;
+  uint32_t wk[KS];
+  i16x8 wa[KS];
+  f32x4 acc[MT], prv[MT];
+  __amdgpu_buffer_rsrc_t rq[MT];
+  uint32_t qoff = 0;
+  u32x2 ev[MT];
+  if constexpr (MODE != 0) {
 #pragma unroll
-  for (int t = 0; t < G::NT; ++t) {
-    f32x4 acc[G::MT];
-#pragma unroll
-    for (int s = 0; s < G::MT; ++s) acc[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-      const i16x8 wa = lds_read128(opaque(c.wk[ks]) + 2u * (uint32_t)((l * D + 16 * t) * D));
-#pragma unroll
-      for (int s = 0; s < G::MT; ++s) acc[s] = mfma16x16x32(wa, __builtin_bit_cast(i16x8, dz.v[s][ks]), acc[s], _Float16());
-    }
-#pragma unroll
-    for (int s = 0; s < G::MT; ++s) {
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = ACT == ACT_NONE ? acc[s][i] : acc[s][i] * act_grad<ACT>(h.v[s][t][i]);
-      out.v[s][t >> 1][(t & 1) * 2] = pack_f16(v[0], v[1]);
-      out.v[s][t >> 1][(t & 1) * 2 + 1] = pack_f16(v[2], v[3]);
+    for (int ks = 0; ks < KS; ++ks) {
+      wk[ks] = opaque(c.wk[ks]) + 2u * (uint32_t)(l * D * D);
+      wa[ks] = lds_read128(wk[ks]);
     }
   }
-}
-
-// dx = dz_1 W_0^T for the wave's rows, stored as fp16 in pairs of unit blocks.
-template <int D>
-__device__ __forceinline__ void input_grad(const MlpBwdParams& p, const BLane<D>& c, const FragB<D>& dz, int tile,
-                                           int w) {
-  using G = BGeo<D>;
-  __amdgpu_buffer_rsrc_t rs[G::MT];
+  if constexpr (MODE == 2) {
 #pragma unroll
-  for (int s = 0; s < G::MT; ++s) rs[s] = brsrc<D>(p.dx, p.M, tile, w, s, p.ldq, 2);
-  const uint32_t qoff = opaque(c.qoff);
-  u32x2 ev[G::MT];
+    for (int s = 0; s < MT; ++s) rq[s] = brsrc<D>(p.dx, p.M, tile, w, s, p.ldq, 2);
+    qoff = opaque(c.qoff);
+  }
+  load_frags(0);
 #pragma unroll
-  for (int t = 0; t < G::NT; ++t) {
-    f32x4 acc[G::MT];
+  for (int t = 0; t <= NT; ++t) {
+    if constexpr (MODE != 0) {
+      if (t < NT) {
 #pragma unroll
-    for (int s = 0; s < G::MT; ++s) acc[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < MT; ++s) acc[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) {
-      const i16x8 wa = lds_read128(opaque(c.wk[ks]) + 2u * (uint32_t)(16 * t * D));
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int s = 0; s < G::MT; ++s) acc[s] = mfma16x16x32(wa, __builtin_bit_cast(i16x8, dz.v[s][ks]), acc[s], _Float16());
+          for (int s = 0; s < MT; ++s) acc[s] = mfma16x16x32(wa[ks], __builtin_bit_cast(i16x8, dz.v[s][ks]), acc[s], _Float16());
+          if (t + 1 < NT) wa[ks] = lds_read128(wk[ks] + 2u * (uint32_t)(16 * D * (t + 1)));
+        }
+      }
     }
+    if (t < NT) {
 #pragma unroll
-    for (int s = 0; s < G::MT; ++s) {
-      const u32x2 o = (u32x2){pack_f16(acc[s][0], acc[s][1]), pack_f16(acc[s][2], acc[s][3])};
-      if (t % 2 == 0)
-        ev[s] = o;
-      else
-        store_pair(rs[s], qoff + 32u * (uint32_t)(t - 1), ev[s], o);
+      for (int m = t * PER; m < (t + 1) * PER && m < NWG; ++m) {
+        const int j = m / (QB * QB), i = (m / QB) % QB, k = m % QB;
+        dw[i][k] = mfma16x16x32(fa[j][i], fb[j][k], dw[i][k], _Float16());
+      }
+      if (t + 1 < NT) load_frags(t + 1);
+    }
+    if constexpr (MODE != 0) {
+      if (t > 0) {
+        const int u = t - 1;
+#pragma unroll
+        for (int s = 0; s < MT; ++s) {
+          if constexpr (MODE == 1) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = apply_grad<ACT>(prv[s][i], h.v[s][u][i]);
+            out.v[s][u >> 1][(u & 1) * 2] = pack_f16(v[0], v[1]);
+            out.v[s][u >> 1][(u & 1) * 2 + 1] = pack_f16(v[2], v[3]);
+          } else {
+            const u32x2 o = (u32x2){pack_f16(prv[s][0], prv[s][1]), pack_f16(prv[s][2], prv[s][3])};
+            if (u % 2 == 0)
+              ev[s] = o;
+            else
+              store_pair(rq[s], qoff + 32u * (uint32_t)(u - 1), ev[s], o);
+          }
+        }
+      }
+    }
+    if (t < NT) interleave_bwd<NM, VPM, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MODE != 0) {
+#pragma unroll
+      for (int s = 0; s < MT; ++s) prv[s] = acc[s];
     }
   }
 }
@@ -336,73 +402,111 @@ __device__ __forceinline__ void input_grad(const MlpBwdParams& p, const BLane<D>
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 #pragma clang diagnostic pop
 
-// Registers carried through a tile.
-template <int D>
-struct BState {
-  FragB<D> dz;    // dz_{l+1} of the wave's rows (B form)
-  FragB<D> nz;    // dz_l being produced
-  RowsF32<D> h;   // h_l of the wave's rows (fp32): derivative source
-  RowsF32<D> ha;  // prefetch: the next fp32 activation layer
-  FragB<D> hx;    // prefetch: x (B form)
-  FragB<D> dn;    // prefetch: dout of the next tile
+// Register and LDS policy of a chain.
+//   FULL: every input of a tile has its own register buffer, reloaded with
+//     the next tile's rows right after its last use (an activation buffer
+//     after the derivative step of its layer, x and dout after staging), so
+//     the loads run most of a tile ahead of their use and no buffer is copied
+//     while its load is in flight.  Chains whose buffers would not fit next
+//     to their weight-gradient accumulators (4 layers of 128, 7 or 8 of 64)
+//     share one activation buffer, loaded one layer ahead.
+//   DB: two sets of staging buffers, used by alternate layers, so that one
+//     barrier per layer suffices (the set written for layer l - 1 was last
+//     read in layer l + 1, before the barrier of layer l).  4 layers of 128
+//     leave no LDS for it and keep one set with two barriers per layer.
+template <int D, int L>
+struct BPolicy {
+  static constexpr bool FULL = D == 128 ? L <= 3 : L <= 6;
+  static constexpr int NA = L == 1 ? 1 : (FULL ? L - 1 : 1);  // activation buffers
+  static constexpr bool DB = L * D * D * 2 + 4 * BGeo<D>::R * D * 2 <= 160 * 1024;
+  static constexpr int SETS = DB ? 2 : 1;
+  static constexpr uint32_t SZ = BGeo<D>::R * D * 2;  // bytes of one staging buffer
 };
 
-// Issue the load of h_j for `tile` (j >= 1: fp32 acts[j - 1]; j == 0: x).
-template <int D>
-__device__ __forceinline__ void prefetch_h(const MlpBwdParams& p, const BLane<D>& c, int j, int tile, int w,
-                                           BState<D>& st) {
+template <int D, int L>
+struct BState {
+  RowsF32<D> h;                      // !FULL: h_l of the wave's rows (fp32), the derivative source
+  RowsF32<D> a[BPolicy<D, L>::NA];   // FULL: a[j - 1] holds h_j; otherwise the next activation layer
+  FragB<D> hx;                       // x of the rows to stage next (B form)
+  FragB<D> dn;                       // dout of the next tile
+};
+
+// Issue the load of h_j of `tile` into its buffer (j >= 1: fp32 acts[j - 1];
+// j == 0: x).  Loads for a tile past the last one are issued anyway: their
+// buffer resources cover zero rows, so they read zeros without touching
+// memory, and the issue stream stays free of branches (a conditional load
+// makes the compiler wait for every outstanding load where the paths join).
+template <int D, int L>
+__device__ __forceinline__ void load_h(const MlpBwdParams& p, const BLane<D>& c, int j, int tile, int w,
+                                       BState<D, L>& st) {
   if (j >= 1)
-    load_acts<D>(p.acts[j - 1], p.lda, opaque(c.aoff), p.M, tile, w, st.ha);
+    load_acts<D>(p.acts[j - 1], p.lda, opaque(c.aoff), p.M, tile, w, st.a[BPolicy<D, L>::FULL ? j - 1 : 0]);
   else
     load_b<D>(p.x, p.ldx, opaque(c.boff), p.M, tile, w, st.hx);
 }
 
-// Layers l .. 0 of one tile.  On entry sH holds h_l and sZ holds dz_{l+1}
-// (this wave's rows written, the barrier not yet passed), st.dz holds
-// dz_{l+1}, st.h holds h_l (l >= 1), and the load of h_{l-1} (or of the
-// next tile's h_{L-1} when l == 0) is in flight.
-template <int D, int L, int l, int ACT, bool DX>
-__device__ __forceinline__ void tile_layers(const MlpBwdParams& p, const BLane<D>& c, uint32_t sH, uint32_t sZ,
-                                            int tile, int next, int w, BState<D>& st,
-                                            f32x4 (&dw)[L][BGeo<D>::QB][BGeo<D>::QB]) {
-  lds_barrier();
-  weight_grad<D>(sH, sZ, c, w, dw[l]);
-  if constexpr (l >= 1) {
-    data_grad<D, l, ACT>(c, st.dz, st.h, st.nz);
-    lds_barrier();
-    st.dz = st.nz;
-    stage_d<D>(sZ, c, st.dz);
-    if constexpr (l - 1 >= 1) {
-      FragB<D> hp;
-      pack_rows<D>(st.ha, hp);
-      stage_d<D>(sH, c, hp);
-      st.h = st.ha;
-    } else {
-      stage_b<D>(sH, c, st.hx);
+// Stage h_j of the current tile into the staging set `set` (sH = set, sZ =
+// set + SZ) and issue the loads that policy attaches to this point.
+template <int D, int L, int j>
+__device__ __forceinline__ void stage_h(const MlpBwdParams& p, const BLane<D>& c, uint32_t set, int tile, int next,
+                                        int w, BState<D, L>& st) {
+  constexpr bool FULL = BPolicy<D, L>::FULL;
+  if constexpr (j >= 1) {
+    FragB<D> hp;
+    pack_rows<D>(st.a[FULL ? j - 1 : 0], hp);
+    stage_d<D>(set, c, hp);
+    if constexpr (!FULL) {
+      st.h = st.a[0];
+      load_h<D, L>(p, c, j - 1, tile, w, st);  // the layer below, one layer ahead
     }
-    if constexpr (l - 2 >= 0)
-      prefetch_h<D>(p, c, l - 2, tile, w, st);
-    else if (next < p.num_tiles)
-      prefetch_h<D>(p, c, L - 1, next, w, st);
-    tile_layers<D, L, l - 1, ACT, DX>(p, c, sH, sZ, tile, next, w, st, dw);
   } else {
-    if constexpr (DX) input_grad<D>(p, c, st.dz, tile, w);
-    lds_barrier();
+    stage_b<D>(set, c, st.hx);
+    if constexpr (FULL)
+      load_h<D, L>(p, c, 0, next, w, st);
+    else
+      load_h<D, L>(p, c, L - 1, next, w, st);  // the next tile's first activation layer
+  }
+}
+
+// Layers l .. 0 of one tile.  On entry the staging set `cur` holds h_l and
+// dz_{l+1} (this wave's rows written, the barrier not yet passed), dz holds
+// dz_{l+1}; nz receives dz_l.  With DB, layer l - 1 stages into `nxt`.
+template <int D, int L, int l, int ACT, bool DX>
+__device__ __forceinline__ void tile_layers(const MlpBwdParams& p, const BLane<D>& c, uint32_t cur, uint32_t nxt,
+                                            int tile, int next, int w, BState<D, L>& st, FragB<D>& dz,
+                                            FragB<D>& nz, f32x4 (&dw)[L][BGeo<D>::QB][BGeo<D>::QB]) {
+  using P = BPolicy<D, L>;
+  lds_barrier();
+  if constexpr (l >= 1) {
+    if constexpr (P::FULL) {
+      layer_grads<D, l, ACT, 1>(p, c, cur, cur + P::SZ, w, tile, dw[l], dz, st.a[l - 1], nz);
+      load_h<D, L>(p, c, l, next, w, st);  // h_l of the next tile, after its last use here
+    } else {
+      layer_grads<D, l, ACT, 1>(p, c, cur, cur + P::SZ, w, tile, dw[l], dz, st.h, nz);
+    }
+    if constexpr (!P::DB) lds_barrier();
+    const uint32_t dst = P::DB ? nxt : cur;
+    stage_d<D>(dst + P::SZ, c, nz);
+    stage_h<D, L, l - 1>(p, c, dst, tile, next, w, st);
+    tile_layers<D, L, l - 1, ACT, DX>(p, c, dst, P::DB ? cur : nxt, tile, next, w, st, nz, dz, dw);
+  } else {
+    layer_grads<D, 0, ACT, DX ? 2 : 0>(p, c, cur, cur + P::SZ, w, tile, dw[0], dz, st.h, nz);
+    if constexpr (!P::DB) lds_barrier();
   }
 }
 
 template <int D, int L, int ACT, bool DX>
 __global__ __launch_bounds__(BGeo<D>::THREADS, 1) void mlp_bwd_kernel(MlpBwdParams p) {
   using G = BGeo<D>;
+  using P = BPolicy<D, L>;
   __shared__ __attribute__((aligned(16))) _Float16 sW[L * D * D];
-  __shared__ __attribute__((aligned(256))) _Float16 sHbuf[G::R * D];
-  __shared__ __attribute__((aligned(256))) _Float16 sZbuf[G::R * D];
+  __shared__ __attribute__((aligned(256))) _Float16 sStage[P::SETS * 2 * G::R * D];
   stage_weights_bwd<D, L>(p, sW);
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BLane<D> c = blane_setup<D>(p, sW, w, lane);
-  const uint32_t sH = lds_addr(sHbuf), sZ = lds_addr(sZbuf);
+  uint32_t cur = lds_addr(sStage), nxt = cur + (P::DB ? 2 * P::SZ : 0);
   const uint32_t doff = (uint32_t)(lane & 15) * (uint32_t)p.ldd * 2u + 16u * (uint32_t)(lane >> 4);
 
   f32x4 dw[L][G::QB][G::QB];
@@ -413,32 +517,34 @@ __global__ __launch_bounds__(BGeo<D>::THREADS, 1) void mlp_bwd_kernel(MlpBwdPara
 #pragma unroll
       for (int k = 0; k < G::QB; ++k) dw[l][i][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  BState<D> st;
+  BState<D, L> st;
+  FragB<D> dz, nz;
   int tile = blockIdx.x;
   if (tile < p.num_tiles) {
     load_b<D>(p.dout, p.ldd, doff, p.M, tile, w, st.dn);
-    prefetch_h<D>(p, c, L - 1, tile, w, st);
+    if constexpr (P::FULL) {
+#pragma unroll
+      for (int j = L - 1; j >= 0; --j) load_h<D, L>(p, c, j, tile, w, st);
+    } else {
+      load_h<D, L>(p, c, L - 1, tile, w, st);
+    }
   }
   __syncthreads();  // weights staged
   while (tile < p.num_tiles) {
     const int next = tile + (int)gridDim.x;
     // the tile's first layer: sZ <- dout, sH <- h_{L-1}
-    st.dz = st.dn;
-    stage_b<D>(sZ, c, st.dz);
-    if constexpr (L >= 2) {
-      FragB<D> hp;
-      pack_rows<D>(st.ha, hp);
-      stage_d<D>(sH, c, hp);
-      st.h = st.ha;
-    } else {
-      stage_b<D>(sH, c, st.hx);
+    dz = st.dn;
+    stage_b<D>(cur + P::SZ, c, dz);
+    load_b<D>(p.dout, p.ldd, doff, p.M, next, w, st.dn);  // zero rows past the last tile
+    stage_h<D, L, L - 1>(p, c, cur, tile, next, w, st);
+    tile_layers<D, L, L - 1, ACT, DX>(p, c, cur, nxt, tile, next, w, st, dz, nz, dw);
+    // layer l used set cur when L - 1 - l is even: the next tile starts on the
+    // set that layer 0 did not use
+    if constexpr (P::DB && (L % 2 == 1)) {
+      const uint32_t t = cur;
+      cur = nxt;
+      nxt = t;
     }
-    if (next < p.num_tiles) load_b<D>(p.dout, p.ldd, doff, p.M, next, w, st.dn);
-    if constexpr (L >= 2)
-      prefetch_h<D>(p, c, L - 2, tile, w, st);
-    else if (next < p.num_tiles)
-      prefetch_h<D>(p, c, 0, next, w, st);
-    tile_layers<D, L, L - 1, ACT, DX>(p, c, sH, sZ, tile, next, w, st, dw);
     tile = next;
   }
 
@@ -456,27 +562,42 @@ __global__ __launch_bounds__(BGeo<D>::THREADS, 1) void mlp_bwd_kernel(MlpBwdPara
       }
 }
 
-// dW_l = sum over the grid's partials, in workgroup order.  One thread per
-// (layer, 16 x 16 block, lane): register i of lane (g, q) of block (kb, nb)
-// is dW[16 kb + 4 g + i][16 nb + q].
+// dW_l = sum over the grid's partials.  The partials are viewed as rows of
+// E = L D D / 4 float4 groups; a workgroup owns 32 groups and splits the
+// partial index over 8 slices (slice s adds partials s, s + 8, ... in order),
+// then adds the 8 slice sums in slice order: a fixed order, so the result is
+// the same on every call with the same grid.  Register i of lane (g, q) of
+// block (kb, nb) is dW[16 kb + 4 g + i][16 nb + q].
+constexpr int RED_GROUPS = 32, RED_SLICES = 8;
+
 template <int D>
-__global__ __launch_bounds__(256) void mlp_bwd_reduce(const float* __restrict__ partial, int nparts, int L,
-                                                      MlpBwdParams p) {
-  const int idx = blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(RED_GROUPS* RED_SLICES) void mlp_bwd_reduce(const float* __restrict__ partial, int nparts,
+                                                                         int L, MlpBwdParams p) {
+  __shared__ f32x4 red[RED_SLICES][RED_GROUPS];
+  const int gi = threadIdx.x % RED_GROUPS, slice = threadIdx.x / RED_GROUPS;
+  const int E = L * D * D / 4;
+  const int e = blockIdx.x * RED_GROUPS + gi;
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (e < E) {
+    const f32x4* src = (const f32x4*)partial + e;
+#pragma unroll 8
+    for (int b = slice; b < nparts; b += RED_SLICES) acc += src[(size_t)b * E];
+  }
+  red[slice][gi] = acc;
+  __syncthreads();
+  if (slice != 0 || e >= E) return;
+  f32x4 sum = red[0][gi];
+#pragma unroll
+  for (int k = 1; k < RED_SLICES; ++k) sum += red[k][gi];
   const int per_layer = D * D / 4;
-  if (idx >= L * per_layer) return;
-  const int l = idx / per_layer;
-  const int rem = idx - l * per_layer;
+  const int l = e / per_layer;
+  const int rem = e - l * per_layer;
   const int blk = rem >> 6, lane = rem & 63;
-  const size_t stride = (size_t)L * D * D;
-  const float* src = partial + (size_t)l * D * D + 4 * (size_t)rem;
-  f32x4 acc = *(const f32x4*)src;
-  for (int b = 1; b < nparts; ++b) acc += *(const f32x4*)(src + (size_t)b * stride);
   const int kb = blk / (D / 16), nb = blk - kb * (D / 16);
   const int k = 16 * kb + 4 * (lane >> 4), n = 16 * nb + (lane & 15);
   float* dst = p.dW[l];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dst[(k + i) * D + n] = acc[i];
+  for (int i = 0; i < 4; ++i) dst[(k + i) * D + n] = sum[i];
 }
 
 template <int D, int L, int ACT, bool DX>
@@ -488,8 +609,9 @@ hipError_t launch_bwd_dl(MlpBwdParams p, int num_cus, hipStream_t stream) {
   hipLaunchKernelGGL((mlp_bwd_kernel<D, L, ACT, DX>), dim3(nwg), dim3(G::THREADS), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int threads = L * D * D / 4;
-  hipLaunchKernelGGL((mlp_bwd_reduce<D>), dim3((threads + 255) / 256), dim3(256), 0, stream, p.partial, nwg, L, p);
+  const int groups = L * D * D / 4;
+  hipLaunchKernelGGL((mlp_bwd_reduce<D>), dim3((groups + RED_GROUPS - 1) / RED_GROUPS), dim3(RED_GROUPS * RED_SLICES),
+                     0, stream, p.partial, nwg, L, p);
   return hipGetLastError();
 }
 
