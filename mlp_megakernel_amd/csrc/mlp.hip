@@ -483,21 +483,25 @@ __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(M
   int tile = wave;
   // Three activation buffers in rotation: the x of the next tile is loaded
   // into the third one when a tile starts, a whole tile ahead of its use.
+  // The load is issued even past the last tile (its buffer resources cover
+  // zero rows, so it reads zeros without touching memory): a conditional
+  // load would make the compiler wait for every outstanding memory operation
+  // where the paths join, stores included.
   HTile<D> ha, hb, hc;
   if (tile < p.num_tiles) load_x<D>(p, c, tile, ha);
   while (tile < p.num_tiles) {
     int next = tile + nwaves;
-    if (next < p.num_tiles) load_x<D>(p, c, next, hc);
+    load_x<D>(p, c, next, hc);
     tile_chain<D, L, 0, ACT, ST>(p, c, tile, ha, hb, mx);
     tile = next;
     if (tile >= p.num_tiles) break;
     next = tile + nwaves;
-    if (next < p.num_tiles) load_x<D>(p, c, next, hb);
+    load_x<D>(p, c, next, hb);
     tile_chain<D, L, 0, ACT, ST>(p, c, tile, hc, ha, mx);
     tile = next;
     if (tile >= p.num_tiles) break;
     next = tile + nwaves;
-    if (next < p.num_tiles) load_x<D>(p, c, next, ha);
+    load_x<D>(p, c, next, ha);
     tile_chain<D, L, 0, ACT, ST>(p, c, tile, hb, hc, mx);
     tile = next;
   }
