@@ -69,6 +69,10 @@ def _load():
     lib.oracle_act_deriv.argtypes = [d, i32]
     lib.oracle_mlp_forward_train.restype = i32
     lib.oracle_mlp_forward_train.argtypes = [p, p, p, i32, p, p, i64, i32, i32]
+    lib.oracle_weight_norm.restype = i32
+    lib.oracle_weight_norm.argtypes = [p, p, p, i64, i64]
+    lib.oracle_weight_norm_backward.restype = i32
+    lib.oracle_weight_norm_backward.argtypes = [p, p, p, p, p, i64, i64]
     lib.oracle_mlp_backward.restype = i32
     lib.oracle_mlp_backward.argtypes = [p, p, p, i32, p, p, p, i64, i32, i32]
     _lib = lib
@@ -263,3 +267,34 @@ def mlp_backward(x, weights: Sequence, dout, hidden_act="softplus", want_dx: boo
     if rc != 0:
         raise ValueError("oracle_mlp_backward rejected its arguments")
     return dWs, dx
+
+
+def weight_norm(v, g) -> np.ndarray:
+    """W = g * v / ||v|| per output unit (column of the x @ W matrix)
+    ("MLP Megakernel" README, "Key ideas": fused weight normalisation)."""
+    lib = _load()
+    v = _f64(v)
+    g = _f64(g).reshape(-1)
+    din, dout = v.shape
+    if g.shape[0] != dout:
+        raise ValueError("g must have one gain per output unit")
+    W = np.empty_like(v)
+    if lib.oracle_weight_norm(_ptr(v), _ptr(g), _ptr(W), din, dout) != 0:
+        raise ValueError("oracle_weight_norm rejected its arguments")
+    return W
+
+
+def weight_norm_backward(v, g, dW):
+    """(dv, dg): gradients of sum(dW * weight_norm(v, g)) with respect to v and g."""
+    lib = _load()
+    v = _f64(v)
+    g = _f64(g).reshape(-1)
+    dW = _f64(dW)
+    din, dout = v.shape
+    if g.shape[0] != dout or dW.shape != v.shape:
+        raise ValueError("shapes of v, g and dW do not match")
+    dv = np.empty_like(v)
+    dg = np.empty(dout, dtype=np.float64)
+    if lib.oracle_weight_norm_backward(_ptr(v), _ptr(g), _ptr(dW), _ptr(dv), _ptr(dg), din, dout) != 0:
+        raise ValueError("oracle_weight_norm_backward rejected its arguments")
+    return dv, dg

@@ -20,6 +20,10 @@
  *  - same README, "Ablation Study / Key findings": softplus(x) = log(1 + e^x)
  *    (the page's guarded form switches to x above 20; the oracle instead
  *    evaluates the exact function in fp64, see oracle_softplus).
+ *  - same README, "Key ideas" (fused weight normalisation W = g v / ||v||):
+ *    the norm is taken per output unit -- over each column of the x @ W
+ *    matrix, torch's weight_norm on a Linear weight -- with one gain g per
+ *    output unit; oracle_weight_norm and its backward.
  *  - same README, "Key ideas" (training: the forward keeps the hidden
  *    activations, the backward multiplies by the derivative of softplus) and
  *    the quick start's out.sum().backward(): the gradients of the chain with
@@ -353,4 +357,46 @@ int oracle_mlp_backward(const double* x, const double* const* W, const int64_t* 
   }
   free(buf);
   return bad ? -1 : 0;
+}
+
+/*
+ * Weight normalisation ("MLP Megakernel" README, "Key ideas"):
+ *   W[k][n] = g[n] v[k][n] / ||v[:, n]||,   ||v[:, n]|| = sqrt(sum_k v[k][n]^2)
+ * for a din x dout matrix v (row-major, the x @ W orientation) and a gain per
+ * output unit n.  A zero column gives 0 * g / 0 = NaN (no guard, as in the
+ * plain formula).  Returns 0, or -1 on a bad argument.
+ */
+int oracle_weight_norm(const double* v, const double* g, double* W, int64_t din, int64_t dout) {
+  if (din < 0 || dout < 0) return -1;
+  if (din > 0 && dout > 0 && (!v || !g || !W)) return -1;
+  for (int64_t n = 0; n < dout; ++n) {
+    double ss = 0.0;
+    for (int64_t k = 0; k < din; ++k) ss += v[k * dout + n] * v[k * dout + n];
+    const double nrm = sqrt(ss);
+    for (int64_t k = 0; k < din; ++k) W[k * dout + n] = g[n] * v[k * dout + n] / nrm;
+  }
+  return 0;
+}
+
+/*
+ * Backward of oracle_weight_norm given dW = dLoss/dW, by the chain rule:
+ *   dg[n]    = sum_k dW[k][n] v[k][n] / ||v_n||
+ *   dv[k][n] = g[n] / ||v_n|| * (dW[k][n] - v[k][n] (sum_j v[j][n] dW[j][n]) / ||v_n||^2)
+ */
+int oracle_weight_norm_backward(const double* v, const double* g, const double* dW, double* dv, double* dg,
+                                int64_t din, int64_t dout) {
+  if (din < 0 || dout < 0) return -1;
+  if (din > 0 && dout > 0 && (!v || !g || !dW || !dv || !dg)) return -1;
+  for (int64_t n = 0; n < dout; ++n) {
+    double ss = 0.0, dot = 0.0;
+    for (int64_t k = 0; k < din; ++k) {
+      ss += v[k * dout + n] * v[k * dout + n];
+      dot += v[k * dout + n] * dW[k * dout + n];
+    }
+    const double nrm = sqrt(ss);
+    dg[n] = dot / nrm;
+    for (int64_t k = 0; k < din; ++k)
+      dv[k * dout + n] = g[n] / nrm * (dW[k * dout + n] - v[k * dout + n] * dot / ss);
+  }
+  return 0;
 }
