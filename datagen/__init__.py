@@ -14,7 +14,8 @@ Recipe (the same everywhere):
   * values are drawn in float64, rounded to float32 (round to nearest even),
     then to bf16/fp16 (round to nearest even) when the input type is 16-bit;
   * tensor ids: A = 1, B = 2, bias = 3, x = 10, W_l = 10 + l (l = 1..L),
-    the upstream gradient dout of the MLP backward = 30.
+    the upstream gradient dout of the MLP backward = 30, weight-normalisation
+    directions v_l = 40 + l and gains g_l = 60 + l.
 
 Workloads (``WORKLOADS``) carry the shapes and value distributions of the
 pages' problems: the FP32 square GEMM + bias + GELU shapes of the "Coalesce"
@@ -199,6 +200,18 @@ def mlp_grad_output(w: MlpWorkload, M: Optional[int] = None, dims: Optional[Sequ
     M = w.M if M is None else M
     dims = tuple(w.dims if dims is None else dims)
     return normal(w.seed_id, TENSOR_DOUT, (M, dims[-1]), 1.0, w.dtype)
+
+
+def wn_inputs(w: MlpWorkload, dims: Optional[Sequence[int]] = None):
+    """([v_1..v_L], [g_1..g_L]) CPU tensors of a weight-normalised chain:
+    v_l ~ N(0, 1/sqrt(d_{l-1})) (d_{l-1} x d_l), g_l ~ N(1, 0.25) (d_l), in
+    the workload's dtype."""
+    dims = tuple(w.dims if dims is None else dims)
+    vs = [normal(w.seed_id, 40 + l + 1, (dims[l], dims[l + 1]), 1.0 / np.sqrt(dims[l]), w.dtype)
+          for l in range(len(dims) - 1)]
+    gs = [_quantize(1.0 + 0.25 * _rng(w.seed_id, 60 + l + 1).standard_normal(dims[l + 1]), w.dtype)
+          for l in range(len(dims) - 1)]
+    return vs, gs
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:

@@ -176,6 +176,38 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
                                       size_t workspace_bytes, void* stream);
 
 /*
+ * Weight normalisation of every layer of a chain in ONE launch ("MLP
+ * Megakernel" README, "Key ideas": the fused kernel normalises all weight
+ * matrices, W = g * v / ||v||, so that per-layer launches do not dominate at
+ * small sizes).  The norm is taken per output unit, i.e. over each column of
+ * the x @ W matrix (torch's weight_norm on a Linear weight):
+ *   W[l][k][n] = g[l][n] * v[l][k][n] / sqrt(sum_k v[l][k][n]^2)
+ *   v, W  HOST arrays of L device pointers; layer l is dims[l] x dims[l+1]
+ *         fp16, dense row-major; W[l] is written
+ *   g     HOST array of L device pointers to dims[l+1] fp16 gains
+ *   dims  HOST array of L + 1 positive widths; 1 <= L <= 16
+ * Sums of squares in fp32 (added in a fixed order), the scale g / ||v|| in
+ * fp32, one rounding of W to fp16.  A column of zeros gives NaN, as the
+ * formula does.  dtype must be F16.  Outputs must not overlap inputs.
+ */
+coalesce_status coalesce_weight_norm(const void* const* v, const void* const* g, void* const* W, const int64_t* dims,
+                                     int32_t L, coalesce_dtype dtype, void* stream);
+
+/*
+ * Backward of coalesce_weight_norm for all layers in one launch, from the
+ * weight gradients dW (fp32, e.g. from coalesce_mlp_backward):
+ *   dg[l][n]    = <dW[l][:, n], v[l][:, n]> / ||v[l][:, n]||
+ *   dv[l][k][n] = g[l][n] / ||v[l][:, n]|| * (dW[l][k][n] - v[l][k][n] <dW, v>_n / ||v_n||^2)
+ *   v, g, dims  as coalesce_weight_norm (fp16)
+ *   dW          HOST array of L device pointers, dims[l] x dims[l+1] fp32
+ *   dv, dg      HOST arrays of L device pointers, fp32, written
+ * Everything in fp32; reductions in a fixed order.
+ */
+coalesce_status coalesce_weight_norm_backward(const void* const* v, const void* const* g, const float* const* dW,
+                                              float* const* dv, float* const* dg, const int64_t* dims, int32_t L,
+                                              coalesce_dtype dtype, void* stream);
+
+/*
  * Unfused baseline, step 2: Y = X + bias (bias broadcast over rows), each
  * element converted to fp32, added, and rounded once to y_dtype.  The
  * elementwise-kernel design of the "Fuse Elementwise Ops" page (vectorised

@@ -36,6 +36,8 @@ SIGNATURES = {
     "coalesce_mlp_backward_workspace_size": (_sz, [_p, _i32]),
     "coalesce_mlp_backward": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _p, _i64, _p, _p, _i64, _i64, _i32, _i32,
                                      _p, _sz, _p]),
+    "coalesce_weight_norm": (_i32, [_p, _p, _p, _p, _i32, _i32, _p]),
+    "coalesce_weight_norm_backward": (_i32, [_p, _p, _p, _p, _p, _p, _i32, _i32, _p]),
     "coalesce_bias_add": (_i32, [_p, _i64, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
     "coalesce_activation": (_i32, [_p, _i64, _p, _i64, _i64, _i64, _i32, _i32, _p]),
     "coalesce_flush_caches": (_i32, [_p, _sz, _p, _p]),
@@ -266,6 +268,56 @@ def mlp_backward(x: torch.Tensor, weights: Sequence[torch.Tensor], acts: Sequenc
     return list(dW), dx
 
 
+def _wn_dims(vs, gs):
+    if len(vs) != len(gs) or not vs:
+        raise ValueError("need one gain vector per weight matrix")
+    dims = [vs[0].shape[0]]
+    for i, (v, g) in enumerate(zip(vs, gs)):
+        if v.dim() != 2 or not v.is_contiguous() or not v.is_cuda or v.dtype != torch.float16:
+            raise ValueError("v[%d] must be a contiguous 2-D fp16 device tensor" % i)
+        if v.shape[0] != dims[-1]:
+            raise ValueError("layer widths do not chain")
+        if g.shape != (v.shape[1],) or not g.is_contiguous() or g.dtype != torch.float16 or not g.is_cuda:
+            raise ValueError("g[%d] must be a contiguous fp16 device vector of v's column count" % i)
+        dims.append(v.shape[1])
+    return dims
+
+
+def weight_norm(vs: Sequence[torch.Tensor], gs: Sequence[torch.Tensor], Ws: Optional[Sequence[torch.Tensor]] = None,
+                stream=None):
+    """[W_l = g_l * v_l / ||v_l||] (norm per column) for all layers in one
+    launch (coalesce_weight_norm)."""
+    lib = load_library()
+    dims = _wn_dims(vs, gs)
+    if Ws is None:
+        Ws = [torch.empty_like(v) for v in vs]
+    for W, v in zip(Ws, vs):
+        if W.shape != v.shape or W.dtype != v.dtype or not W.is_contiguous():
+            raise ValueError("every W must be a contiguous tensor shaped like its v")
+    dp = (ctypes.c_int64 * len(dims))(*dims)
+    _check(lib.coalesce_weight_norm(_ptr_array(vs), _ptr_array(gs), _ptr_array(Ws), ctypes.cast(dp, ctypes.c_void_p),
+                                    len(vs), F16, _stream(stream)))
+    return list(Ws)
+
+
+def weight_norm_backward(vs: Sequence[torch.Tensor], gs: Sequence[torch.Tensor], dWs: Sequence[torch.Tensor],
+                         stream=None):
+    """(dv list, dg list), fp32, for all layers in one launch
+    (coalesce_weight_norm_backward)."""
+    lib = load_library()
+    dims = _wn_dims(vs, gs)
+    for i, (dW, v) in enumerate(zip(dWs, vs)):
+        if dW.shape != v.shape or dW.dtype != torch.float32 or not dW.is_contiguous():
+            raise ValueError("dW[%d] must be a contiguous float32 tensor shaped like v[%d]" % (i, i))
+    dvs = [torch.empty(v.shape, dtype=torch.float32, device=v.device) for v in vs]
+    dgs = [torch.empty(g.shape, dtype=torch.float32, device=g.device) for g in gs]
+    dp = (ctypes.c_int64 * len(dims))(*dims)
+    _check(lib.coalesce_weight_norm_backward(_ptr_array(vs), _ptr_array(gs), _ptr_array(dWs), _ptr_array(dvs),
+                                             _ptr_array(dgs), ctypes.cast(dp, ctypes.c_void_p), len(vs), F16,
+                                             _stream(stream)))
+    return dvs, dgs
+
+
 def bias_add(X: torch.Tensor, bias: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
     """Y = X + bias (unfused baseline step)."""
     lib = load_library()
@@ -359,3 +411,62 @@ class FusedMLPSoftplus(torch.nn.Module):
         if torch.is_grad_enabled() and (x.requires_grad or any(w.requires_grad for w in ws)):
             return _FusedMLPFunction.apply(x, self.hidden_act, *ws)
         return mlp_forward(x, ws, hidden_act=self.hidden_act)
+
+
+class _FusedMLPWNFunction(torch.autograd.Function):
+    """Training step of the weight-normalised chain: one launch normalises
+    every layer, the training megakernel runs the chain, and the backward is
+    the fused backward followed by one weight-normalisation backward launch."""
+
+    @staticmethod
+    def forward(ctx, x, hidden_act, L, *vg):
+        vs, gs = list(vg[:L]), list(vg[L:])
+        Ws = weight_norm(vs, gs)
+        out, acts = mlp_forward_train(x, Ws, hidden_act=hidden_act)
+        ctx.hidden_act = hidden_act
+        ctx.L = L
+        ctx.save_for_backward(x, *vs, *gs, *Ws, *acts)
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        L = ctx.L
+        saved = ctx.saved_tensors
+        x, vs, gs, Ws, acts = saved[0], list(saved[1:1 + L]), list(saved[1 + L:1 + 2 * L]), \
+            list(saved[1 + 2 * L:1 + 3 * L]), list(saved[1 + 3 * L:])
+        if dout.dim() != 2 or dout.stride(-1) != 1 or (dout.data_ptr() % 16) or (dout.stride(0) * 2) % 16:
+            dout = aligned_copy(dout.to(x.dtype), dout.device)
+        dW, dx = mlp_backward(x, Ws, acts, dout.to(x.dtype), hidden_act=ctx.hidden_act,
+                              want_dx=ctx.needs_input_grad[0])
+        dvs, dgs = weight_norm_backward(vs, gs, dW)
+        return (dx, None, None) + tuple(d.to(v.dtype) for d, v in zip(dvs, vs)) + \
+            tuple(d.to(g.dtype) for d, g in zip(dgs, gs))
+
+
+class FusedMLPSoftplusWN(torch.nn.Module):
+    """The weight-normalised module of the page's quick start: parameters
+    v_l (direction) and g_l (one gain per output unit), W_l = g_l v_l / ||v_l||
+    computed for all layers in one launch before the megakernel."""
+
+    def __init__(self, D: int = 128, H: int = 128, out_features: int = 128, layers: int = 3,
+                 device="cuda", dtype=torch.float16, hidden_act="softplus"):
+        super().__init__()
+        dims = [D] + [H] * (layers - 1) + [out_features]
+        self.hidden_act = hidden_act
+        self.v = torch.nn.ParameterList(
+            [torch.nn.Parameter(torch.empty(dims[i], dims[i + 1], device=device, dtype=dtype)) for i in range(layers)])
+        self.g = torch.nn.ParameterList(
+            [torch.nn.Parameter(torch.empty(dims[i + 1], device=device, dtype=dtype)) for i in range(layers)])
+        with torch.no_grad():
+            for v, g in zip(self.v, self.g):
+                torch.nn.init.normal_(v, std=v.shape[0] ** -0.5)
+                g.copy_(v.float().norm(dim=0).to(dtype))  # W starts equal to v
+
+    def weights(self):
+        return weight_norm([v for v in self.v], [g for g in self.g])
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        vs, gs = [v for v in self.v], [g for g in self.g]
+        if torch.is_grad_enabled() and (x.requires_grad or any(p.requires_grad for p in vs + gs)):
+            return _FusedMLPWNFunction.apply(x, self.hidden_act, len(vs), *vs, *gs)
+        return mlp_forward(x, weight_norm(vs, gs), hidden_act=self.hidden_act)

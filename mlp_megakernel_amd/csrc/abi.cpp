@@ -350,6 +350,33 @@ coalesce_status coalesce_mlp_forward(const void* x, int64_t ldx, const void* con
   return coalesce_mlp_forward_grid(x, ldx, W, dims, L, out, ldo, M, dtype, hidden_act, 0, stream);
 }
 
+// Shared checks of the weight-normalisation entry points: a chain of L
+// (1..16) layers of positive widths, fp16, every pointer present.
+static coalesce_status check_wn(const int64_t* dims, int32_t L, coalesce_dtype dtype, const void* const* a,
+                                const char* an, const void* const* b, const char* bn, WnParams* p) {
+  if (!dims) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (L < 1) return fail(COALESCE_ERR_INVALID_ARGUMENT, "L must be at least 1 (got %d)", (int)L);
+  if (L > kMaxWnLayers) return fail(COALESCE_ERR_UNSUPPORTED, "at most %d layers per call", kMaxWnLayers);
+  if (!valid_dtype(dtype)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown dtype");
+  if (dtype != COALESCE_F16) return fail(COALESCE_ERR_UNSUPPORTED, "weight normalisation takes fp16 v and g");
+  for (int l = 0; l <= L; ++l)
+    if (dims[l] <= 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dims[%d] = %lld is not positive", l, (long long)dims[l]);
+  for (int l = 0; l < L; ++l)
+    if (dims[l] * dims[l + 1] > kMaxExtent || dims[l + 1] > 65535LL * 64)
+      return fail(COALESCE_ERR_UNSUPPORTED, "layer %d is too large", l);
+  if (!a || !b) return fail(COALESCE_ERR_INVALID_ARGUMENT, "%s or %s is NULL", an, bn);
+  p->L = L;
+  for (int l = 0; l < L; ++l) {
+    if (!a[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "%s[%d] is NULL", an, l);
+    if (!b[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "%s[%d] is NULL", bn, l);
+    if ((reinterpret_cast<uintptr_t>(a[l]) | reinterpret_cast<uintptr_t>(b[l])) & 1u)
+      return fail(COALESCE_ERR_UNSUPPORTED, "%s[%d] and %s[%d] must be 2-byte aligned", an, l, bn, l);
+    p->din[l] = (int)dims[l];
+    p->dout[l] = (int)dims[l + 1];
+  }
+  return COALESCE_OK;
+}
+
 static coalesce_status check_elementwise(const void* X, int64_t ldx, void* Y, int64_t ldy, int64_t M, int64_t N,
                                          int64_t es) {
   if (M < 0 || N < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative extent");
@@ -410,6 +437,63 @@ coalesce_status coalesce_flush_caches(const void* buf, size_t bytes, void* sink,
   if (s != COALESCE_OK) return s;
   hipError_t e = launch_flush(buf, bytes, sink, (hipStream_t)stream, cus);
   if (e != hipSuccess) return device_fail(e, "flush launch");
+  return ok();
+}
+
+coalesce_status coalesce_weight_norm(const void* const* v, const void* const* g, void* const* W, const int64_t* dims,
+                                     int32_t L, coalesce_dtype dtype, void* stream) {
+  WnParams p{};
+  coalesce_status s = check_wn(dims, L, dtype, v, "v", g, "g", &p);
+  if (s != COALESCE_OK) return s;
+  if (!W) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W is NULL");
+  for (int l = 0; l < L; ++l) {
+    if (!W[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W[%d] is NULL", l);
+    if (reinterpret_cast<uintptr_t>(W[l]) & 1u) return fail(COALESCE_ERR_UNSUPPORTED, "W[%d] must be 2-byte aligned", l);
+    const Range rw = span(W[l], dims[l], dims[l + 1], dims[l + 1], 2);
+    for (int j = 0; j < L; ++j)
+      if (overlap(rw, span(v[j], dims[j], dims[j + 1], dims[j + 1], 2)) || overlap(rw, span(g[j], 1, dims[j + 1], dims[j + 1], 2)) ||
+          (j != l && overlap(rw, span(W[j], dims[j], dims[j + 1], dims[j + 1], 2))))
+        return fail(COALESCE_ERR_INVALID_ARGUMENT, "W[%d] overlaps an input or another output", l);
+    p.v[l] = v[l];
+    p.g[l] = g[l];
+    p.W[l] = W[l];
+  }
+  hipError_t e = launch_weight_norm(p, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "weight_norm launch");
+  return ok();
+}
+
+coalesce_status coalesce_weight_norm_backward(const void* const* v, const void* const* g, const float* const* dW,
+                                              float* const* dv, float* const* dg, const int64_t* dims, int32_t L,
+                                              coalesce_dtype dtype, void* stream) {
+  WnParams p{};
+  coalesce_status s = check_wn(dims, L, dtype, v, "v", g, "g", &p);
+  if (s != COALESCE_OK) return s;
+  if (!dW || !dv || !dg) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW, dv or dg is NULL");
+  for (int l = 0; l < L; ++l) {
+    if (!dW[l] || !dv[l] || !dg[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW, dv or dg[%d] is NULL", l);
+    if ((reinterpret_cast<uintptr_t>(dW[l]) | reinterpret_cast<uintptr_t>(dv[l]) | reinterpret_cast<uintptr_t>(dg[l])) & 3u)
+      return fail(COALESCE_ERR_UNSUPPORTED, "dW, dv and dg[%d] must be 4-byte aligned", l);
+    const Range rv = span(dv[l], dims[l], dims[l + 1], dims[l + 1], 4), rg = span(dg[l], 1, dims[l + 1], dims[l + 1], 4);
+    if (overlap(rv, rg)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dv[%d] overlaps dg[%d]", l, l);
+    for (int j = 0; j < L; ++j) {
+      const Range ins[3] = {span(v[j], dims[j], dims[j + 1], dims[j + 1], 2), span(g[j], 1, dims[j + 1], dims[j + 1], 2),
+                            span(dW[j], dims[j], dims[j + 1], dims[j + 1], 4)};
+      for (const Range& r : ins)
+        if (overlap(rv, r) || overlap(rg, r))
+          return fail(COALESCE_ERR_INVALID_ARGUMENT, "dv[%d] or dg[%d] overlaps an input", l, l);
+      if (j != l && (overlap(rv, span(dv[j], dims[j], dims[j + 1], dims[j + 1], 4)) ||
+                     overlap(rg, span(dg[j], 1, dims[j + 1], dims[j + 1], 4))))
+        return fail(COALESCE_ERR_INVALID_ARGUMENT, "outputs of layers %d and %d overlap", l, j);
+    }
+    p.v[l] = v[l];
+    p.g[l] = g[l];
+    p.dW[l] = dW[l];
+    p.dv[l] = dv[l];
+    p.dg[l] = dg[l];
+  }
+  hipError_t e = launch_weight_norm_backward(p, (hipStream_t)stream);
+  if (e != hipSuccess) return device_fail(e, "weight_norm_backward launch");
   return ok();
 }
 

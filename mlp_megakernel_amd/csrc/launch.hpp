@@ -57,6 +57,21 @@ size_t mlp_backward_workspace(int D, int L, int num_cus);
 // hold mlp_backward_workspace(D, L, num_cus) bytes.
 hipError_t launch_mlp_backward(MlpBwdParams p, int D, int L, int hidden_act, int num_cus, hipStream_t stream);
 
+constexpr int kMaxWnLayers = 16;
+struct WnParams {
+  const void* v[kMaxWnLayers];  // fp16 din x dout, dense
+  const void* g[kMaxWnLayers];  // fp16 dout
+  void* W[kMaxWnLayers];        // fp16 din x dout (forward output)
+  const float* dW[kMaxWnLayers];  // backward input
+  float* dv[kMaxWnLayers];        // backward outputs
+  float* dg[kMaxWnLayers];
+  int din[kMaxWnLayers], dout[kMaxWnLayers];
+  int L;
+};
+// Weight normalisation of p.L layers in one launch, and its backward.
+hipError_t launch_weight_norm(const WnParams& p, hipStream_t stream);
+hipError_t launch_weight_norm_backward(const WnParams& p, hipStream_t stream);
+
 hipError_t launch_bias_add(const void* X, int64_t ldx, const void* bias, void* Y, int64_t ldy, int M, int N,
                            DType xt, DType bt, DType yt, hipStream_t stream, int num_cus);
 hipError_t launch_activation(const void* X, int64_t ldx, void* Y, int64_t ldy, int M, int N, DType dt, int act,

@@ -171,3 +171,40 @@ def test_mlp_backward_workspace_size_of_unsupported_chain_is_zero():
         d = (ctypes.c_int64 * len(dims))(*dims)
         assert lib.coalesce_mlp_backward_workspace_size(ctypes.cast(d, ctypes.c_void_p), len(dims) - 1) == 0
     assert lib.coalesce_mlp_backward_workspace_size(None, 3) == 0
+
+
+def wn(L=3, dims=None, back=False, **kw):
+    lib = mk.load_library()
+    dims = dims if dims is not None else [128] * (L + 1)
+    arr = lambda xs: None if xs is None else ctypes.cast((ctypes.c_void_p * len(xs))(*xs), ctypes.c_void_p)
+    v = kw.pop("v", [P * (16 + 4 * l) for l in range(L)])
+    g = kw.pop("g", [P * (64 + l) for l in range(L)])
+    d = (ctypes.c_int64 * len(dims))(*dims)
+    dt = kw.pop("dt", mk.F16)
+    if not back:
+        W = kw.pop("W", [P * (128 + 4 * l) for l in range(L)])
+        return lib.coalesce_weight_norm(arr(v), arr(g), arr(W), ctypes.cast(d, ctypes.c_void_p), L, dt, None)
+    dW = kw.pop("dW", [P * (256 + 4 * l) for l in range(L)])
+    dv = kw.pop("dv", [P * (512 + 4 * l) for l in range(L)])
+    dg = kw.pop("dg", [P * (768 + l) for l in range(L)])
+    return lib.coalesce_weight_norm_backward(arr(v), arr(g), arr(dW), arr(dv), arr(dg), ctypes.cast(d, ctypes.c_void_p),
+                                             L, dt, None)
+
+
+@pytest.mark.parametrize("back", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(L=0), INV), (dict(L=17, dims=[8] * 18), UNS), (dict(dims=[128, 0, 128, 128]), INV), (dict(dt=mk.F32), UNS),
+    (dict(dt=9), INV), (dict(v=None), INV), (dict(g=[P * 64, None, P * 66]), INV), (dict(v=[P * 16 + 1, P * 20, P * 24]), UNS),
+])
+def test_weight_norm_rejects_before_launch(back, kw, status):
+    assert wn(back=back, **kw) == status
+    assert len(mk.load_library().coalesce_last_error()) > 0
+
+
+def test_weight_norm_output_checks():
+    assert wn(W=None) == INV
+    assert wn(W=[P * 128, P * 16, P * 136]) == INV        # W[1] overlaps v[0]
+    assert wn(W=[P * 128 + 1, P * 132, P * 136]) == UNS   # odd address
+    assert wn(back=True, dg=[P * 768, P * 768, P * 770]) == INV  # dg[0] and dg[1] coincide
+    assert wn(back=True, dv=[P * 256, P * 516, P * 520]) == INV  # dv[0] overlaps dW[0]
+    assert wn(back=True, dW=[P * 256 + 2, P * 260, P * 264]) == UNS
