@@ -22,6 +22,10 @@ TFLOP/s.  The same line carries
     forward (which also stores the fp32 hidden activations) and the fused
     backward (weight gradients of every layer and dx) -- each timed the same
     way, with its HBM roofline, and rows/s of one forward + backward step;
+  * weight_norm: the fused weight normalisation of both MLPs' weights (all
+    layers in one launch) and its backward, against per-layer eager torch
+    ops, and the weight-normalised training step (normalise, training
+    forward, backward, normalisation backward);
   * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
     sample of the primary workload.
 All inputs are synthetic and seeded (datagen).
@@ -56,6 +60,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mlp", action="store_true")
     ap.add_argument("--no-train", action="store_true", help="skip the MLP training pair")
+    ap.add_argument("--no-wn", action="store_true", help="skip the weight-normalisation section")
     ap.add_argument("--prewarm-ms", type=float, default=500.0,
                     help="untimed back-to-back running before the warmup steps of each timed case")
     ap.add_argument("--harness-iters", type=int, default=100)
@@ -330,6 +335,58 @@ def main():
             del fwd, bwd, step
             torch.cuda.empty_cache()
         result["mlp_train"] = train_res
+
+    # ------------------------------------------------ weight normalisation
+    if not args.no_wn:
+        wn_res = {}
+        for w in (datagen.MLP3, datagen.MLP5):
+            print("bench: weight normalisation %s" % w.name, file=sys.stderr, flush=True)
+            vs, gs = datagen.wn_inputs(w)
+            vs = [t.to(dev).contiguous() for t in vs]
+            gs = [t.to(dev).contiguous() for t in gs]
+            Ws = [torch.empty_like(v) for v in vs]
+            dWs = [torch.randn(v.shape, device=dev, dtype=torch.float32) for v in vs]
+
+            def fused_wn():
+                mk.weight_norm(vs, gs, Ws)
+
+            def fused_wn_bwd():
+                mk.weight_norm_backward(vs, gs, dWs)
+
+            def eager_wn():  # per layer: norm, divide, multiply, cast (several launches each)
+                for v, g, W in zip(vs, gs, Ws):
+                    W.copy_((g.float() * v.float() / v.float().norm(dim=0)).to(v.dtype))
+
+            by = sum(4.0 * v.numel() + 2.0 * g.numel() for v, g in zip(vs, gs))
+            f_ms, f_ev = timed_steps(fused_wn, max(50, args.steps), 10)
+            b_ms, _ = timed_steps(fused_wn_bwd, max(50, args.steps), 10)
+            e_ms, _ = timed_steps(eager_wn, max(50, args.steps), 10)
+            # the weight-normalised training step of the page's quick start
+            x = datagen.mlp_inputs(w)[0].to(dev)
+            g_out = datagen.mlp_grad_output(w).to(dev)
+            acts = [torch.empty((w.M, d), dtype=torch.float32, device=dev) for d in w.dims[1:-1]]
+            out = torch.empty((w.M, w.dims[-1]), dtype=torch.float16, device=dev)
+            dW = [torch.empty(v.shape, dtype=torch.float32, device=dev) for v in vs]
+            dx = torch.empty_like(x)
+            wsp = torch.empty(mk.mlp_backward_workspace_size(w.dims), dtype=torch.uint8, device=dev)
+
+            def wn_step():
+                mk.weight_norm(vs, gs, Ws)
+                mk.mlp_forward_train(x, Ws, out=out, acts=acts)
+                mk.mlp_backward(x, Ws, acts, g_out, dW=dW, dx=dx, workspace=wsp)
+                mk.weight_norm_backward(vs, gs, dW)
+
+            s_ms, _ = timed_steps(wn_step, max(20, args.steps), 10)
+            wn_res[w.name] = {"layers": w.L, "fused_us": round(f_ms * 1e3, 2), "fused_launches": 1,
+                              "eager_us": round(e_ms * 1e3, 2), "eager_launches": "several per layer",
+                              "fused_speedup": round(e_ms / f_ms, 2), "backward_fused_us": round(b_ms * 1e3, 2),
+                              "bytes_per_call": by, "achieved_GBps": round(by / (f_ev * 1e-3) / 1e9, 1),
+                              "bound": "launch latency (the matrices are a few KB)",
+                              "training_step_ms": round(s_ms, 5),
+                              "training_step_rows_per_s": round(w.M / (s_ms * 1e-3), 1)}
+            del x, g_out, acts, out, dW, dx, wsp
+            torch.cuda.empty_cache()
+        result["weight_norm"] = wn_res
 
     # ------------------------------------------- the other GEMM workloads (harness)
     if not args.no_harness:

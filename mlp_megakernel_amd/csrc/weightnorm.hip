@@ -8,19 +8,21 @@
 //   dv_l[k][n] = g_l[n] / ||v_l[:, n]|| (dW_l[k][n] - v_l[k][n] <dW_l[:, n], v_l[:, n]> / ||v_l[:, n]||^2)
 //
 // The matrices are a few to a few hundred KB, so what costs is the launch,
-// not the bytes.  Grid (column blocks, layers): workgroup (c, l) owns the 64
-// output units 64 c .. 64 c + 63 of layer l; its 256 threads are 64 columns
-// x 4 row slices, so each wave reads one 128-byte run (64 fp16) per row.  The
-// slices' partial sums (fp32, each element's square exact in fp32) meet in
-// LDS and are added in slice order: repeated calls give the same bits.  A
-// column of zeros gives 0 x g / 0 = NaN, as the formula does.
+// not the bytes: the kernel is one memory round trip deep.  Grid (column
+// blocks, layers): workgroup (c, l) owns the 64 output units 64 c .. 64 c + 63
+// of layer l; its 1024 threads are 64 columns x 16 row slices (a thread reads
+// d_in / 16 rows, loads issued back to back), so each wave reads one 128-byte
+// run (64 fp16) per row.  The slices' partial sums (fp32, each element's
+// square exact in fp32) meet in LDS and are added in slice order: repeated
+// calls give the same bits.  A column of zeros gives 0 x g / 0 = NaN, as the
+// formula does.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace coalesce {
 namespace {
 
-constexpr int WN_COLS = 64, WN_SLICES = 4;
+constexpr int WN_COLS = 64, WN_SLICES = 16;
 
 __device__ __forceinline__ float ld16(const _Float16* p, size_t i) { return (float)p[i]; }
 
@@ -33,6 +35,7 @@ __global__ __launch_bounds__(WN_COLS* WN_SLICES) void weight_norm_kernel(WnParam
   const _Float16* v = (const _Float16*)p.v[l];
   float ss = 0.0f;
   if (n < dout)
+#pragma unroll 4
     for (int k = sl; k < din; k += WN_SLICES) {
       const float x = ld16(v, (size_t)k * dout + n);
       ss = __builtin_fmaf(x, x, ss);
@@ -40,7 +43,9 @@ __global__ __launch_bounds__(WN_COLS* WN_SLICES) void weight_norm_kernel(WnParam
   part[sl][c] = ss;
   __syncthreads();
   if (n >= dout) return;
-  const float tot = ((part[0][c] + part[1][c]) + part[2][c]) + part[3][c];
+  float tot = part[0][c];
+#pragma unroll
+  for (int i = 1; i < WN_SLICES; ++i) tot += part[i][c];
   const float scale = ld16((const _Float16*)p.g[l], n) / __builtin_sqrtf(tot);
   _Float16* W = (_Float16*)p.W[l];
   for (int k = sl; k < din; k += WN_SLICES) W[(size_t)k * dout + n] = (_Float16)(ld16(v, (size_t)k * dout + n) * scale);
@@ -56,6 +61,7 @@ __global__ __launch_bounds__(WN_COLS* WN_SLICES) void weight_norm_backward_kerne
   const float* dW = p.dW[l];
   float ss = 0.0f, dot = 0.0f;
   if (n < dout)
+#pragma unroll 4
     for (int k = sl; k < din; k += WN_SLICES) {
       const size_t i = (size_t)k * dout + n;
       const float x = ld16(v, i);
@@ -66,8 +72,12 @@ __global__ __launch_bounds__(WN_COLS* WN_SLICES) void weight_norm_backward_kerne
   pdot[sl][c] = dot;
   __syncthreads();
   if (n >= dout) return;
-  const float tss = ((pss[0][c] + pss[1][c]) + pss[2][c]) + pss[3][c];
-  const float tdot = ((pdot[0][c] + pdot[1][c]) + pdot[2][c]) + pdot[3][c];
+  float tss = pss[0][c], tdot = pdot[0][c];
+#pragma unroll
+  for (int i = 1; i < WN_SLICES; ++i) {
+    tss += pss[i][c];
+    tdot += pdot[i][c];
+  }
   const float nrm = __builtin_sqrtf(tss);
   if (sl == 0) p.dg[l][n] = tdot / nrm;
   const float a = ld16((const _Float16*)p.g[l], n) / nrm;
