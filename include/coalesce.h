@@ -93,8 +93,14 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
  *         dense row-major (the x @ W orientation)
  *   dims  HOST array of L + 1 widths
  *   out   device, M x dims[L] fp16, leading dimension ldo >= dims[L] (written)
- * Supported: dtype F16; hidden_act SOFTPLUS, RELU or NONE (a linear chain); all
- * widths equal to 64 (L = 1..8) or to 128 (L = 1..4).  M == 0 is a no-op.
+ * Supported: dtype F16; hidden_act SOFTPLUS, RELU or NONE (a linear chain);
+ * widths multiples of 8 and at most 128, in any mix (the quick start's D, H,
+ * out_features), L = 1..8 when every width is at most 64, L = 1..4 otherwise.
+ * Chains whose widths are not all 64 or all 128 run at kernel width 64 or 128
+ * with the weights zero-padded in LDS and x loads / out stores limited to the
+ * true columns: the padded units add exact zeros, so the result is the one
+ * the narrower chain gives.  x is M x dims[0], out M x dims[L], W[l] dense
+ * dims[l] x dims[l+1].  M == 0 is a no-op.
  */
 coalesce_status coalesce_mlp_forward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims, int32_t L,
                                      void* out, int64_t ldo, int64_t M, coalesce_dtype dtype, coalesce_act hidden_act,
@@ -120,9 +126,9 @@ coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void
  * in fp32: the activation as computed on the fp32 accumulators, before its
  * rounding to the next layer's fp16 operand.
  *   acts  HOST array of L - 1 device pointers, each M x dims[l+1] fp32 with
- *         leading dimension lda (D <= lda <= 2^24, 16-byte aligned rows),
- *         not overlapping x, out, the weights or each other; may be NULL
- *         when L == 1.
+ *         leading dimension lda (dims[l+1] <= lda <= 2^24, 16-byte aligned
+ *         rows), not overlapping x, out, the weights or each other; may be
+ *         NULL when L == 1.
  * Other arguments, support and errors as coalesce_mlp_forward.
  */
 coalesce_status coalesce_mlp_forward_train(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
@@ -164,8 +170,9 @@ size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L);
  * on `stream`: the fused backward (one persistent workgroup per compute
  * unit; each sums its rows' weight-gradient terms in registers) and a
  * reduction that adds the per-workgroup sums in a fixed order, so repeated
- * calls give identical bits.  M == 0 gives dW = 0.  Supported chains as
- * coalesce_mlp_forward.  Outputs must not overlap the inputs, each other or
+ * calls give identical bits.  M == 0 gives dW = 0.  Supported chains: every
+ * width equal to 64 (L = 1..8) or to 128 (L = 1..4).  Outputs must not
+ * overlap the inputs, each other or
  * the workspace.  Calls that share a workspace must be ordered on one
  * stream.
  */

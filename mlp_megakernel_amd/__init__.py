@@ -205,7 +205,7 @@ def mlp_forward_train(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_a
     if (Mo, Do) != (M, dims[-1]):
         raise ValueError("out must be M x dims[L]")
     if acts is None:
-        pitch = max(4, (dims[0] + 3) // 4 * 4)
+        pitch = max(4, (max(dims[1:-1], default=4) + 3) // 4 * 4)
         acts = [torch.empty((M, pitch), dtype=torch.float32, device=x.device)[:, :dims[l]] for l in range(1, L)]
     if len(acts) != L - 1:
         raise ValueError("need L - 1 activation buffers")

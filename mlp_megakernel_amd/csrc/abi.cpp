@@ -155,32 +155,42 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
 
 namespace {
 
-// Shared checks of the MLP entry points: the chain's widths (all equal to 64
-// or 128), depth, dtype, activation and weights.  Fills D and p_W.
+// Shared checks of the MLP entry points: the chain's widths, depth, dtype,
+// activation and weights.  Widths are multiples of 8 and at most 128; the
+// chain runs at kernel width P = 64 if every width is at most 64, else 128
+// (then *square says whether every width equals P).  Depth: P = 128 holds at
+// most 4 layers of weights in LDS, P = 64 at most 8.
 coalesce_status check_mlp_chain(const void* const* W, const int64_t* dims, int32_t L, int64_t M,
-                                coalesce_dtype dtype, coalesce_act hidden_act, int64_t* D_out) {
+                                coalesce_dtype dtype, coalesce_act hidden_act, int64_t* P_out, bool* square) {
   if (L < 1) return fail(COALESCE_ERR_INVALID_ARGUMENT, "L must be at least 1 (got %d)", (int)L);
   if (!W || !dims) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W or dims is NULL");
   if (M < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative M");
   if (!valid_dtype(dtype)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown dtype");
   if (!valid_act(hidden_act)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown activation");
-  for (int l = 0; l <= L && l <= 8; ++l)
+  if (L > 8) return fail(COALESCE_ERR_UNSUPPORTED, "at most 8 layers (got %d)", (int)L);
+  int64_t mx = 0;
+  for (int l = 0; l <= L; ++l) {
     if (dims[l] <= 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dims[%d] = %lld is not positive", l, (long long)dims[l]);
+    if (dims[l] % 8 || dims[l] > 128)
+      return fail(COALESCE_ERR_UNSUPPORTED, "MLP width %lld not supported (a multiple of 8, at most 128)",
+                  (long long)dims[l]);
+    if (dims[l] > mx) mx = dims[l];
+  }
   if (dtype != COALESCE_F16) return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel takes fp16 only");
   if (hidden_act == COALESCE_ACT_GELU_ERF)
     return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel supports softplus, relu or no hidden activation");
-  const int64_t D = dims[0];
-  if (D != 64 && D != 128) return fail(COALESCE_ERR_UNSUPPORTED, "MLP width %lld not supported (64 or 128)", (long long)D);
-  if ((D == 128 && L > 4) || (D == 64 && L > 8))
-    return fail(COALESCE_ERR_UNSUPPORTED, "%d layers of width %lld do not fit in LDS", (int)L, (long long)D);
-  for (int l = 1; l <= L; ++l)
-    if (dims[l] != D) return fail(COALESCE_ERR_UNSUPPORTED, "all MLP widths must be equal");
+  const int64_t P = mx <= 64 ? 64 : 128;
+  if (P == 128 && L > 4)
+    return fail(COALESCE_ERR_UNSUPPORTED, "%d layers of width up to 128 do not fit in LDS (at most 4)", (int)L);
+  bool sq = true;
+  for (int l = 0; l <= L; ++l) sq = sq && dims[l] == P;
   if (M > kMaxExtent - 256) return fail(COALESCE_ERR_UNSUPPORTED, "M must be below 2^31 - 256");
   for (int l = 0; l < L; ++l) {
     if (!W[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W[%d] is NULL", l);
     if (!aligned16(W[l])) return fail(COALESCE_ERR_UNSUPPORTED, "W[%d] must be 16-byte aligned", l);
   }
-  *D_out = D;
+  *P_out = P;
+  *square = sq;
   return COALESCE_OK;
 }
 
@@ -200,34 +210,40 @@ coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* 
                                  void* out, int64_t ldo, float* const* acts, int64_t lda, int64_t M,
                                  coalesce_dtype dtype, coalesce_act hidden_act, int64_t num_workgroups, bool train,
                                  void* stream) {
-  int64_t D = 0;
-  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &D);
+  int64_t P = 0;
+  bool square = true;
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square);
   if (s != COALESCE_OK) return s;
   if (num_workgroups < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative workgroup count");
   if (num_workgroups > (int64_t)INT32_MAX) return fail(COALESCE_ERR_UNSUPPORTED, "workgroup count too large");
   if (M == 0) return ok();
+  const int64_t D = dims[0], O = dims[L];
   if ((s = check_rows(x, ldx, D, 2, "x")) != COALESCE_OK) return s;
-  if ((s = check_rows(out, ldo, D, 2, "out")) != COALESCE_OK) return s;
-  const Range ro = span(out, M, D, ldo, 2);
+  if ((s = check_rows(out, ldo, O, 2, "out")) != COALESCE_OK) return s;
+  const Range ro = span(out, M, O, ldo, 2);
   if (overlap(ro, span(x, M, D, ldx, 2))) return fail(COALESCE_ERR_INVALID_ARGUMENT, "out overlaps x");
   MlpParams p{};
   for (int l = 0; l < L; ++l) {
-    if (overlap(ro, span(W[l], D, D, D, 2))) return fail(COALESCE_ERR_INVALID_ARGUMENT, "out overlaps W[%d]", l);
+    if (overlap(ro, span(W[l], dims[l], dims[l + 1], dims[l + 1], 2)))
+      return fail(COALESCE_ERR_INVALID_ARGUMENT, "out overlaps W[%d]", l);
     p.W[l] = W[l];
   }
+  for (int l = 0; l <= L; ++l) p.dims[l] = (int)dims[l];
   if (train && L > 1) {
     if (!acts) return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts is NULL");
     for (int l = 0; l + 1 < L; ++l) {
       char name[16];
       snprintf(name, sizeof(name), "acts[%d]", l);
-      if ((s = check_rows(acts[l], lda, D, 4, name)) != COALESCE_OK) return s;
-      const Range ra = span(acts[l], M, D, lda, 4);
+      const int64_t H = dims[l + 1];
+      if ((s = check_rows(acts[l], lda, H, 4, name)) != COALESCE_OK) return s;
+      const Range ra = span(acts[l], M, H, lda, 4);
       if (overlap(ra, span(x, M, D, ldx, 2)) || overlap(ra, ro))
         return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts[%d] overlaps x or out", l);
       for (int j = 0; j < L; ++j)
-        if (overlap(ra, span(W[j], D, D, D, 2))) return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts[%d] overlaps W[%d]", l, j);
+        if (overlap(ra, span(W[j], dims[j], dims[j + 1], dims[j + 1], 2)))
+          return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts[%d] overlaps W[%d]", l, j);
       for (int j = 0; j < l; ++j)
-        if (overlap(ra, span(acts[j], M, D, lda, 4)))
+        if (overlap(ra, span(acts[j], M, dims[j + 1], lda, 4)))
           return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts[%d] overlaps acts[%d]", l, j);
       p.acts[l] = acts[l];
     }
@@ -241,8 +257,8 @@ coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* 
   p.ldo = ldo;
   p.lda = train ? lda : 0;
   p.M = (int)M;
-  hipError_t e = launch_mlp(p, (int)D, (int)L, act_code(hidden_act), train && L > 1, (int)num_workgroups, cus,
-                            (hipStream_t)stream);
+  hipError_t e = launch_mlp(p, (int)P, (int)L, act_code(hidden_act), train && L > 1, !square, (int)num_workgroups,
+                            cus, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "MLP launch");
   return ok();
 }
@@ -282,8 +298,10 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
                                       coalesce_dtype dtype, coalesce_act hidden_act, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   int64_t D = 0;
-  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &D);
+  bool square = true;
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &D, &square);
   if (s != COALESCE_OK) return s;
+  if (!square) return fail(COALESCE_ERR_UNSUPPORTED, "the backward takes chains whose widths all equal 64 or 128");
   if (!dW) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW is NULL");
   MlpBwdParams p{};
   for (int l = 0; l < L; ++l) {

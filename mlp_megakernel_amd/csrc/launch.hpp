@@ -27,15 +27,20 @@ struct MlpParams {
   const void* x;
   void* out;
   const void* W[8];
-  float* acts[8];  // training forward: acts[l] receives h_{l+1} (fp32, M x D, pitch lda), l = 0..L-2
+  float* acts[8];  // training forward: acts[l] receives h_{l+1} (fp32, M x dims[l+1], pitch lda), l = 0..L-2
+  int dims[9];     // the chain's true widths (each a multiple of 8, at most the kernel width)
   int64_t ldx, ldo, lda;
   int M;
   int num_tiles;  // row tiles (set by the launcher)
 };
-// Widths all equal to D (64 or 128), L layers (1..8 for 64, 1..4 for 128).
-// num_workgroups <= 0: min(#CUs x occupancy, workgroups with work).
-// store_acts: also write the hidden activations to p.acts (training forward).
-hipError_t launch_mlp(const MlpParams& p, int D, int L, int hidden_act, bool store_acts, int num_workgroups,
+// The chain runs at kernel width D (64 or 128), L layers (1..8 for 64, 1..4
+// for 128).  pad = false: every width equals D; pad = true: p.dims holds the
+// true widths (multiples of 8, at most D) and the kernel runs the chain with
+// the weights zero-padded to D x D in LDS, x loads and out / activation stores
+// masked to the true columns.  num_workgroups <= 0: min(#CUs x occupancy,
+// workgroups with work).  store_acts: also write the hidden activations to
+// p.acts (training forward).
+hipError_t launch_mlp(const MlpParams& p, int D, int L, int hidden_act, bool store_acts, bool pad, int num_workgroups,
                       int num_cus, hipStream_t stream);
 
 struct MlpBwdParams {

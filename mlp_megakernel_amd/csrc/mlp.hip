@@ -111,7 +111,9 @@ __device__ __forceinline__ int w_offset(int l, int n, int slot) {
 // 16-byte chunk cb of the 8 W^T rows n = 8 nb .. 8 nb + 7: it loads the 8
 // rows of W_l (16 bytes each) whose units land in that chunk, transposes the
 // 8 x 8 block in registers and writes 8 chunks of 16 bytes.
-template <int D, int L>
+// With PAD the layer is the true dims[l] x dims[l+1] matrix (pitch dims[l+1])
+// and every unit outside it is staged as zero.
+template <int D, int L, bool PAD>
 __device__ __forceinline__ void stage_weights(const MlpParams& p, _Float16* sW) {
   constexpr int NB = D / 8;  // 8-row blocks (and 16-byte chunks) per layer
   for (int idx = threadIdx.x; idx < L * NB * NB; idx += Geo<D>::THREADS) {
@@ -120,12 +122,16 @@ __device__ __forceinline__ void stage_weights(const MlpParams& p, _Float16* sW) 
     const int nb = rem / NB;
     const int cb = rem - nb * NB;
     const _Float16* Wl = (const _Float16*)p.W[l];
+    const int K = PAD ? p.dims[l] : D, N = PAD ? p.dims[l + 1] : D;
     f16x8 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int slot = 8 * cb + j;
       const int k = l == 0 ? slot : layer_slot_k(slot);
-      v[j] = *(const f16x8*)(Wl + (int64_t)k * D + 8 * nb);
+      if (PAD && (k >= K || 8 * nb >= N))
+        v[j] = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+      else
+        v[j] = *(const f16x8*)(Wl + (int64_t)k * N + 8 * nb);
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -190,15 +196,26 @@ __device__ __forceinline__ void store_act(__amdgpu_buffer_rsrc_t rs, uint32_t of
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, (f32x4){a0, a1, a2, a3}), rs, off, 0, 0);
 }
 
-template <int D>
+// Narrower chains (PAD): a lane's access to columns at or beyond the true
+// width goes to a buffer offset past every resource's size (the host bounds
+// 16 rows of any operand below 2^31 bytes), so the load reads zero and the
+// store is dropped.
+constexpr uint32_t OFF_NONE = 0x80000000u;
+__device__ __forceinline__ uint32_t masked(bool ok, uint32_t off) { return ok ? off : OFF_NONE; }
+__device__ __forceinline__ int lane_group() { return (int)(threadIdx.x & 63) >> 4; }
+
+template <int D, bool PAD>
 __device__ __forceinline__ void load_x(const MlpParams& p, const Lane<D>& c, int tile, HTile<D>& h) {
   const uint32_t xoff = opaque(c.xoff);  // keeps the k-step offsets in the instructions' immediate field
 #pragma unroll
   for (int s = 0; s < Geo<D>::MT; ++s) {
     const __amdgpu_buffer_rsrc_t rs = sub_rsrc<D>(p.x, p.M, tile, s, p.ldx);
 #pragma unroll
-    for (int ks = 0; ks < Geo<D>::KS; ++ks)
-      h.v[s][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, xoff + 64u * ks, 0, 0);
+    for (int ks = 0; ks < Geo<D>::KS; ++ks) {
+      // units 32 ks + 8 g .. + 7 of the row
+      const uint32_t off = PAD ? masked(32 * ks + 8 * lane_group() < p.dims[0], xoff + 64u * ks) : xoff + 64u * ks;
+      h.v[s][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+    }
   }
 }
 
@@ -252,7 +269,7 @@ __device__ __forceinline__ void interleave() {
 // Hidden layer l for one row tile: hout = act(hin W_l), in the step pipeline
 // described at the top, with the unguarded softplus; the largest output is
 // folded into mx.
-template <int D, int l, int ACT, bool ST>
+template <int D, int l, int ACT, bool ST, bool PAD>
 __device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& c, const HTile<D>& hin,
                                              HTile<D>& hout, u16x2& mx, int tile) {
   using G = Geo<D>;
@@ -308,7 +325,10 @@ __device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& 
         hout.v[s][u >> 1][(u & 1) * 2 + 1] = pack_f16(v[2], v[3]);
         if constexpr (ST) {
           const float sc = SP ? 0.693147180559945309f : 1.0f;
-          store_act(ra[s], aoff + 64u * (uint32_t)u, v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
+          // units 16 u + 4 g .. + 3
+          const uint32_t off = PAD ? masked(16 * u + 4 * lane_group() < p.dims[l + 1], aoff + 64u * (uint32_t)u)
+                                   : aoff + 64u * (uint32_t)u;
+          store_act(ra[s], off, v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc);
         }
       }
     }
@@ -339,7 +359,7 @@ __device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& 
 // Last layer l = L - 1 for one row tile: out = hin W_L (times ln 2 when hin
 // is in base-2 units), fp16, stored through a buffer resource that drops the
 // rows beyond M.
-template <int D, int l, int ACT>
+template <int D, int l, int ACT, bool PAD>
 __device__ __forceinline__ void last_layer(const MlpParams& p, const Lane<D>& c, const HTile<D>& hin,
                                            int tile) {
   using G = Geo<D>;
@@ -379,7 +399,11 @@ __device__ __forceinline__ void last_layer(const MlpParams& p, const Lane<D>& c,
         if (u % 2 == 0)
           ev[s] = o;
         else
-          store_pair(rs[s], ooff + 32u * (uint32_t)(u - 1), ev[s], o);
+          store_pair(rs[s],
+                     PAD ? masked(16 * (u - 1) + 16 * (lane_group() & 1) + 8 * (lane_group() >> 1) < p.dims[l + 1],
+                                  ooff + 32u * (uint32_t)(u - 1))
+                         : ooff + 32u * (uint32_t)(u - 1),
+                     ev[s], o);
       }
     }
     if (MLP_INTERLEAVE && t > 0 && t < G::NT) interleave<G::KS * G::MT, VPM, true, G::MT, true, ST_EVERY>();
@@ -394,7 +418,7 @@ __device__ __forceinline__ void last_layer(const MlpParams& p, const Lane<D>& c,
 // Per element it executes the same MFMA accumulation order and the same
 // exp2/add/log2/pack instructions as the pipelined path, so it reproduces
 // that path's bits wherever the guard does not apply.
-template <int D, int L, int ACT, bool ST>
+template <int D, int L, int ACT, bool ST, bool PAD>
 __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& c, int tile) {
   using G = Geo<D>;
   constexpr bool SP = ACT == ACT_SOFTPLUS;
@@ -406,7 +430,9 @@ __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& 
     u32x4 h[G::KS], hn[G::KS];
     u32x2 ev;
 #pragma unroll
-    for (int ks = 0; ks < G::KS; ++ks) h[ks] = __builtin_amdgcn_raw_buffer_load_b128(rx, xoff + 64u * ks, 0, 0);
+    for (int ks = 0; ks < G::KS; ++ks)
+      h[ks] = __builtin_amdgcn_raw_buffer_load_b128(
+          rx, PAD ? masked(32 * ks + 8 * lane_group() < p.dims[0], xoff + 64u * ks) : xoff + 64u * ks, 0, 0);
 #pragma unroll 1
     for (int l = 0; l < L; ++l) {
       const bool in_b2 = SP && l > 0;
@@ -434,8 +460,10 @@ __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& 
           hn[t >> 1][(t & 1) * 2 + 1] = pack_f16(v[2], v[3]);
           if constexpr (ST) {
             const float sc = SP ? 0.693147180559945309f : 1.0f;
-            store_act(act_rsrc<D>(p.acts[l], p.M, tile, s, p.lda), opaque(c.aoff) + 64u * (uint32_t)t, v[0] * sc,
-                      v[1] * sc, v[2] * sc, v[3] * sc);
+            const uint32_t off = opaque(c.aoff) + 64u * (uint32_t)t;
+            store_act(act_rsrc<D>(p.acts[l], p.M, tile, s, p.lda),
+                      PAD ? masked(16 * t + 4 * lane_group() < p.dims[l + 1], off) : off, v[0] * sc, v[1] * sc,
+                      v[2] * sc, v[3] * sc);
           }
         } else {
           const float sc = in_b2 ? 0.693147180559945309f : 1.0f;
@@ -443,7 +471,11 @@ __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& 
           if (t % 2 == 0)
             ev = o;
           else
-            store_pair(ro, ooff + 32u * (uint32_t)(t - 1), ev, o);
+            store_pair(ro,
+                       PAD ? masked(16 * (t - 1) + 16 * (lane_group() & 1) + 8 * (lane_group() >> 1) < p.dims[L],
+                                    ooff + 32u * (uint32_t)(t - 1))
+                           : ooff + 32u * (uint32_t)(t - 1),
+                       ev, o);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -455,24 +487,24 @@ __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& 
 
 // One row tile, layers l .. L-1.  hin holds the layer-l input; hfree is free.
 // mx collects the largest unguarded softplus output.
-template <int D, int L, int l, int ACT, bool ST>
+template <int D, int L, int l, int ACT, bool ST, bool PAD>
 __device__ __forceinline__ void tile_chain(const MlpParams& p, const Lane<D>& c, int tile, HTile<D>& hin,
                                            HTile<D>& hfree, u16x2& mx) {
   if constexpr (l < L - 1) {
-    hidden_layer<D, l, ACT, ST>(p, c, hin, hfree, mx, tile);
-    tile_chain<D, L, l + 1, ACT, ST>(p, c, tile, hfree, hin, mx);
+    hidden_layer<D, l, ACT, ST, PAD>(p, c, hin, hfree, mx, tile);
+    tile_chain<D, L, l + 1, ACT, ST, PAD>(p, c, tile, hfree, hin, mx);
   } else {
-    last_layer<D, l, ACT>(p, c, hin, tile);
+    last_layer<D, l, ACT, PAD>(p, c, hin, tile);
   }
 }
 
 // Several waves per SIMD (MlpCfg::MINW) so that memory latency and the
 // dependent activation chains of some waves hide behind the work of others.
-template <int D, int L, int ACT, bool ST>
+template <int D, int L, int ACT, bool ST, bool PAD>
 __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(MlpParams p) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(16))) _Float16 sW[L * D * D];
-  stage_weights<D, L>(p, sW);
+  stage_weights<D, L, PAD>(p, sW);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
@@ -488,21 +520,21 @@ __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(M
   // load would make the compiler wait for every outstanding memory operation
   // where the paths join, stores included.
   HTile<D> ha, hb, hc;
-  if (tile < p.num_tiles) load_x<D>(p, c, tile, ha);
+  if (tile < p.num_tiles) load_x<D, PAD>(p, c, tile, ha);
   while (tile < p.num_tiles) {
     int next = tile + nwaves;
-    load_x<D>(p, c, next, hc);
-    tile_chain<D, L, 0, ACT, ST>(p, c, tile, ha, hb, mx);
+    load_x<D, PAD>(p, c, next, hc);
+    tile_chain<D, L, 0, ACT, ST, PAD>(p, c, tile, ha, hb, mx);
     tile = next;
     if (tile >= p.num_tiles) break;
     next = tile + nwaves;
-    load_x<D>(p, c, next, hb);
-    tile_chain<D, L, 0, ACT, ST>(p, c, tile, hc, ha, mx);
+    load_x<D, PAD>(p, c, next, hb);
+    tile_chain<D, L, 0, ACT, ST, PAD>(p, c, tile, hc, ha, mx);
     tile = next;
     if (tile >= p.num_tiles) break;
     next = tile + nwaves;
-    load_x<D>(p, c, next, ha);
-    tile_chain<D, L, 0, ACT, ST>(p, c, tile, hb, hc, mx);
+    load_x<D, PAD>(p, c, next, ha);
+    tile_chain<D, L, 0, ACT, ST, PAD>(p, c, tile, hb, hc, mx);
     tile = next;
   }
   if constexpr (ACT == ACT_SOFTPLUS && L > 1) {
@@ -513,7 +545,7 @@ __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(M
     // they are overwritten.
     if (__builtin_amdgcn_ballot_w64(max(mx[0], mx[1]) >= SP_FLAG_B2_F16) != 0) {
       wait_vmcnt0();
-      for (int t = wave; t < p.num_tiles; t += nwaves) tile_guarded<D, L, ACT, ST>(p, c, t);
+      for (int t = wave; t < p.num_tiles; t += nwaves) tile_guarded<D, L, ACT, ST, PAD>(p, c, t);
     }
   }
 }
@@ -521,14 +553,14 @@ __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(M
 // Persistent grid: min(#CUs x workgroups that fit on a CU, #workgroups with
 // work), unless the caller fixed the count.  The per-CU occupancy comes from
 // the runtime for the compiled kernel (its VGPR and LDS use) and is cached.
-template <int D, int L, int ACT, bool ST>
+template <int D, int L, int ACT, bool ST, bool PAD>
 hipError_t launch_dl(MlpParams p, int num_workgroups, int num_cus, hipStream_t stream) {
   using G = Geo<D>;
   p.num_tiles = (int)(((int64_t)p.M + G::TR - 1) / G::TR);
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mlp_kernel<D, L, ACT, ST>, G::THREADS, 0);
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mlp_kernel<D, L, ACT, ST, PAD>, G::THREADS, 0);
     if (e != hipSuccess) return e;
     per_cu = n > 0 ? n : 1;
   }
@@ -539,50 +571,54 @@ hipError_t launch_dl(MlpParams p, int num_workgroups, int num_cus, hipStream_t s
     nwg = need < cap ? need : (int)cap;
     if (nwg < 1) nwg = 1;
   }
-  hipLaunchKernelGGL((mlp_kernel<D, L, ACT, ST>), dim3(nwg), dim3(G::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((mlp_kernel<D, L, ACT, ST, PAD>), dim3(nwg), dim3(G::THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, int ACT, bool ST>
+template <int D, int ACT, bool ST, bool PAD>
 hipError_t launch_d(const MlpParams& p, int L, int nwg, int cus, hipStream_t stream) {
   if constexpr (D == 128) {
     switch (L) {
-      case 1: return launch_dl<D, 1, ACT, ST>(p, nwg, cus, stream);
-      case 2: return launch_dl<D, 2, ACT, ST>(p, nwg, cus, stream);
-      case 3: return launch_dl<D, 3, ACT, ST>(p, nwg, cus, stream);
-      case 4: return launch_dl<D, 4, ACT, ST>(p, nwg, cus, stream);
+      case 1: return launch_dl<D, 1, ACT, ST, PAD>(p, nwg, cus, stream);
+      case 2: return launch_dl<D, 2, ACT, ST, PAD>(p, nwg, cus, stream);
+      case 3: return launch_dl<D, 3, ACT, ST, PAD>(p, nwg, cus, stream);
+      case 4: return launch_dl<D, 4, ACT, ST, PAD>(p, nwg, cus, stream);
     }
   } else {
     switch (L) {
-      case 1: return launch_dl<D, 1, ACT, ST>(p, nwg, cus, stream);
-      case 2: return launch_dl<D, 2, ACT, ST>(p, nwg, cus, stream);
-      case 3: return launch_dl<D, 3, ACT, ST>(p, nwg, cus, stream);
-      case 4: return launch_dl<D, 4, ACT, ST>(p, nwg, cus, stream);
-      case 5: return launch_dl<D, 5, ACT, ST>(p, nwg, cus, stream);
-      case 6: return launch_dl<D, 6, ACT, ST>(p, nwg, cus, stream);
-      case 7: return launch_dl<D, 7, ACT, ST>(p, nwg, cus, stream);
-      case 8: return launch_dl<D, 8, ACT, ST>(p, nwg, cus, stream);
+      case 1: return launch_dl<D, 1, ACT, ST, PAD>(p, nwg, cus, stream);
+      case 2: return launch_dl<D, 2, ACT, ST, PAD>(p, nwg, cus, stream);
+      case 3: return launch_dl<D, 3, ACT, ST, PAD>(p, nwg, cus, stream);
+      case 4: return launch_dl<D, 4, ACT, ST, PAD>(p, nwg, cus, stream);
+      case 5: return launch_dl<D, 5, ACT, ST, PAD>(p, nwg, cus, stream);
+      case 6: return launch_dl<D, 6, ACT, ST, PAD>(p, nwg, cus, stream);
+      case 7: return launch_dl<D, 7, ACT, ST, PAD>(p, nwg, cus, stream);
+      case 8: return launch_dl<D, 8, ACT, ST, PAD>(p, nwg, cus, stream);
     }
   }
   return hipErrorInvalidValue;
 }
 
-template <int D, bool ST>
+template <int D, bool ST, bool PAD>
 hipError_t launch_da(const MlpParams& p, int L, int act, int nwg, int cus, hipStream_t stream) {
-  if (act == ACT_NONE) return launch_d<D, ACT_NONE, ST>(p, L, nwg, cus, stream);
-  if (act == ACT_RELU) return launch_d<D, ACT_RELU, ST>(p, L, nwg, cus, stream);
-  return launch_d<D, ACT_SOFTPLUS, ST>(p, L, nwg, cus, stream);
+  if (act == ACT_NONE) return launch_d<D, ACT_NONE, ST, PAD>(p, L, nwg, cus, stream);
+  if (act == ACT_RELU) return launch_d<D, ACT_RELU, ST, PAD>(p, L, nwg, cus, stream);
+  return launch_d<D, ACT_SOFTPLUS, ST, PAD>(p, L, nwg, cus, stream);
+}
+
+template <int D>
+hipError_t launch_dp(const MlpParams& p, int L, int act, bool st, bool pad, int nwg, int cus, hipStream_t stream) {
+  if (pad)
+    return st ? launch_da<D, true, true>(p, L, act, nwg, cus, stream) : launch_da<D, false, true>(p, L, act, nwg, cus, stream);
+  return st ? launch_da<D, true, false>(p, L, act, nwg, cus, stream) : launch_da<D, false, false>(p, L, act, nwg, cus, stream);
 }
 
 }  // namespace
 
-hipError_t launch_mlp(const MlpParams& p, int D, int L, int act, bool store_acts, int num_workgroups, int num_cus,
-                      hipStream_t stream) {
-  if (D == 128)
-    return store_acts ? launch_da<128, true>(p, L, act, num_workgroups, num_cus, stream)
-                      : launch_da<128, false>(p, L, act, num_workgroups, num_cus, stream);
-  return store_acts ? launch_da<64, true>(p, L, act, num_workgroups, num_cus, stream)
-                    : launch_da<64, false>(p, L, act, num_workgroups, num_cus, stream);
+hipError_t launch_mlp(const MlpParams& p, int D, int L, int act, bool store_acts, bool pad, int num_workgroups,
+                      int num_cus, hipStream_t stream) {
+  if (D == 128) return launch_dp<128>(p, L, act, store_acts, pad, num_workgroups, num_cus, stream);
+  return launch_dp<64>(p, L, act, store_acts, pad, num_workgroups, num_cus, stream);
 }
 
 }  // namespace coalesce

@@ -84,8 +84,8 @@ def mlp(D=128, L=3, dims=None, **kw):
     (dict(L=0), INV), (dict(M=-1), INV), (dict(g=-1), INV), (dict(dt=5), INV), (dict(act=4), INV),
     (dict(x=None), INV), (dict(out=None), INV), (dict(ldx=100), INV), (dict(ldo=127), INV),
     (dict(dt=mk.BF16), UNS), (dict(act=mk.ACT_GELU_ERF), UNS),
-    (dict(D=96), UNS), (dict(D=128, L=5), UNS), (dict(D=64, L=9), UNS),
-    (dict(dims=[128, 64, 128, 128]), UNS),
+    (dict(D=100), UNS), (dict(D=136), UNS), (dict(D=128, L=5), UNS), (dict(D=64, L=9), UNS),
+    (dict(dims=[128, 60, 128, 128]), UNS), (dict(L=5, dims=[64, 128, 64, 64, 64, 64]), UNS),
     (dict(x=P + 2), UNS), (dict(ldx=132), UNS),
 ])
 def test_mlp_rejects_before_launch(kw, status):
@@ -158,6 +158,7 @@ def mlp_bwd(D=128, L=3, **kw):
     (dict(x=None), INV), (dict(dout=None), INV), (dict(acts=None), INV), (dict(ldd=100), INV), (dict(ldq=64), INV),
     (dict(dout=P * 128 + 8), UNS), (dict(lda=129), UNS), (dict(dx=P + 64), INV),  # dx overlaps x
     (dict(act=mk.ACT_GELU_ERF), UNS), (dict(dt=mk.F32), UNS), (dict(D=64, L=9), UNS), (dict(D=32), UNS),
+    (dict(D=100), UNS),
     (dict(L=0), INV), (dict(M=-5), INV), (dict(act=11), INV),
 ])
 def test_mlp_backward_rejects_before_launch(kw, status):
