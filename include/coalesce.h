@@ -156,23 +156,25 @@ size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L);
  * logistic sigmoid of z_l; absolute error at most 2^-23), relu -> 1 where
  * h_l > 0 else 0, none -> 1.  h_l and dz_l are rounded to fp16 (nearest
  * even) as MFMA operands; products accumulate in fp32.
- *   x         device, M x D fp16 (ldx)          the forward's input
+ *   x         device, M x dims[0] fp16 (ldx)    the forward's input
  *   W, dims   as coalesce_mlp_forward
- *   acts      HOST array of L - 1 device pointers, M x D fp32 (lda), as
- *             written by coalesce_mlp_forward_train; may be NULL when L == 1
- *   dout      device, M x D fp16 (ldd)          dLoss/d(out)
- *   dW        HOST array of L device pointers, each D x D fp32, dense
- *             row-major (the x @ W orientation of W[l]), overwritten
- *   dx        device, M x D fp16 (ldq), written; or NULL to skip it
+ *   acts      HOST array of L - 1 device pointers, M x dims[l+1] fp32 (lda),
+ *             as written by coalesce_mlp_forward_train; may be NULL when L == 1
+ *   dout      device, M x dims[L] fp16 (ldd)    dLoss/d(out)
+ *   dW        HOST array of L device pointers, each dims[l] x dims[l+1] fp32,
+ *             dense row-major (the x @ W orientation of W[l]), overwritten
+ *   dx        device, M x dims[0] fp16 (ldq), written; or NULL to skip it
  *   workspace device, at least coalesce_mlp_backward_workspace_size(dims, L)
  *             bytes, 16-byte aligned; its contents on entry are ignored
- * Pitches obey D <= ld <= 2^24 with 16-byte aligned rows.  Two kernels run
+ * Pitches are at least the operand's width and at most 2^24, with 16-byte
+ * aligned rows.  Two kernels run
  * on `stream`: the fused backward (one persistent workgroup per compute
  * unit; each sums its rows' weight-gradient terms in registers) and a
  * reduction that adds the per-workgroup sums in a fixed order, so repeated
- * calls give identical bits.  M == 0 gives dW = 0.  Supported chains: every
- * width equal to 64 (L = 1..8) or to 128 (L = 1..4).  Outputs must not
- * overlap the inputs, each other or
+ * calls give identical bits.  M == 0 gives dW = 0.  Supported chains as
+ * coalesce_mlp_forward (non-square ones run padded and write only the true
+ * dims[l] x dims[l+1] of each dW and the true columns of dx).  Outputs must
+ * not overlap the inputs, each other or
  * the workspace.  Calls that share a workspace must be ordered on one
  * stream.
  */

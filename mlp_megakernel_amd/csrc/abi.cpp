@@ -282,14 +282,16 @@ coalesce_status coalesce_mlp_forward_train(const void* x, int64_t ldx, const voi
 
 size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L) {
   if (!dims || L < 1 || L > 8) return 0;
-  const int64_t D = dims[0];
-  if (D != 64 && D != 128) return 0;
-  if (D == 128 && L > 4) return 0;
-  for (int l = 1; l <= L; ++l)
-    if (dims[l] != D) return 0;
+  int64_t mx = 0;
+  for (int l = 0; l <= L; ++l) {
+    if (dims[l] <= 0 || dims[l] % 8 || dims[l] > 128) return 0;
+    if (dims[l] > mx) mx = dims[l];
+  }
+  const int64_t P = mx <= 64 ? 64 : 128;  // the kernel width the chain runs at
+  if (P == 128 && L > 4) return 0;
   int cus = 0;
   if (current_cus(&cus) != COALESCE_OK) return 0;
-  return mlp_backward_workspace((int)D, (int)L, cus);
+  return mlp_backward_workspace((int)P, (int)L, cus);
 }
 
 coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
@@ -297,12 +299,13 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
                                       int64_t ldd, float* const* dW, void* dx, int64_t ldq, int64_t M,
                                       coalesce_dtype dtype, coalesce_act hidden_act, void* workspace,
                                       size_t workspace_bytes, void* stream) {
-  int64_t D = 0;
+  int64_t P = 0;
   bool square = true;
-  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &D, &square);
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square);
   if (s != COALESCE_OK) return s;
-  if (!square) return fail(COALESCE_ERR_UNSUPPORTED, "the backward takes chains whose widths all equal 64 or 128");
   if (!dW) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW is NULL");
+  const int64_t D = dims[0], O = dims[L];
+  auto wspan = [&](const void* t, int l, int64_t es) { return span(t, dims[l], dims[l + 1], dims[l + 1], es); };
   MlpBwdParams p{};
   for (int l = 0; l < L; ++l) {
     if (!dW[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW[%d] is NULL", l);
@@ -310,31 +313,32 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
     p.W[l] = W[l];
     p.dW[l] = dW[l];
   }
+  for (int l = 0; l <= L; ++l) p.dims[l] = (int)dims[l];
   if (M > 0) {
     if ((s = check_rows(x, ldx, D, 2, "x")) != COALESCE_OK) return s;
-    if ((s = check_rows(dout, ldd, D, 2, "dout")) != COALESCE_OK) return s;
+    if ((s = check_rows(dout, ldd, O, 2, "dout")) != COALESCE_OK) return s;
     if (L > 1) {
       if (!acts) return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts is NULL");
       for (int l = 0; l + 1 < L; ++l) {
         char name[16];
         snprintf(name, sizeof(name), "acts[%d]", l);
-        if ((s = check_rows(acts[l], lda, D, 4, name)) != COALESCE_OK) return s;
+        if ((s = check_rows(acts[l], lda, dims[l + 1], 4, name)) != COALESCE_OK) return s;
         p.acts[l] = acts[l];
       }
     }
     if (dx) {
       if ((s = check_rows(dx, ldq, D, 2, "dx")) != COALESCE_OK) return s;
       const Range rq = span(dx, M, D, ldq, 2);
-      bool bad = overlap(rq, span(x, M, D, ldx, 2)) || overlap(rq, span(dout, M, D, ldd, 2));
-      for (int l = 0; l < L; ++l) bad = bad || overlap(rq, span(W[l], D, D, D, 2)) || overlap(rq, span(dW[l], D, D, D, 4));
-      for (int l = 0; l + 1 < L; ++l) bad = bad || overlap(rq, span(acts[l], M, D, lda, 4));
+      bool bad = overlap(rq, span(x, M, D, ldx, 2)) || overlap(rq, span(dout, M, O, ldd, 2));
+      for (int l = 0; l < L; ++l) bad = bad || overlap(rq, wspan(W[l], l, 2)) || overlap(rq, wspan(dW[l], l, 4));
+      for (int l = 0; l + 1 < L; ++l) bad = bad || overlap(rq, span(acts[l], M, dims[l + 1], lda, 4));
       if (bad) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dx overlaps an input or a weight gradient");
     }
   }
   int cus = 0;
   s = current_cus(&cus);
   if (s != COALESCE_OK) return s;
-  const size_t need = mlp_backward_workspace((int)D, (int)L, cus);
+  const size_t need = mlp_backward_workspace((int)P, (int)L, cus);
   if (!workspace) return fail(COALESCE_ERR_INVALID_ARGUMENT, "workspace is NULL");
   if (!aligned16(workspace)) return fail(COALESCE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
@@ -342,10 +346,10 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
                 need);
   const Range rw = {(uintptr_t)workspace, (uintptr_t)workspace + need};
   for (int l = 0; l < L; ++l) {
-    const Range rg = span(dW[l], D, D, D, 4);
+    const Range rg = wspan(dW[l], l, 4);
     if (overlap(rg, rw)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW[%d] overlaps the workspace", l);
     for (int j = 0; j < L; ++j)
-      if ((j != l && overlap(rg, span(dW[j], D, D, D, 4))) || overlap(rg, span(W[j], D, D, D, 2)))
+      if ((j != l && overlap(rg, wspan(dW[j], j, 4))) || overlap(rg, wspan(W[j], j, 2)))
         return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW[%d] overlaps another weight or gradient", l);
   }
   p.x = x;
@@ -357,7 +361,8 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
   p.lda = lda;
   p.ldq = ldq;
   p.M = (int)M;
-  hipError_t e = launch_mlp_backward(p, (int)D, (int)L, act_code(hidden_act), cus, (hipStream_t)stream);
+  (void)square;
+  hipError_t e = launch_mlp_backward(p, (int)P, (int)L, act_code(hidden_act), cus, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "MLP backward launch");
   return ok();
 }

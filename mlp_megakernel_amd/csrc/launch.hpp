@@ -50,7 +50,8 @@ struct MlpBwdParams {
   const float* acts[8]; // acts[l] = h_{l+1}, M x D fp32, pitch lda (l = 0..L-2)
   void* dx;             // M x D fp16, pitch ldq, or nullptr
   float* partial;       // grid x L x D x D fp32 per-workgroup weight-gradient sums
-  float* dW[8];         // D x D fp32, dense: the reduced weight gradients
+  float* dW[8];         // dims[l] x dims[l+1] fp32, dense: the reduced weight gradients
+  int dims[9];          // the chain's true widths (multiples of 8, at most the kernel width D)
   int64_t ldx, ldd, lda, ldq;
   int M;
   int num_tiles;        // row tiles (set by the launcher)

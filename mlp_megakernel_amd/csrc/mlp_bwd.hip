@@ -91,16 +91,21 @@ __device__ __forceinline__ void stage_weights_bwd(const MlpBwdParams& p, _Float1
     const int rem = idx - l * D * CPR;
     const int k = rem / CPR;
     const int cb = rem - k * CPR;
-    const _Float16* row = (const _Float16*)p.W[l] + (int64_t)k * D;
+    // the true layer is dims[l] x dims[l+1] (pitch dims[l+1]); units outside
+    // it are staged as zero (a narrower chain run at width D)
+    const int K = p.dims[l], N = p.dims[l + 1];
+    const _Float16* row = (const _Float16*)p.W[l] + (int64_t)k * N;
+    const f16x4 z4 = (f16x4){0, 0, 0, 0};
     f16x8 v;
     if (l == L - 1) {
-      v = *(const f16x8*)(row + 8 * cb);
+      v = (k < K && 8 * cb < N) ? *(const f16x8*)(row + 8 * cb) : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
     } else {
       // slots 8 cb .. 8 cb + 7 (cb = 4 a + b) hold units 32 a + 4 b + 0..3
-      // and 32 a + 16 + 4 b + 0..3
+      // and 32 a + 16 + 4 b + 0..3 (each group of 4 is inside or outside N
+      // as a whole, N being a multiple of 8)
       const int a = cb >> 2, b = cb & 3;
-      const f16x4 lo = *(const f16x4*)(row + 32 * a + 4 * b);
-      const f16x4 hi = *(const f16x4*)(row + 32 * a + 16 + 4 * b);
+      const f16x4 lo = (k < K && 32 * a + 4 * b < N) ? *(const f16x4*)(row + 32 * a + 4 * b) : z4;
+      const f16x4 hi = (k < K && 32 * a + 16 + 4 * b < N) ? *(const f16x4*)(row + 32 * a + 16 + 4 * b) : z4;
       v = (f16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
     *(f16x8*)(sW + (l * D + k) * D + ((cb ^ wswz<D>(k)) << 3)) = v;
@@ -165,26 +170,38 @@ struct RowsF32 {  // fp32 result layout: v[s][t] = units 16 t + 4 g .. + 3 of th
   f32x4 v[BGeo<D>::MT][BGeo<D>::NT];
 };
 
+// A lane's access to columns at or beyond the operand's true width goes to a
+// buffer offset past every resource's size (16 rows of any operand span
+// less than 2^31 bytes), so the load reads zero and the store is dropped.
+constexpr uint32_t OFF_NONE = 0x80000000u;
+__device__ __forceinline__ uint32_t masked(bool ok, uint32_t off) { return ok ? off : OFF_NONE; }
+__device__ __forceinline__ int lane_group() { return (int)(threadIdx.x & 63) >> 4; }
+
+// B-form fp16 rows (x, dout) of `width` true columns: units 32 ks + 8 g .. + 7.
 template <int D>
-__device__ __forceinline__ void load_b(const void* base, int64_t ld, uint32_t off, int M, int tile, int w,
+__device__ __forceinline__ void load_b(const void* base, int64_t ld, uint32_t off, int M, int tile, int w, int width,
                                        FragB<D>& f) {
 #pragma unroll
   for (int s = 0; s < BGeo<D>::MT; ++s) {
     const __amdgpu_buffer_rsrc_t rs = brsrc<D>(base, M, tile, w, s, ld, 2);
 #pragma unroll
-    for (int ks = 0; ks < BGeo<D>::KS; ++ks) f.v[s][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64u * ks, 0, 0);
+    for (int ks = 0; ks < BGeo<D>::KS; ++ks)
+      f.v[s][ks] = __builtin_amdgcn_raw_buffer_load_b128(rs, masked(32 * ks + 8 * lane_group() < width, off + 64u * ks),
+                                                         0, 0);
   }
 }
 
+// fp32 activation rows of `width` true columns: units 16 t + 4 g .. + 3.
 template <int D>
 __device__ __forceinline__ void load_acts(const float* base, int64_t ld, uint32_t off, int M, int tile, int w,
-                                          RowsF32<D>& f) {
+                                          int width, RowsF32<D>& f) {
 #pragma unroll
   for (int s = 0; s < BGeo<D>::MT; ++s) {
     const __amdgpu_buffer_rsrc_t rs = brsrc<D>(base, M, tile, w, s, ld, 4);
 #pragma unroll
     for (int t = 0; t < BGeo<D>::NT; ++t)
-      f.v[s][t] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off + 64u * t, 0, 0));
+      f.v[s][t] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, masked(16 * t + 4 * lane_group() < width, off + 64u * t), 0, 0));
   }
 }
 
@@ -381,7 +398,10 @@ __device__ __forceinline__ void layer_grads(const MlpBwdParams& p, const BLane<D
             if (u % 2 == 0)
               ev[s] = o;
             else
-              store_pair(rq[s], qoff + 32u * (uint32_t)(u - 1), ev[s], o);
+              store_pair(rq[s],
+                         masked(16 * (u - 1) + 16 * (lane_group() & 1) + 8 * (lane_group() >> 1) < p.dims[0],
+                                qoff + 32u * (uint32_t)(u - 1)),
+                         ev[s], o);
           }
         }
       }
@@ -440,9 +460,9 @@ template <int D, int L>
 __device__ __forceinline__ void load_h(const MlpBwdParams& p, const BLane<D>& c, int j, int tile, int w,
                                        BState<D, L>& st) {
   if (j >= 1)
-    load_acts<D>(p.acts[j - 1], p.lda, opaque(c.aoff), p.M, tile, w, st.a[BPolicy<D, L>::FULL ? j - 1 : 0]);
+    load_acts<D>(p.acts[j - 1], p.lda, opaque(c.aoff), p.M, tile, w, p.dims[j], st.a[BPolicy<D, L>::FULL ? j - 1 : 0]);
   else
-    load_b<D>(p.x, p.ldx, opaque(c.boff), p.M, tile, w, st.hx);
+    load_b<D>(p.x, p.ldx, opaque(c.boff), p.M, tile, w, p.dims[0], st.hx);
 }
 
 // Stage h_j of the current tile into the staging set `set` (sH = set, sZ =
@@ -521,7 +541,7 @@ __global__ __launch_bounds__(BGeo<D>::THREADS, 1) void mlp_bwd_kernel(MlpBwdPara
   FragB<D> dz, nz;
   int tile = blockIdx.x;
   if (tile < p.num_tiles) {
-    load_b<D>(p.dout, p.ldd, doff, p.M, tile, w, st.dn);
+    load_b<D>(p.dout, p.ldd, doff, p.M, tile, w, p.dims[L], st.dn);
     if constexpr (P::FULL) {
 #pragma unroll
       for (int j = L - 1; j >= 0; --j) load_h<D, L>(p, c, j, tile, w, st);
@@ -535,7 +555,7 @@ __global__ __launch_bounds__(BGeo<D>::THREADS, 1) void mlp_bwd_kernel(MlpBwdPara
     // the tile's first layer: sZ <- dout, sH <- h_{L-1}
     dz = st.dn;
     stage_b<D>(cur + P::SZ, c, dz);
-    load_b<D>(p.dout, p.ldd, doff, p.M, next, w, st.dn);  // zero rows past the last tile
+    load_b<D>(p.dout, p.ldd, doff, p.M, next, w, p.dims[L], st.dn);  // zero rows past the last tile
     stage_h<D, L, L - 1>(p, c, cur, tile, next, w, st);
     tile_layers<D, L, L - 1, ACT, DX>(p, c, cur, nxt, tile, next, w, st, dz, nz, dw);
     // layer l used set cur when L - 1 - l is even: the next tile starts on the
@@ -595,9 +615,11 @@ __global__ __launch_bounds__(RED_GROUPS* RED_SLICES) void mlp_bwd_reduce(const f
   const int blk = rem >> 6, lane = rem & 63;
   const int kb = blk / (D / 16), nb = blk - kb * (D / 16);
   const int k = 16 * kb + 4 * (lane >> 4), n = 16 * nb + (lane & 15);
+  const int K = p.dims[l], N = p.dims[l + 1];  // the true layer (a narrower chain writes its part only)
   float* dst = p.dW[l];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dst[(k + i) * D + n] = sum[i];
+  for (int i = 0; i < 4; ++i)
+    if (k + i < K && n < N) dst[(k + i) * N + n] = sum[i];
 }
 
 template <int D, int L, int ACT, bool DX>

@@ -157,7 +157,7 @@ def mlp_bwd(D=128, L=3, **kw):
     (dict(dW=None), INV), (dict(dW=[P * 1024, None, P * 1032]), INV), (dict(dW=[P * 1024 + 2, P * 1028, P * 1032]), UNS),
     (dict(x=None), INV), (dict(dout=None), INV), (dict(acts=None), INV), (dict(ldd=100), INV), (dict(ldq=64), INV),
     (dict(dout=P * 128 + 8), UNS), (dict(lda=129), UNS), (dict(dx=P + 64), INV),  # dx overlaps x
-    (dict(act=mk.ACT_GELU_ERF), UNS), (dict(dt=mk.F32), UNS), (dict(D=64, L=9), UNS), (dict(D=32), UNS),
+    (dict(act=mk.ACT_GELU_ERF), UNS), (dict(dt=mk.F32), UNS), (dict(D=64, L=9), UNS), (dict(D=136), UNS),
     (dict(D=100), UNS),
     (dict(L=0), INV), (dict(M=-5), INV), (dict(act=11), INV),
 ])

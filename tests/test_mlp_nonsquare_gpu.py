@@ -95,3 +95,45 @@ def test_nonsquare_grid_invariance():
     b = mk.mlp_forward(xg, wg, num_workgroups=7)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("dims", CHAINS, ids=lambda d: "x".join(map(str, d)))
+def test_backward_random_parity(dims):
+    L = len(dims) - 1
+    for M in (65, 3001):
+        progress("nonsquare backward %s M=%d" % (dims, M))
+        x, Ws = datagen.mlp_inputs(datagen.MLP5, M=M, dims=dims)
+        g = datagen.mlp_grad_output(datagen.MLP5, M=M, dims=dims)
+        xg = _padded(x, 8, float("nan"))       # NaN beyond x's width must never be read
+        gg = _padded(g, 16, float("nan"))      # nor beyond dout's
+        wg = [w.to("cuda") for w in Ws]
+        _, acts = mk.mlp_forward_train(xg, wg)
+        dW = [torch.full((dims[l], dims[l + 1]), 5.0, device="cuda") for l in range(L)]
+        dx = _padded(torch.zeros(M, dims[0], dtype=torch.float16), 24, 9.0)
+        mk.mlp_backward(xg, wg, acts, gg, dW=dW, dx=dx)
+        torch.cuda.synchronize()
+        o_dW, o_dx = oracle.mlp_backward(f64(x), [f64(w) for w in Ws], f64(g))
+        for l in range(L):
+            assert_close(f64(dW[l]), o_dW[l], 2e-2, "dW[%d] %s M=%d" % (l, dims, M))
+        assert_close(f64(dx), o_dx, 2e-2, "dx %s M=%d" % (dims, M))
+        base = dx.as_strided((M, dx.stride(0)), (dx.stride(0), 1))
+        assert torch.all(base[:, dims[0]:] == 9.0), "a store went past dx's width"
+
+
+@pytest.mark.parametrize("act", ["none", "relu"])
+@pytest.mark.parametrize("dims", CHAINS, ids=lambda d: "x".join(map(str, d)))
+def test_backward_selection_chains_exact(act, dims):
+    L = len(dims) - 1
+    M = 333
+    x = datagen.integer_matrix((M, dims[0]), 3, 7, 17, 8, "f16")
+    g = datagen.integer_matrix((M, dims[-1]), 5, 3, 13, 6, "f16")
+    Ws = [_selection(dims[l], dims[l + 1], 70 * l + len(dims)) for l in range(L)]
+    xg, gg = mk.aligned_copy(x), mk.aligned_copy(g)
+    wg = [w.to("cuda") for w in Ws]
+    _, acts = mk.mlp_forward_train(xg, wg, hidden_act=act)
+    dW, dx = mk.mlp_backward(xg, wg, acts, gg, hidden_act=act)
+    torch.cuda.synchronize()
+    o_dW, o_dx = oracle.mlp_backward(f64(x), [f64(w) for w in Ws], f64(g), hidden_act=act)
+    for l in range(L):
+        assert np.array_equal(f64(dW[l]), o_dW[l]), (act, dims, l)
+    assert np.array_equal(f64(dx), o_dx), (act, dims)
