@@ -246,6 +246,54 @@ coalesce_status coalesce_activation(const void* X, int64_t ldx, void* Y, int64_t
  */
 coalesce_status coalesce_flush_caches(const void* buf, size_t bytes, void* sink, void* stream);
 
+/*
+ * Per-shape autotuning ("Coalesce" README, plan's phase 4 and its finding that
+ * tile shape was worth more than anything else measured; "MLP Megakernel"
+ * README, "Autotuning": an exhaustive search per shape, a cached fast path,
+ * and post-tune correctness validation).  An autotune call takes the same
+ * arguments as the entry point it tunes and computes the same output; it
+ * runs every candidate launch configuration `iters` times on the caller's
+ * data (the persistent grid size and the tile-group order of the bf16/fp16
+ * GEMM, the tile shape and group order of the FP32 GEMM, the grid size of
+ * the MLP megakernel), keeps the fastest whose output equals the default
+ * configuration's bit for bit (every candidate performs the same arithmetic
+ * per output element, so equality is the exact test; the default is kept
+ * unless a candidate is more than 1 % faster), and records it: later
+ * calls of coalesce_gemm_bias_act / coalesce_mlp_forward with the same
+ * device, shape, dtypes and activation use it.
+ *   iters      timed launches per candidate, 1..10000
+ *   workspace  device, 16-byte aligned, at least
+ *              round_up(rows * row_bytes of the output, 256) + 256 bytes
+ *              (the reference copy and a counter)
+ *   report     filled when not NULL
+ * Autotuning synchronises `stream` and may take a while (candidates x iters
+ * launches).  Errors as the tuned entry point; COALESCE_ERR_DEVICE also when
+ * no candidate reproduced the default output (nothing is recorded then).
+ */
+typedef struct {
+  int32_t candidates;  /* configurations tried (the default first) */
+  int32_t valid;       /* of them, those whose output matched the default's bit for bit */
+  float default_us;    /* mean launch time of the default configuration */
+  float best_us;       /* mean launch time of the chosen one */
+  int32_t grid;        /* the chosen workgroup count (0: the launcher's default) */
+  int32_t group_m;     /* the chosen tile-group height (0: default) */
+  int32_t variant;     /* FP32 GEMM tile shape: 0 heuristic, 1 = 128 x 128, 2 = 64 x 64 */
+} coalesce_tune_report;
+
+coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb,
+                                                const void* bias, void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                                coalesce_dtype in_dtype, coalesce_dtype out_dtype, coalesce_act act,
+                                                int32_t iters, void* workspace, size_t workspace_bytes,
+                                                coalesce_tune_report* report, void* stream);
+
+coalesce_status coalesce_autotune_mlp_forward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                              int32_t L, void* out, int64_t ldo, int64_t M, coalesce_dtype dtype,
+                                              coalesce_act hidden_act, int32_t iters, void* workspace,
+                                              size_t workspace_bytes, coalesce_tune_report* report, void* stream);
+
+/* Forget every tuned configuration (all devices). */
+coalesce_status coalesce_autotune_clear(void);
+
 /* Number of compute units of the current device (cached per device). */
 int32_t coalesce_device_cu_count(void);
 

@@ -38,6 +38,11 @@ SIGNATURES = {
                                      _p, _sz, _p]),
     "coalesce_weight_norm": (_i32, [_p, _p, _p, _p, _i32, _i32, _p]),
     "coalesce_weight_norm_backward": (_i32, [_p, _p, _p, _p, _p, _p, _i32, _i32, _p]),
+    "coalesce_autotune_gemm_bias_act": (_i32, [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
+                                               _i32, _p, _sz, _p, _p]),
+    "coalesce_autotune_mlp_forward": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _i64, _i32, _i32, _i32, _p, _sz, _p,
+                                             _p]),
+    "coalesce_autotune_clear": (_i32, []),
     "coalesce_bias_add": (_i32, [_p, _i64, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
     "coalesce_activation": (_i32, [_p, _i64, _p, _i64, _i64, _i64, _i32, _i32, _p]),
     "coalesce_flush_caches": (_i32, [_p, _sz, _p, _p]),
@@ -123,6 +128,13 @@ def gemm_bias_act(A: torch.Tensor, B: torch.Tensor, bias: Optional[torch.Tensor]
                   out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None, stream=None):
     """Y = act(A @ B + bias) in one fused kernel (coalesce_gemm_bias_act)."""
     lib = load_library()
+    M, N, K, lda, ldb, ldy, out, odt = _gemm_args(A, B, bias, out_dtype, out)
+    _check(lib.coalesce_gemm_bias_act(_ptr(A), lda, _ptr(B), ldb, _ptr(bias), _ptr(out), ldy, M, N, K,
+                                      _DTYPES[A.dtype], _DTYPES[odt], _ACTS[act], _stream(stream)))
+    return out
+
+
+def _gemm_args(A, B, bias, out_dtype, out):
     M, K, lda = _matrix(A, "A")
     K2, N, ldb = _matrix(B, "B")
     if K2 != K:
@@ -138,9 +150,7 @@ def gemm_bias_act(A: torch.Tensor, B: torch.Tensor, bias: Optional[torch.Tensor]
     Mo, No, ldy = _matrix(out, "out")
     if (Mo, No) != (M, N) or out.dtype != odt:
         raise ValueError("out must be M x N of out_dtype")
-    _check(lib.coalesce_gemm_bias_act(_ptr(A), lda, _ptr(B), ldb, _ptr(bias), _ptr(out), ldy, M, N, K,
-                                      _DTYPES[A.dtype], _DTYPES[odt], _ACTS[act], _stream(stream)))
-    return out
+    return M, N, K, lda, ldb, ldy, out, odt
 
 
 def _chain_dims(x: torch.Tensor, weights: Sequence[torch.Tensor]):
@@ -316,6 +326,64 @@ def weight_norm_backward(vs: Sequence[torch.Tensor], gs: Sequence[torch.Tensor],
                                              _ptr_array(dgs), ctypes.cast(dp, ctypes.c_void_p), len(vs), F16,
                                              _stream(stream)))
     return dvs, dgs
+
+
+class TuneReport(ctypes.Structure):
+    """coalesce_tune_report."""
+    _fields_ = [("candidates", ctypes.c_int32), ("valid", ctypes.c_int32), ("default_us", ctypes.c_float),
+                ("best_us", ctypes.c_float), ("grid", ctypes.c_int32), ("group_m", ctypes.c_int32),
+                ("variant", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+def _tune_workspace(rows, row_bytes, device):
+    n = ((rows * row_bytes + 255) // 256) * 256 + 256
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def autotune_gemm_bias_act(A: torch.Tensor, B: torch.Tensor, bias: Optional[torch.Tensor] = None, act="gelu",
+                           out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                           iters: int = 10, stream=None):
+    """(Y, report dict): tune the fused GEMM's launch configuration for this
+    shape (coalesce_autotune_gemm_bias_act); later gemm_bias_act calls with
+    the same shape use the winner."""
+    lib = load_library()
+    M, N, K, lda, ldb, ldy, out, odt = _gemm_args(A, B, bias, out_dtype, out)
+    ws = _tune_workspace(M, N * out.element_size(), A.device)
+    rep = TuneReport()
+    _check(lib.coalesce_autotune_gemm_bias_act(_ptr(A), lda, _ptr(B), ldb, _ptr(bias), _ptr(out), ldy, M, N, K,
+                                               _DTYPES[A.dtype], _DTYPES[odt], _ACTS[act], int(iters), _ptr(ws),
+                                               ws.numel(), ctypes.byref(rep), _stream(stream)))
+    return out, rep.as_dict()
+
+
+def autotune_mlp_forward(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_act="softplus",
+                         out: Optional[torch.Tensor] = None, iters: int = 10, stream=None):
+    """(out, report dict): tune the megakernel's grid for this chain and
+    batch (coalesce_autotune_mlp_forward); later mlp_forward calls with the
+    same shape use the winner."""
+    lib = load_library()
+    M, ldx, dims = _chain_dims(x, weights)
+    L = len(weights)
+    if out is None:
+        out = aligned_empty(M, dims[-1], x.dtype, x.device)
+    Mo, Do, ldo = _matrix(out, "out")
+    if (Mo, Do) != (M, dims[-1]):
+        raise ValueError("out must be M x dims[L]")
+    ws = _tune_workspace(M, dims[-1] * out.element_size(), x.device)
+    rep = TuneReport()
+    dp = (ctypes.c_int64 * (L + 1))(*dims)
+    _check(lib.coalesce_autotune_mlp_forward(_ptr(x), ldx, _ptr_array(weights), ctypes.cast(dp, ctypes.c_void_p), L,
+                                             _ptr(out), ldo, M, _DTYPES[x.dtype], _ACTS[hidden_act], int(iters),
+                                             _ptr(ws), ws.numel(), ctypes.byref(rep), _stream(stream)))
+    return out, rep.as_dict()
+
+
+def autotune_clear():
+    """Forget all tuned configurations."""
+    _check(load_library().coalesce_autotune_clear())
 
 
 def bias_add(X: torch.Tensor, bias: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):

@@ -3,10 +3,15 @@
 // check passes; no device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <map>
 #include <mutex>
+#include <string>
+#include <vector>
 
 #include "../../include/coalesce.h"
 #include "launch.hpp"
@@ -84,12 +89,50 @@ int act_code(coalesce_act a) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb, const void* bias,
-                                       void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
-                                       coalesce_dtype in_dtype, coalesce_dtype out_dtype, coalesce_act act,
-                                       void* stream) {
+// A launch configuration the autotuner may choose (0 in a field: the
+// launcher's own default).
+struct TuneCfg {
+  int grid = 0, group_m = 0, variant = 0;
+};
+
+// Tuned configurations, per device and problem key.  The public entry points
+// consult it (a relaxed flag keeps the untuned path free of the lock).
+std::mutex g_tune_mutex;
+std::map<std::string, TuneCfg> g_tuned;
+std::atomic<bool> g_tuned_any{false};
+
+std::string gemm_key(int dev, int64_t M, int64_t N, int64_t K, int in, int out, int act, bool bias) {
+  char b[160];
+  snprintf(b, sizeof(b), "gemm:%d:%lld:%lld:%lld:%d:%d:%d:%d", dev, (long long)M, (long long)N, (long long)K, in, out,
+           act, (int)bias);
+  return b;
+}
+
+std::string mlp_key(int dev, const int64_t* dims, int L, int64_t M, int act) {
+  std::string k = "mlp:" + std::to_string(dev) + ":" + std::to_string(M) + ":" + std::to_string(act) + ":";
+  for (int l = 0; l <= L; ++l) k += std::to_string(dims[l]) + ",";
+  return k;
+}
+
+bool tuned_lookup(const std::string& key, TuneCfg* cfg) {
+  if (!g_tuned_any.load(std::memory_order_relaxed)) return false;
+  std::lock_guard<std::mutex> lock(g_tune_mutex);
+  auto it = g_tuned.find(key);
+  if (it == g_tuned.end()) return false;
+  *cfg = it->second;
+  return true;
+}
+
+int current_device() {
+  int dev = 0;
+  return hipGetDevice(&dev) == hipSuccess ? dev : -1;
+}
+
+coalesce_status gemm_impl(const void* A, int64_t lda, const void* B, int64_t ldb, const void* bias, void* Y,
+                          int64_t ldy, int64_t M, int64_t N, int64_t K, coalesce_dtype in_dtype,
+                          coalesce_dtype out_dtype, coalesce_act act, void* stream, const TuneCfg* cfg) {
   if (M < 0 || N < 0 || K < 0)
     return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative extent (M=%lld N=%lld K=%lld)", (long long)M, (long long)N,
                 (long long)K);
@@ -141,6 +184,14 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
   p.M = (int)M;
   p.N = (int)N;
   p.K = (int)K;
+  TuneCfg tc;
+  if (cfg)
+    tc = *cfg;
+  else
+    tuned_lookup(gemm_key(current_device(), M, N, K, in_dtype, out_dtype, act, bias != nullptr), &tc);
+  p.grid_override = tc.grid;
+  p.group_m = tc.group_m;
+  p.variant = tc.variant;
   hipError_t e;
   if (in_dtype == COALESCE_F32)
     e = launch_gemm32(p, act_code(act), (hipStream_t)stream, cus);
@@ -149,6 +200,17 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
                       act_code(act), (hipStream_t)stream, cus);
   if (e != hipSuccess) return device_fail(e, "GEMM launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb, const void* bias,
+                                       void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                       coalesce_dtype in_dtype, coalesce_dtype out_dtype, coalesce_act act,
+                                       void* stream) {
+  return gemm_impl(A, lda, B, ldb, bias, Y, ldy, M, N, K, in_dtype, out_dtype, act, stream, nullptr);
 }
 
 }  // extern "C"
@@ -209,7 +271,7 @@ coalesce_status check_rows(const void* t, int64_t ld, int64_t D, int64_t es, con
 coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* W, const int64_t* dims, int32_t L,
                                  void* out, int64_t ldo, float* const* acts, int64_t lda, int64_t M,
                                  coalesce_dtype dtype, coalesce_act hidden_act, int64_t num_workgroups, bool train,
-                                 void* stream) {
+                                 bool use_cache, void* stream) {
   int64_t P = 0;
   bool square = true;
   coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square);
@@ -257,6 +319,10 @@ coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* 
   p.ldo = ldo;
   p.lda = train ? lda : 0;
   p.M = (int)M;
+  if (num_workgroups == 0 && !train && use_cache) {
+    TuneCfg tc;
+    if (tuned_lookup(mlp_key(current_device(), dims, L, M, hidden_act), &tc)) num_workgroups = tc.grid;
+  }
   hipError_t e = launch_mlp(p, (int)P, (int)L, act_code(hidden_act), train && L > 1, !square, (int)num_workgroups,
                             cus, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "MLP launch");
@@ -270,14 +336,14 @@ extern "C" {
 coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
                                           int32_t L, void* out, int64_t ldo, int64_t M, coalesce_dtype dtype,
                                           coalesce_act hidden_act, int64_t num_workgroups, void* stream) {
-  return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, num_workgroups, false,
+  return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, num_workgroups, false, true,
                           stream);
 }
 
 coalesce_status coalesce_mlp_forward_train(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
                                            int32_t L, void* out, int64_t ldo, float* const* acts, int64_t lda,
                                            int64_t M, coalesce_dtype dtype, coalesce_act hidden_act, void* stream) {
-  return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, acts, lda, M, dtype, hidden_act, 0, true, stream);
+  return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, acts, lda, M, dtype, hidden_act, 0, true, false, stream);
 }
 
 size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L) {
@@ -517,6 +583,226 @@ coalesce_status coalesce_weight_norm_backward(const void* const* v, const void* 
   }
   hipError_t e = launch_weight_norm_backward(p, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "weight_norm_backward launch");
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Time `iters` back-to-back launches of run() on the stream (after one
+// untimed launch) and check the output against the reference with the
+// compare kernel.  Synchronises the stream.
+struct Trial {
+  float us = 0.f;
+  bool valid = false;
+  coalesce_status status = COALESCE_OK;
+};
+
+template <typename Run>
+Trial trial(Run run, int iters, hipStream_t st, const void* out, int64_t out_pitch_bytes, const void* ref,
+            int64_t rows, int64_t row_bytes, unsigned int* counter, int cus) {
+  Trial t;
+  hipEvent_t a = nullptr, b = nullptr;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+    if (a) hipEventDestroy(a);
+    t.status = fail(COALESCE_ERR_DEVICE, "hipEventCreate failed");
+    return t;
+  }
+  t.status = run();
+  if (t.status == COALESCE_OK) {
+    hipEventRecord(a, st);
+    for (int i = 0; i < iters && t.status == COALESCE_OK; ++i) t.status = run();
+    hipEventRecord(b, st);
+  }
+  unsigned int diff = 1;
+  if (t.status == COALESCE_OK) {
+    hipError_t e = hipMemsetAsync(counter, 0, sizeof(unsigned int), st);
+    if (e == hipSuccess) e = launch_compare(out, out_pitch_bytes, ref, row_bytes, rows, row_bytes, counter, st, cus);
+    if (e == hipSuccess) e = hipMemcpyAsync(&diff, counter, sizeof(diff), hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+    if (e != hipSuccess) t.status = device_fail(e, "autotune timing");
+    t.us = ms * 1e3f / (float)(iters > 0 ? iters : 1);
+    t.valid = diff == 0;
+  }
+  hipEventDestroy(a);
+  hipEventDestroy(b);
+  return t;
+}
+
+// The autotuner's own arguments: iters in range, a workspace large enough
+// for the reference copy of the output (rows x row_bytes, rounded up to 256
+// bytes) and the counter, apart from every operand.
+coalesce_status check_tune_args(int iters, const void* workspace, size_t workspace_bytes, int64_t rows,
+                                int64_t row_bytes, const std::vector<Range>& operands) {
+  if (iters < 1 || iters > 10000) return fail(COALESCE_ERR_INVALID_ARGUMENT, "iters must be in 1..10000");
+  const size_t need = (((size_t)rows * (size_t)row_bytes + 255) & ~(size_t)255) + 256;
+  if (!workspace) return fail(COALESCE_ERR_INVALID_ARGUMENT, "workspace is NULL");
+  if (!aligned16(workspace)) return fail(COALESCE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(COALESCE_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu needed", workspace_bytes, need);
+  const Range rw = {(uintptr_t)workspace, (uintptr_t)workspace + need};
+  for (const Range& r : operands)
+    if (overlap(rw, r)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "the workspace overlaps an operand");
+  return COALESCE_OK;
+}
+
+// Run the default, keep its output as the reference, try every candidate
+// (the default first), keep the fastest whose output equals the reference
+// bit for bit.
+template <typename Run>
+coalesce_status tune(const std::vector<TuneCfg>& cands, Run run, int iters, void* stream, void* out,
+                     int64_t out_pitch_bytes, int64_t rows, int64_t row_bytes, void* workspace, size_t workspace_bytes,
+                     const std::vector<Range>& operands, const std::string& key, coalesce_tune_report* report) {
+  const size_t ref_bytes = (size_t)rows * (size_t)row_bytes;
+  coalesce_status s = check_tune_args(iters, workspace, workspace_bytes, rows, row_bytes, operands);
+  if (s != COALESCE_OK) return s;
+  int cus = 0;
+  s = current_cus(&cus);
+  if (s != COALESCE_OK) return s;
+  hipStream_t st = (hipStream_t)stream;
+  char* ref = (char*)workspace;
+  unsigned int* counter = (unsigned int*)(ref + ((ref_bytes + 255) & ~(size_t)255));
+  const TuneCfg dflt{};
+  if ((s = run(dflt)) != COALESCE_OK) return s;
+  hipError_t e = hipMemcpy2DAsync(ref, (size_t)row_bytes, out, (size_t)out_pitch_bytes, (size_t)row_bytes, (size_t)rows,
+                                  hipMemcpyDeviceToDevice, st);
+  if (e != hipSuccess) return device_fail(e, "autotune reference copy");
+  TuneCfg best = dflt;
+  float best_us = 0.f, default_us = 0.f;
+  bool default_valid = false;
+  int valid = 0;
+  for (size_t i = 0; i < cands.size(); ++i) {
+    const TuneCfg c = cands[i];
+    Trial t = trial([&]() { return run(c); }, iters, st, out, out_pitch_bytes, ref, rows, row_bytes, counter, cus);
+    if (t.status != COALESCE_OK) return t.status;
+    if (i == 0) default_us = t.us;
+    if (!t.valid) continue;
+    if (i == 0) default_valid = true;
+    ++valid;
+    if (valid == 1 || t.us < best_us) {
+      best = c;
+      best_us = t.us;
+    }
+  }
+  if (valid == 0) return fail(COALESCE_ERR_DEVICE, "no configuration reproduced the default's output");
+  // a candidate has to beat the default by more than timing noise (1 %) to
+  // replace it
+  if (valid > 0 && default_valid && best_us > 0.99f * default_us) {
+    best = dflt;
+    best_us = default_us;
+  }
+  {
+    std::lock_guard<std::mutex> lock(g_tune_mutex);
+    g_tuned[key] = best;
+    g_tuned_any.store(true);
+  }
+  if ((s = run(best)) != COALESCE_OK) return s;
+  if (report) {
+    report->candidates = (int32_t)cands.size();
+    report->valid = valid;
+    report->default_us = default_us;
+    report->best_us = best_us;
+    report->grid = best.grid;
+    report->group_m = best.group_m;
+    report->variant = best.variant;
+  }
+  return ok();
+}
+
+void add_unique(std::vector<TuneCfg>& v, TuneCfg c) {
+  for (const TuneCfg& x : v)
+    if (x.grid == c.grid && x.group_m == c.group_m && x.variant == c.variant) return;
+  v.push_back(c);
+}
+
+}  // namespace
+
+extern "C" {
+
+coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb,
+                                                const void* bias, void* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                                                coalesce_dtype in_dtype, coalesce_dtype out_dtype, coalesce_act act,
+                                                int32_t iters, void* workspace, size_t workspace_bytes,
+                                                coalesce_tune_report* report, void* stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown dtype");
+  const int64_t is = dsize(in_dtype), os = dsize(out_dtype);
+  std::vector<Range> operands;
+  const bool work = M > 0 && N > 0 && M <= kMaxExtent && N <= kMaxExtent;
+  if (work) {
+    operands = {span(Y, M, N, ldy, os), span(bias, 1, N, N, is)};
+    if (K > 0) {
+      operands.push_back(span(A, M, K, lda, is));
+      operands.push_back(span(B, K, N, ldb, is));
+    }
+    coalesce_status s = check_tune_args(iters, workspace, workspace_bytes, M, N * os, operands);
+    if (s != COALESCE_OK) return s;
+  }
+  // the entry point's own checks (and a first launch) through the untuned path
+  const TuneCfg dflt{};
+  coalesce_status s = gemm_impl(A, lda, B, ldb, bias, Y, ldy, M, N, K, in_dtype, out_dtype, act, stream, &dflt);
+  if (s != COALESCE_OK) return s;
+  if (!work) return ok();
+  int cus = 0;
+  if ((s = current_cus(&cus)) != COALESCE_OK) return s;
+  std::vector<TuneCfg> cands;
+  cands.push_back(dflt);
+  if (in_dtype == COALESCE_F32) {
+    for (int variant : {1, 2})
+      for (int gm : {4, 8, 16}) add_unique(cands, TuneCfg{0, gm, variant});
+  } else {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    std::vector<int> grids = {0, cus / 2, (3 * cus) / 4};
+    if (tiles <= 4 * (int64_t)cus) grids.push_back((int)tiles);
+    for (int g : grids)
+      for (int gm : {4, 8, 16})
+        if (g >= 0 && g <= tiles) add_unique(cands, TuneCfg{g, gm, 0});
+  }
+  const std::string key = gemm_key(current_device(), M, N, K, in_dtype, out_dtype, act, bias != nullptr);
+  return tune(
+      cands,
+      [&](const TuneCfg& c) {
+        return gemm_impl(A, lda, B, ldb, bias, Y, ldy, M, N, K, in_dtype, out_dtype, act, stream, &c);
+      },
+      iters, stream, Y, ldy * os, M, N * os, workspace, workspace_bytes, operands, key, report);
+}
+
+coalesce_status coalesce_autotune_mlp_forward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                              int32_t L, void* out, int64_t ldo, int64_t M, coalesce_dtype dtype,
+                                              coalesce_act hidden_act, int32_t iters, void* workspace,
+                                              size_t workspace_bytes, coalesce_tune_report* report, void* stream) {
+  int64_t P = 0;
+  bool square = true;
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square);
+  if (s != COALESCE_OK) return s;
+  std::vector<Range> operands = {span(x, M, dims[0], ldx, 2), span(out, M, dims[L], ldo, 2)};
+  for (int l = 0; l < L; ++l) operands.push_back(span(W[l], dims[l], dims[l + 1], dims[l + 1], 2));
+  if (M > 0 && (s = check_tune_args(iters, workspace, workspace_bytes, M, dims[L] * 2, operands)) != COALESCE_OK)
+    return s;
+  s = mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, 0, false, false, stream);
+  if (s != COALESCE_OK) return s;
+  if (M == 0) return ok();
+  int cus = 0;
+  if ((s = current_cus(&cus)) != COALESCE_OK) return s;
+  std::vector<TuneCfg> cands;
+  cands.push_back(TuneCfg{});
+  for (int g : {cus / 4, cus / 2, cus, 2 * cus, 3 * cus}) add_unique(cands, TuneCfg{g, 0, 0});
+  const std::string key = mlp_key(current_device(), dims, L, M, hidden_act);
+  return tune(
+      cands,
+      [&](const TuneCfg& c) {
+        return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, c.grid, false, false,
+                                stream);
+      },
+      iters, stream, out, ldo * 2, M, dims[L] * 2, workspace, workspace_bytes, operands, key, report);
+}
+
+coalesce_status coalesce_autotune_clear(void) {
+  std::lock_guard<std::mutex> lock(g_tune_mutex);
+  g_tuned.clear();
+  g_tuned_any.store(false);
   return ok();
 }
 

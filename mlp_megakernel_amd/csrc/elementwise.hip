@@ -93,6 +93,21 @@ __global__ __launch_bounds__(256) void flush_kernel(const u32x4* __restrict__ bu
   if (v == 0x9e3779b9u) sink[0] = v;
 }
 
+// Autotuning's validation: count the 16-bit words in which two matrices of
+// rows x row_bytes differ (grid-stride over rows and words; one atomic add
+// per thread that saw a difference).
+__global__ __launch_bounds__(256) void compare_kernel(const unsigned short* __restrict__ a, int64_t pitch_a,
+                                                      const unsigned short* __restrict__ b, int64_t pitch_b,
+                                                      int64_t rows, int64_t words, unsigned int* counter) {
+  unsigned int diff = 0;
+  const int64_t total = rows * words;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / words, c = i - r * words;
+    diff += a[r * pitch_a + c] != b[r * pitch_b + c] ? 1u : 0u;
+  }
+  if (diff) atomicAdd(counter, diff);
+}
+
 int grid_for(int64_t work_items, int num_cus) {
   const int64_t blocks = (work_items + 255) / 256;
   const int64_t cap = (int64_t)num_cus * 16;
@@ -145,6 +160,15 @@ hipError_t launch_activation(const void* X, int64_t ldx, void* Y, int64_t ldy, i
     case DT_F16: return act_dispatch<_Float16>(X, ldx, Y, ldy, M, N, act, stream, num_cus);
     default: return act_dispatch<__bf16>(X, ldx, Y, ldy, M, N, act, stream, num_cus);
   }
+}
+
+hipError_t launch_compare(const void* a, int64_t pitch_a, const void* b, int64_t pitch_b, int64_t rows,
+                          int64_t row_bytes, unsigned int* counter, hipStream_t stream, int num_cus) {
+  const int64_t words = row_bytes / 2;
+  if (rows <= 0 || words <= 0) return hipSuccess;
+  hipLaunchKernelGGL(compare_kernel, dim3(grid_for(rows * words, num_cus)), dim3(256), 0, stream,
+                     (const unsigned short*)a, pitch_a / 2, (const unsigned short*)b, pitch_b / 2, rows, words, counter);
+  return hipGetLastError();
 }
 
 hipError_t launch_flush(const void* buf, size_t bytes, void* sink, hipStream_t stream, int num_cus) {

@@ -514,7 +514,8 @@ __global__ __launch_bounds__(Geo<NW>::THREADS, 1) void gemm16_kernel(GemmParams 
 #endif
 
 // Grid: min(#tiles, #CUs x workgroups per CU), the per-CU count from the
-// runtime for the compiled kernel, cached per instantiation.
+// runtime for the compiled kernel, cached per instantiation (or the caller's
+// grid_override, an autotuning knob).
 template <typename T, typename TO, int ACT, bool HAS_BIAS>
 hipError_t launch_bias(const GemmParams& p, hipStream_t stream, int num_cus) {
   constexpr int NW = GEMM16_WAVES;
@@ -527,7 +528,7 @@ hipError_t launch_bias(const GemmParams& p, hipStream_t stream, int num_cus) {
     per_cu = n > 0 ? n : 1;
   }
   const long total = (long)p.tiles_m * p.tiles_n;
-  const long cap = (long)num_cus * per_cu;
+  const long cap = p.grid_override > 0 ? (long)p.grid_override : (long)num_cus * per_cu;
   const int grid = (int)(total < cap ? total : cap);
   hipLaunchKernelGGL((gemm16_kernel<T, TO, ACT, HAS_BIAS, NW>), dim3(grid), dim3(Geo<NW>::THREADS), 0, stream, p);
   return hipGetLastError();
@@ -554,7 +555,7 @@ hipError_t launch_act(GemmParams p, int act, hipStream_t stream, int num_cus) {
 hipError_t launch_gemm16(GemmParams p, DType in, DType out, int act, hipStream_t stream, int num_cus) {
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
-  p.group_m = 8;
+  if (p.group_m <= 0) p.group_m = 8;
   if (in == DT_BF16) {
     if (out == DT_F32) return launch_act<__bf16, float>(p, act, stream, num_cus);
     return launch_act<__bf16, __bf16>(p, act, stream, num_cus);

@@ -227,7 +227,7 @@ template <int BM, int BN, int ACT>
 hipError_t launch_cfg(GemmParams p, hipStream_t stream) {
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
-  p.group_m = 8;
+  if (p.group_m <= 0) p.group_m = 8;
   dim3 grid(p.tiles_m * p.tiles_n), block(THREADS);
   if (p.bias)
     hipLaunchKernelGGL((gemm32_kernel<BM, BN, ACT, true>), grid, block, 0, stream, p);
@@ -250,8 +250,10 @@ hipError_t launch_act(GemmParams p, int act, hipStream_t stream) {
 
 hipError_t launch_gemm32(GemmParams p, int act, hipStream_t stream, int num_cus) {
   // 128 x 128 tiles when they give at least one workgroup per CU, else 64 x 64.
+  // (variant 1 / 2 force one of them: an autotuning knob)
   const long tiles128 = (long)((p.M + 127) / 128) * ((p.N + 127) / 128);
-  if (tiles128 >= num_cus) return launch_act<128, 128>(p, act, stream);
+  const bool big = p.variant == 1 || (p.variant == 0 && tiles128 >= num_cus);
+  if (big) return launch_act<128, 128>(p, act, stream);
   return launch_act<64, 64>(p, act, stream);
 }
 

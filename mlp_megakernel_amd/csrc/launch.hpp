@@ -15,7 +15,10 @@ struct GemmParams {
   void* Y;
   int64_t lda, ldb, ldy;
   int M, N, K;
-  int tiles_m, tiles_n, group_m;
+  int tiles_m, tiles_n;
+  int group_m;        // tile rows per group of the tile order (0: the launcher's default)
+  int grid_override;  // workgroups to launch (0: the launcher's default); persistent kernels walk the rest
+  int variant;        // FP32 GEMM tile shape: 0 heuristic, 1 = 128 x 128, 2 = 64 x 64
 };
 
 // Each launcher picks its tile configuration, fills tiles_* and launches on
@@ -83,5 +86,9 @@ hipError_t launch_bias_add(const void* X, int64_t ldx, const void* bias, void* Y
 hipError_t launch_activation(const void* X, int64_t ldx, void* Y, int64_t ldy, int M, int N, DType dt, int act,
                              hipStream_t stream, int num_cus);
 hipError_t launch_flush(const void* buf, size_t bytes, void* sink, hipStream_t stream, int num_cus);
+// counter += number of 16-bit words that differ between two rows x row_bytes
+// matrices (pitches in bytes; row_bytes even).
+hipError_t launch_compare(const void* a, int64_t pitch_a, const void* b, int64_t pitch_b, int64_t rows,
+                          int64_t row_bytes, unsigned int* counter, hipStream_t stream, int num_cus);
 
 }  // namespace coalesce

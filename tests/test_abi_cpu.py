@@ -209,3 +209,48 @@ def test_weight_norm_output_checks():
     assert wn(back=True, dg=[P * 768, P * 768, P * 770]) == INV  # dg[0] and dg[1] coincide
     assert wn(back=True, dv=[P * 256, P * 516, P * 520]) == INV  # dv[0] overlaps dW[0]
     assert wn(back=True, dW=[P * 256 + 2, P * 260, P * 264]) == UNS
+
+
+def tune_gemm(ws=P * 64, wsb=1 << 20, iters=5, **kw):
+    a = dict(A=P, lda=64, B=P * 2, ldb=64, bias=None, Y=P * 4, ldy=64, M=8, N=64, K=64, i=mk.F16, o=mk.F16,
+             act=mk.ACT_GELU_ERF)
+    a.update(kw)
+    return mk.load_library().coalesce_autotune_gemm_bias_act(
+        a["A"], a["lda"], a["B"], a["ldb"], a["bias"], a["Y"], a["ldy"], a["M"], a["N"], a["K"], a["i"], a["o"],
+        a["act"], iters, ws, wsb, None, None)
+
+
+def tune_mlp(D=128, L=3, ws=P * 256, wsb=1 << 20, iters=5, **kw):
+    W = (ctypes.c_void_p * L)(*[P * (16 + l) for l in range(L)])
+    d = (ctypes.c_int64 * (L + 1))(*([D] * (L + 1)))
+    a = dict(x=P, ldx=D, out=P * 64, ldo=D, M=100, act=mk.ACT_SOFTPLUS)
+    a.update(kw)
+    return mk.load_library().coalesce_autotune_mlp_forward(
+        a["x"], a["ldx"], ctypes.cast(W, ctypes.c_void_p), ctypes.cast(d, ctypes.c_void_p), L, a["out"], a["ldo"],
+        a["M"], mk.F16, a["act"], iters, ws, wsb, None, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(iters=0), INV), (dict(iters=10001), INV), (dict(ws=None), INV), (dict(ws=P * 64 + 8), UNS),
+    (dict(wsb=8 * 64 * 2 + 255), INV),  # the reference copy (1 KiB, rounded to 256) plus 256 bytes
+    (dict(ws=P * 4), INV),  # the workspace is Y
+    (dict(ws=P + 64), INV),  # the workspace overlaps A
+    (dict(M=-1), INV), (dict(i=7), INV), (dict(ldy=60), INV), (dict(i=mk.F16, o=mk.BF16), UNS),
+])
+def test_autotune_gemm_rejects_before_launch(kw, status):
+    assert tune_gemm(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(iters=0), INV), (dict(ws=None), INV), (dict(wsb=100 * 256 + 255), INV), (dict(ws=P * 64), INV),
+    (dict(ws=P * 17), INV), (dict(L=0), INV), (dict(D=100), UNS), (dict(act=mk.ACT_GELU_ERF), UNS),
+    (dict(ldo=127), INV),
+])
+def test_autotune_mlp_rejects_before_launch(kw, status):
+    assert tune_mlp(**kw) == status
+
+
+def test_autotune_empty_and_clear_need_no_device():
+    assert tune_gemm(M=0) == mk.OK
+    assert tune_mlp(M=0) == mk.OK
+    assert mk.load_library().coalesce_autotune_clear() == mk.OK
