@@ -19,10 +19,11 @@
 //     one n) come from the transposing LDS read ds_read_b64_tr_b16;
 //   * LDS rows are XOR-swizzled in 16-byte chunks so that fragment reads
 //     spread over the banks;
-//   * each 32-deep slice is issued as 4 groups of {2 copies, 8 MFMAs, the
-//     fragment reads of the next slice}, fenced so the compiler keeps that
-//     interleave: the copies never arrive as a burst that stalls the wave's
-//     in-order issue, and the MFMA pipe is fed between them;
+//   * each 32-deep slice is issued as 4 groups of {2 copies, 8 MFMAs, a
+//     share of the next slice's fragment reads, those its first group needs
+//     first}, fenced so the compiler keeps that interleave: the copies never
+//     arrive as a burst that stalls the wave's in-order issue, and the MFMA
+//     pipe is fed between them;
 //   * the epilogue stages each wave's block in the (then free) LDS and stores
 //     whole 128-byte lines of Y;
 //   * the kernel is persistent (one workgroup per CU walking its tiles), and
@@ -229,17 +230,25 @@ __device__ __forceinline__ i16x4 read_af_half(Stage<T> st, int ks, int wn, int t
 }
 
 // One slice: NT groups of {2 copies of K step k + 2 when `copy` (a uniform
-// branch around the copies only), the MT MFMAs of sub-tile t, the next
-// slice's fragment reads for sub-tile t (and MT / NT of the m sub-tiles)}.
-// A scheduling fence closes every group.  The MFMAs never sit inside a
-// branch, so the accumulators stay in AGPRs.  On the last K step the "next"
-// reads fetch stale but in-bounds LDS and are unused.
+// branch around the copies only), the MT MFMAs of sub-tile t, a share of the
+// next slice's fragment reads}.  The next slice's first group needs every
+// m-side fragment and a[0], so those are read in the first two groups and the
+// later a[t] after them: no MFMA at the start of a slice waits for a read
+// issued just before it (1.8 % faster than reading a[t] and two m-side
+// fragments in group t).  A scheduling fence closes every group.  The MFMAs
+// never sit inside a branch, so the accumulators stay in AGPRs.  On the last
+// K step the "next" reads fetch stale but in-bounds LDS and are unused.
 template <typename T, int NW>
 __device__ __forceinline__ void slice(const Frags<NW>& cur, f32x4 (&acc)[Geo<NW>::NT][Geo<NW>::MT], Frags<NW>& nxt,
                                       Stage<T> rst, int rks, int wm, int wn, int lane, bool copy,
                                       const DmaPlan<NW>& d, const void* ab, const void* bb, Stage<T> cst, int wu) {
   typedef Geo<NW> G;
-  constexpr int BPG = G::MT / G::NT;  // m-side fragment reads per group
+  static_assert(G::NT == 4 && G::MT == 8, "the read plan assumes 4 x 8 sub-tiles");
+  auto read_a = [&](int t) {
+    const i16x4 lo = read_af_half<T, NW>(rst, rks, wn, t, 0, lane);
+    const i16x4 hi = read_af_half<T, NW>(rst, rks, wn, t, 1, lane);
+    nxt.a[t] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
 #pragma unroll
   for (int t = 0; t < G::NT; ++t) {
     if (copy) {
@@ -248,14 +257,22 @@ __device__ __forceinline__ void slice(const Frags<NW>& cur, f32x4 (&acc)[Geo<NW>
     }
 #pragma unroll
     for (int s = 0; s < G::MT; ++s) acc[t][s] = mfma16x16x32(cur.a[t], cur.b[s], acc[t][s], T());
-    // The reads after the MFMAs: nxt.a[t] then takes the registers of
+    // The reads after the MFMAs: nxt.a[t] may then take the registers of
     // cur.a[t], which the MFMAs above were its last use of.
     __builtin_amdgcn_sched_barrier(0);
-    const i16x4 lo = read_af_half<T, NW>(rst, rks, wn, t, 0, lane);
-    const i16x4 hi = read_af_half<T, NW>(rst, rks, wn, t, 1, lane);
-    nxt.a[t] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if (t == 0) {
+      read_a(0);
 #pragma unroll
-    for (int i = 0; i < BPG; ++i) nxt.b[t * BPG + i] = read_bf<T>(rst, rks, wm, t * BPG + i, lane);
+      for (int i = 0; i < 4; ++i) nxt.b[i] = read_bf<T>(rst, rks, wm, i, lane);
+    } else if (t == 1) {
+#pragma unroll
+      for (int i = 4; i < 8; ++i) nxt.b[i] = read_bf<T>(rst, rks, wm, i, lane);
+    } else if (t == 2) {
+      read_a(1);
+      read_a(2);
+    } else {
+      read_a(3);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
