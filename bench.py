@@ -76,8 +76,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; the workloads shard by rows with no exchange "
-              "(see DESIGN.md), but multi-GPU runs are not part of it. Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the workloads shard by rows with no exchange between GPUs, "
+              "but runs on more than one GPU are not supported. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -17,7 +17,7 @@
  *   COALESCE_ERR_INVALID_ARGUMENT  a NULL pointer where data is needed, a
  *                                  negative extent, a leading dimension
  *                                  shorter than the row, an unknown enum.
- *   COALESCE_ERR_UNSUPPORTED       a valid request this build does not
+ *   COALESCE_ERR_UNSUPPORTED       a valid request the library does not
  *                                  implement (alignment, dtype combination,
  *                                  MLP width or depth), see each function.
  *   COALESCE_ERR_DEVICE            a HIP call failed (launch or device query).
