@@ -187,7 +187,7 @@ coalesce_status gemm_impl(const void* A, int64_t lda, const void* B, int64_t ldb
   TuneCfg tc;
   if (cfg)
     tc = *cfg;
-  else
+  else if (g_tuned_any.load(std::memory_order_relaxed))  // (no key is built while nothing is recorded)
     tuned_lookup(gemm_key(current_device(), M, N, K, in_dtype, out_dtype, act, bias != nullptr), &tc);
   p.grid_override = tc.grid;
   p.group_m = tc.group_m;
@@ -319,7 +319,7 @@ coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* 
   p.ldo = ldo;
   p.lda = train ? lda : 0;
   p.M = (int)M;
-  if (num_workgroups == 0 && !train && use_cache) {
+  if (num_workgroups == 0 && !train && use_cache && g_tuned_any.load(std::memory_order_relaxed)) {
     TuneCfg tc;
     if (tuned_lookup(mlp_key(current_device(), dims, L, M, hidden_act), &tc)) num_workgroups = tc.grid;
   }
