@@ -26,6 +26,11 @@ TFLOP/s.  The same line carries
     layers in one launch) and its backward, against per-layer eager torch
     ops, and the weight-normalised training step (normalise, training
     forward, backward, normalisation backward);
+  * variants: two non-square chains (forward with its HBM roofline, and one
+    training step), the FFN GEMM with the ReLU / softplus / no epilogue, and
+    the 3 x 128 MLP with ReLU / no hidden activation;
+  * autotune: the ordinary entry points timed before and after per-shape
+    autotuning, with the configuration chosen;
   * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
     sample of the primary workload.
 All inputs are synthetic and seeded (datagen).
@@ -62,6 +67,8 @@ def parse():
     ap.add_argument("--no-train", action="store_true", help="skip the MLP training pair")
     ap.add_argument("--no-wn", action="store_true", help="skip the weight-normalisation section")
     ap.add_argument("--no-tune", action="store_true", help="skip the per-shape autotuning section")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the non-square chains and the other epilogues / hidden activations")
     ap.add_argument("--prewarm-ms", type=float, default=500.0,
                     help="untimed back-to-back running before the warmup steps of each timed case")
     ap.add_argument("--harness-iters", type=int, default=100)
@@ -393,6 +400,74 @@ def main():
             del x, g_out, acts, out, dW, dx, wsp
             torch.cuda.empty_cache()
         result["weight_norm"] = wn_res
+
+    # ------------------------------- non-square chains, other epilogues
+    if not args.no_variants:
+        var = {}
+        for w in (datagen.MLP_NS1, datagen.MLP_NS2):
+            print("bench: non-square chain %s" % w.name, file=sys.stderr, flush=True)
+            x, Ws = datagen.mlp_inputs(w)
+            x, Ws = x.to(dev), [t.to(dev) for t in Ws]
+            g_out = datagen.mlp_grad_output(w).to(dev)
+            out = torch.empty((w.M, w.dims[-1]), dtype=torch.float16, device=dev)
+            H = max(w.dims[1:-1])  # the activations share one pitch
+            acts = [torch.empty((w.M, H), dtype=torch.float32, device=dev)[:, :d] for d in w.dims[1:-1]]
+            dW = [torch.empty(t.shape, dtype=torch.float32, device=dev) for t in Ws]
+            dx = torch.empty_like(x)
+            wsp = torch.empty(mk.mlp_backward_workspace_size(w.dims), dtype=torch.uint8, device=dev)
+
+            def fwd():
+                mk.mlp_forward(x, Ws, out=out)
+
+            def step():
+                mk.mlp_forward_train(x, Ws, out=out, acts=acts)
+                mk.mlp_backward(x, Ws, acts, g_out, dW=dW, dx=dx, workspace=wsp)
+
+            f_ms, f_ev = timed_steps(fwd, max(20, args.steps), 10)
+            s_ms, _ = timed_steps(step, max(20, args.steps), 10)
+            P = 64 if max(w.dims) <= 64 else 128
+            # algorithmic bytes: x read, out written (true widths); the kernel
+            # computes at the padded width P
+            ach = w.bytes() / (f_ev * 1e-3) / 1e9
+            padded = 2.0 * w.M * w.L * P * P
+            var[w.name] = {"dims": list(w.dims), "rows": w.M, "kernel_width": P,
+                           "mfma_tflops": round(w.flops() / (f_ev * 1e-3) / 1e12, 1),
+                           "padded_flop_factor": round(padded / w.flops(), 3),
+                           "forward_ms": round(f_ms, 5), "forward_rows_per_s": round(w.M / (f_ms * 1e-3), 1),
+                           "forward_roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                                                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                                                "algorithmic_bytes_per_launch": w.bytes(),
+                                                "mean_launch_ms": round(f_ev, 5)},
+                           "train_step_ms": round(s_ms, 5), "train_step_rows_per_s": round(w.M / (s_ms * 1e-3), 1)}
+            del x, Ws, g_out, out, acts, dW, dx, wsp
+            torch.cuda.empty_cache()
+        # the FFN GEMM with the other epilogues (GELU is the primary line)
+        g = datagen.BF16_FFN
+        A, B, bias = datagen.gemm_inputs(g)
+        A, B, bias = A.to(dev), B.to(dev), bias.to(dev)
+        Y = torch.empty((g.M, g.N), dtype=torch.bfloat16, device=dev)
+        epi = {}
+        for act in ("relu", "softplus", "none"):
+            print("bench: FFN GEMM epilogue %s" % act, file=sys.stderr, flush=True)
+            _, ev = timed_steps(lambda: mk.gemm_bias_act(A, B, bias, act=act, out=Y), max(20, args.steps), 5)
+            epi[act] = {"mean_launch_ms": round(ev, 5), "tflops": round(g.flops() / (ev * 1e-3) / 1e12, 1),
+                        "frac_of_peak": round(g.flops() / (ev * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+        var["bf16_ffn_up_epilogues"] = epi
+        del A, B, bias, Y
+        torch.cuda.empty_cache()
+        # the 3 x 128 MLP with the other hidden activations
+        x, Ws = datagen.mlp_inputs(datagen.MLP3)
+        x, Ws = x.to(dev), [t.to(dev) for t in Ws]
+        out = torch.empty((datagen.MLP3.M, 128), dtype=torch.float16, device=dev)
+        hid = {}
+        for act in ("relu", "none"):
+            print("bench: MLP 3x128 hidden activation %s" % act, file=sys.stderr, flush=True)
+            _, ev = timed_steps(lambda: mk.mlp_forward(x, Ws, hidden_act=act, out=out), max(20, args.steps), 10)
+            hid[act] = {"mean_launch_ms": round(ev, 5), "rows_per_s": round(datagen.MLP3.M / (ev * 1e-3), 1)}
+        var["fp16_mlp3_d128_hidden_acts"] = hid
+        del x, Ws, out
+        torch.cuda.empty_cache()
+        result["variants"] = var
 
     # ------------------------------------------------- per-shape autotuning
     if not args.no_tune:

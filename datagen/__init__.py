@@ -164,6 +164,12 @@ MLP3 = _reg(MlpWorkload("fp16_mlp3_d128", 4, 1 << 20, (128, 128, 128, 128), "f16
 MLP5 = _reg(MlpWorkload("fp16_mlp5_d64", 5, 1 << 22, (64, 64, 64, 64, 64, 64), "f16",
                         description="fp16 5-layer softplus MLP, D=H=out=64, 2^22 rows, x~N(0,1), "
                                     "W~N(0,1/8)"))
+# Non-square chains of the quick start's FusedMLPSoftplus(D, H, out_features)
+# kind (narrow input and output, wide hidden layers), same value recipe.
+MLP_NS1 = _reg(MlpWorkload("fp16_mlp_32_128_128_16", 6, 1 << 20, (32, 128, 128, 16), "f16",
+                           description="fp16 3-layer softplus MLP 32 -> 128 -> 128 -> 16, 2^20 rows"))
+MLP_NS2 = _reg(MlpWorkload("fp16_mlp_64_128_96_128_32", 7, 1 << 20, (64, 128, 96, 128, 32), "f16",
+                           description="fp16 4-layer softplus MLP 64 -> 128 -> 96 -> 128 -> 32, 2^20 rows"))
 
 
 def gemm_inputs(w: GemmWorkload, M: Optional[int] = None, N: Optional[int] = None, K: Optional[int] = None):

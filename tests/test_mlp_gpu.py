@@ -144,7 +144,8 @@ def test_unfused_baseline_matches_oracle():
     assert_close(f64(h), ref, 2e-2, "unfused MLP")
 
 
-@pytest.mark.parametrize("name", ["fp16_mlp3_d128", "fp16_mlp5_d64"])
+@pytest.mark.parametrize("name", ["fp16_mlp3_d128", "fp16_mlp5_d64", "fp16_mlp_32_128_128_16",
+                                  "fp16_mlp_64_128_96_128_32"])
 def test_full_size_sampled_rows(name):
     w = datagen.WORKLOADS[name]
     progress("full size %s" % name)

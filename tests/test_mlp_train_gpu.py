@@ -200,7 +200,7 @@ def test_module_autograd_matches_oracle():
         assert torch.equal(model(xg), mk.mlp_forward(xg, [w for w in model.weights]))
 
 
-@pytest.mark.parametrize("w", [datagen.MLP3, datagen.MLP5], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [datagen.MLP3, datagen.MLP5, datagen.MLP_NS1, datagen.MLP_NS2], ids=lambda w: w.name)
 def test_full_size_periodic_rows_and_sampled_dx(w):
     # Full-size rows in the benchmark's launch configuration.  The rows repeat
     # with period P, so every weight gradient is (M / P) times the oracle's
