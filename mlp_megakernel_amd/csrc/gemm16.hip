@@ -32,6 +32,8 @@
 // The last, partial K step (K not a multiple of 64) goes through masked
 // register loads that zero every element past K.  Rows past M read a
 // clamped (valid) row and are never stored; columns past N are masked.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -536,13 +538,17 @@ __global__ __launch_bounds__(Geo<NW>::THREADS, 1) void gemm16_kernel(GemmParams 
 template <typename T, typename TO, int ACT, bool HAS_BIAS>
 hipError_t launch_bias(const GemmParams& p, hipStream_t stream, int num_cus) {
   constexpr int NW = GEMM16_WAVES;
-  static int per_cu = 0;
+  // (atomic: concurrent first calls from several host threads store the
+  // same value)
+  static std::atomic<int> per_cu_cache{0};
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int n = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm16_kernel<T, TO, ACT, HAS_BIAS, NW>,
                                                                 Geo<NW>::THREADS, 0);
     if (e != hipSuccess) return e;
     per_cu = n > 0 ? n : 1;
+    per_cu_cache.store(per_cu, std::memory_order_relaxed);
   }
   const long total = (long)p.tiles_m * p.tiles_n;
   const long cap = p.grid_override > 0 ? (long)p.grid_override : (long)num_cus * per_cu;

@@ -35,6 +35,8 @@
 //   * the activation is VALU-bound (two transcendentals per element), so
 //     the softplus guard is taken out of the per-element path: see
 //     softplus_b2_fast and the check at the end of mlp_kernel.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mlp_common.hpp"
@@ -557,12 +559,16 @@ template <int D, int L, int ACT, bool ST, bool PAD>
 hipError_t launch_dl(MlpParams p, int num_workgroups, int num_cus, hipStream_t stream) {
   using G = Geo<D>;
   p.num_tiles = (int)(((int64_t)p.M + G::TR - 1) / G::TR);
-  static int per_cu = 0;
+  // (atomic: concurrent first calls from several host threads store the
+  // same value)
+  static std::atomic<int> per_cu_cache{0};
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
     int n = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mlp_kernel<D, L, ACT, ST, PAD>, G::THREADS, 0);
     if (e != hipSuccess) return e;
     per_cu = n > 0 ? n : 1;
+    per_cu_cache.store(per_cu, std::memory_order_relaxed);
   }
   int nwg = num_workgroups;
   if (nwg <= 0) {
