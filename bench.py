@@ -27,8 +27,9 @@ TFLOP/s.  The same line carries
     ops, and the weight-normalised training step (normalise, training
     forward, backward, normalisation backward);
   * variants: two non-square chains (forward with its HBM roofline, and one
-    training step), the FFN GEMM with the ReLU / softplus / no epilogue, and
-    the 3 x 128 MLP with ReLU / no hidden activation;
+    training step), the FFN GEMM with the ReLU / softplus / no epilogue, the
+    3 x 128 MLP with ReLU / no hidden activation, and the 3 x 128 MLP on small
+    batches, launched eagerly and replayed from a HIP graph;
   * autotune: the ordinary entry points timed before and after per-shape
     autotuning, with the configuration chosen;
   * cpu_baseline: the fp64 oracle timed on this host's cores on a bounded
@@ -465,6 +466,27 @@ def main():
             _, ev = timed_steps(lambda: mk.mlp_forward(x, Ws, hidden_act=act, out=out), max(20, args.steps), 10)
             hid[act] = {"mean_launch_ms": round(ev, 5), "rows_per_s": round(datagen.MLP3.M / (ev * 1e-3), 1)}
         var["fp16_mlp3_d128_hidden_acts"] = hid
+        # small batches, where the launch dominates: per-call time of eager
+        # back-to-back launches and of the same calls replayed from a HIP graph
+        small = {}
+        for m in (64, 1024, 8192):
+            xs = x[:m].contiguous()
+            os_ = torch.empty((m, 128), dtype=torch.float16, device=dev)
+            _, eager_ms = timed_steps(lambda: mk.mlp_forward(xs, Ws, out=os_), 200, 20)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                mk.mlp_forward(xs, Ws, out=os_)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(20):
+                    mk.mlp_forward(xs, Ws, out=os_)
+            _, graph_ms = timed_steps(graph.replay, 20, 3)
+            small["M%d" % m] = {"eager_us": round(eager_ms * 1e3, 2), "graph_us": round(graph_ms * 1e3 / 20, 2)}
+            del graph
+        var["fp16_mlp3_d128_small_batch"] = small
         del x, Ws, out
         torch.cuda.empty_cache()
         result["variants"] = var
