@@ -260,8 +260,10 @@ coalesce_status coalesce_flush_caches(const void* buf, size_t bytes, void* sink,
  * per output element, so equality is the exact test; the default is kept
  * unless a candidate is more than 1 % faster), and records it: later
  * calls of coalesce_gemm_bias_act / coalesce_mlp_forward with the same
- * device, shape, dtypes and activation use it.
- *   iters      timed launches per candidate, 1..10000
+ * device, shape, dtypes and activation use it.  Each candidate is timed in
+ * two passes (the second in reverse order) and keeps its faster time, so
+ * the warm-up drift of the clocks favours none of them.
+ *   iters      timed launches per candidate and pass, 1..10000
  *   workspace  device, 16-byte aligned, at least
  *              round_up(rows * row_bytes of the output, 256) + 256 bytes
  *              (the reference copy and a counter)
@@ -277,7 +279,7 @@ typedef struct {
   float best_us;       /* mean launch time of the chosen one */
   int32_t grid;        /* the chosen workgroup count (0: the launcher's default) */
   int32_t group_m;     /* the chosen tile-group height (0: default) */
-  int32_t variant;     /* FP32 GEMM tile shape: 0 heuristic, 1 = 128 x 128, 2 = 64 x 64 */
+  int32_t variant;     /* FP32 GEMM tile shape: 0 heuristic, 1 = 128 x 128, 2 = 64 x 64, 3 = 32 x 32 */
 } coalesce_tune_report;
 
 coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb,

@@ -2,10 +2,11 @@
 //
 // Same method as the 16-bit kernel (bias and activation applied to the fp32
 // accumulators in registers, one store of Y), on v_mfma_f32_16x16x4_f32:
-//   * workgroup tile BM x BN (128 x 128, or 64 x 64 when the problem has too
-//     few 128 x 128 tiles to occupy the GPU), K step 32, 4 waves in a 2 x 2
-//     grid; each wave computes Y^T blocks (A operand = B^T, B operand = A^T)
-//     so each lane holds 4 consecutive n of one row m;
+//   * workgroup tile BM x BN (128 x 128; 64 x 64 when the problem has too
+//     few 128 x 128 tiles to occupy the GPU; 32 x 32 when it has too few of
+//     those), K step 32, 4 waves in a 2 x 2 grid; each wave computes Y^T
+//     blocks (A operand = B^T, B operand = A^T) so each lane holds 4
+//     consecutive n of one row m;
 //   * per 16-deep k group a wave reads its A^T operand as one 128-bit LDS read
 //     per 16 rows (4 consecutive k, one per MFMA) and its B^T operand as 32-bit
 //     reads; fp32 MFMA takes one k per lane, so no transpose is needed;
@@ -32,9 +33,18 @@ __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
 // distinct 16-byte slots of a 256-byte window (8 of a 128-byte one).
 // B tile: 32 rows of BN floats (BN / 4 chunks); chunk c of row k at slot
 // c ^ 4 ((k >> 2) & 3): the 32-bit reads of one MFMA (rows k, k+4, k+8, k+12,
-// 16 consecutive n each) land in 4 disjoint 64-byte segments.
+// 16 consecutive n each) land in 4 disjoint 64-byte segments.  With 32-float
+// rows (BN = 32) only two 64-byte segments fit in a row, so c ^ 4 ((k >> 2) &
+// 1) and the rows k and k+8 share banks (a 2-way conflict the small
+// problems that use this tile can afford).
 __device__ __forceinline__ int swzA(int m) { return ((m >> 1) & 7) ^ ((m & 1) << 2); }
-__device__ __forceinline__ int swzB(int k) { return ((k >> 2) & 3) << 2; }
+template <int BN>
+__device__ __forceinline__ int swzB(int k) {
+  if constexpr (BN >= 64)
+    return ((k >> 2) & 3) << 2;
+  else
+    return ((k >> 2) & 1) << 2;
+}
 
 template <int BM, int BN>
 struct Cfg {
@@ -64,7 +74,7 @@ __device__ __forceinline__ void fill_dma(const GemmParams& p, int m0, int n0, in
   for (int j = 0; j < C::B_BLOCKS / 4; ++j) {
     const int blk = wu * (C::B_BLOCKS / 4) + j;
     const int row = blk * C::B_ROWS_PER_BLOCK + lane / C::B_CHUNKS;
-    const int c = (lane % C::B_CHUNKS) ^ swzB(row);
+    const int c = (lane % C::B_CHUNKS) ^ swzB<BN>(row);
     const int gn = min(n0 + c * 4, nlast);
     dma16(B + (int64_t)(k0 + row) * p.ldb + gn, lds_addr(sb) + blk * 1024);
   }
@@ -97,7 +107,7 @@ __device__ __forceinline__ void fill_tail(const GemmParams& p, int m0, int n0, i
   for (int j = 0; j < C::B_BLOCKS / 4; ++j) {
     const int blk = w * (C::B_BLOCKS / 4) + j;
     const int row = blk * C::B_ROWS_PER_BLOCK + lane / C::B_CHUNKS;
-    const int c = (lane % C::B_CHUNKS) ^ swzB(row);
+    const int c = (lane % C::B_CHUNKS) ^ swzB<BN>(row);
     const int gn = min(n0 + c * 4, nlast);
     f32x4 v = (f32x4){0.f, 0.f, 0.f, 0.f};
     if (k0 + row < p.K) v = *(const f32x4*)(B + (int64_t)(k0 + row) * p.ldb + gn);
@@ -130,7 +140,7 @@ __device__ __forceinline__ void compute_stage(const float* sa, const float* sb, 
 #pragma unroll
       for (int t = 0; t < C::NT; ++t) {
         const int n = wn * C::WN + 16 * t + q;
-        bt[t] = sb[k * BN + ((((n >> 2) ^ swzB(k))) << 2) + (n & 3)];
+        bt[t] = sb[k * BN + ((((n >> 2) ^ swzB<BN>(k))) << 2) + (n & 3)];
       }
 #pragma unroll
       for (int t = 0; t < C::NT; ++t)
@@ -249,12 +259,16 @@ hipError_t launch_act(GemmParams p, int act, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_gemm32(GemmParams p, int act, hipStream_t stream, int num_cus) {
-  // 128 x 128 tiles when they give at least one workgroup per CU, else 64 x 64.
-  // (variant 1 / 2 force one of them: an autotuning knob)
+  // 128 x 128 tiles when they give at least one workgroup per CU, else 64 x 64
+  // when those do, else 32 x 32 (variant 1 / 2 / 3 force one of them: an
+  // autotuning knob)
   const long tiles128 = (long)((p.M + 127) / 128) * ((p.N + 127) / 128);
-  const bool big = p.variant == 1 || (p.variant == 0 && tiles128 >= num_cus);
-  if (big) return launch_act<128, 128>(p, act, stream);
-  return launch_act<64, 64>(p, act, stream);
+  const long tiles64 = (long)((p.M + 63) / 64) * ((p.N + 63) / 64);
+  int v = p.variant;
+  if (v == 0) v = tiles128 >= num_cus ? 1 : tiles64 >= num_cus ? 2 : 3;
+  if (v == 1) return launch_act<128, 128>(p, act, stream);
+  if (v == 2) return launch_act<64, 64>(p, act, stream);
+  return launch_act<32, 32>(p, act, stream);
 }
 
 }  // namespace coalesce
