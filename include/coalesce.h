@@ -279,7 +279,8 @@ typedef struct {
   float best_us;       /* mean launch time of the chosen one */
   int32_t grid;        /* the chosen workgroup count (0: the launcher's default) */
   int32_t group_m;     /* the chosen tile-group height (0: default) */
-  int32_t variant;     /* FP32 GEMM tile shape: 0 heuristic, 1 = 128 x 128, 2 = 64 x 64, 3 = 32 x 32 */
+  int32_t variant;     /* FP32 GEMM tile shape: 0 heuristic, 1 = 128 x 128, 2 = 64 x 64, 3 = 32 x 32,
+                          4 = 64 x 32 */
 } coalesce_tune_report;
 
 coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb,

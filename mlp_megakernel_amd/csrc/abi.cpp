@@ -762,7 +762,7 @@ coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, cons
   std::vector<TuneCfg> cands;
   cands.push_back(dflt);
   if (in_dtype == COALESCE_F32) {
-    for (int variant : {1, 2, 3})
+    for (int variant : {1, 2, 3, 4})
       for (int gm : {4, 8, 16}) add_unique(cands, TuneCfg{0, gm, variant});
   } else {
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);

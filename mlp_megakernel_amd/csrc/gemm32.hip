@@ -2,11 +2,10 @@
 //
 // Same method as the 16-bit kernel (bias and activation applied to the fp32
 // accumulators in registers, one store of Y), on v_mfma_f32_16x16x4_f32:
-//   * workgroup tile BM x BN (128 x 128; 64 x 64 when the problem has too
-//     few 128 x 128 tiles to occupy the GPU; 32 x 32 when it has too few of
-//     those), K step 32, 4 waves in a 2 x 2 grid; each wave computes Y^T
-//     blocks (A operand = B^T, B operand = A^T) so each lane holds 4
-//     consecutive n of one row m;
+//   * workgroup tile BM x BN (128 x 128; 64 x 64, 64 x 32 or 32 x 32 when the
+//     problem has too few larger tiles to occupy the GPU), K step 32, 4 waves
+//     in a 2 x 2 grid; each wave computes Y^T blocks (A operand = B^T,
+//     B operand = A^T) so each lane holds 4 consecutive n of one row m;
 //   * per 16-deep k group a wave reads its A^T operand as one 128-bit LDS read
 //     per 16 rows (4 consecutive k, one per MFMA) and its B^T operand as 32-bit
 //     reads; fp32 MFMA takes one k per lane, so no transpose is needed;
@@ -259,15 +258,19 @@ hipError_t launch_act(GemmParams p, int act, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_gemm32(GemmParams p, int act, hipStream_t stream, int num_cus) {
-  // 128 x 128 tiles when they give at least one workgroup per CU, else 64 x 64
-  // when those do, else 32 x 32 (variant 1 / 2 / 3 force one of them: an
-  // autotuning knob)
+  // 128 x 128 tiles when they give at least one workgroup per CU; else 64 x 64
+  // when those give two; else 64 x 32 when those give one; else 32 x 32
+  // (measured: 1024^3 runs 5 % faster on 64 x 32 than on 64 x 64, 512^3 best
+  // on 32 x 32).  Variant 1 / 2 / 3 / 4 forces 128 x 128 / 64 x 64 / 32 x 32
+  // / 64 x 32: an autotuning knob.
   const long tiles128 = (long)((p.M + 127) / 128) * ((p.N + 127) / 128);
   const long tiles64 = (long)((p.M + 63) / 64) * ((p.N + 63) / 64);
+  const long tiles6432 = (long)((p.M + 63) / 64) * ((p.N + 31) / 32);
   int v = p.variant;
-  if (v == 0) v = tiles128 >= num_cus ? 1 : tiles64 >= num_cus ? 2 : 3;
+  if (v == 0) v = tiles128 >= num_cus ? 1 : tiles64 >= 2L * num_cus ? 2 : tiles6432 >= num_cus ? 4 : 3;
   if (v == 1) return launch_act<128, 128>(p, act, stream);
   if (v == 2) return launch_act<64, 64>(p, act, stream);
+  if (v == 4) return launch_act<64, 32>(p, act, stream);
   return launch_act<32, 32>(p, act, stream);
 }
 
