@@ -53,6 +53,9 @@ METRIC = "fused GEMM+bias+GELU TFLOP/s & % MFMA peak; MLP megakernel rows/sec"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+# transcendental (v_exp_f32 / v_log_f32) rate: a quarter of the fp32 vector
+# lane rate of 78.6e12 per second (256 CUs x 4 SIMDs x 32 lanes x 2.4 GHz)
+PEAK_TRANS_PER_S = 78.6e12 / 4
 FLUSH_BYTES = 512 << 20
 
 
@@ -254,12 +257,17 @@ def main():
 
     def roofline_mlp(w, mean_ms):
         by = w.bytes()
+        trans = 2.0 * w.M * sum(w.dims[1:-1])
         ach = by / (mean_ms * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": measured_traffic("mlp_kernel/" + w.name),
                 "kernel": "mlp_kernel",
                 "algorithmic_bytes_per_launch": by, "algorithmic_flop_per_launch": w.flops(),
-                "mfma_tflops": round(w.flops() / (mean_ms * 1e-3) / 1e12, 2), "mean_launch_ms": round(mean_ms, 5)}
+                "mfma_tflops": round(w.flops() / (mean_ms * 1e-3) / 1e12, 2), "mean_launch_ms": round(mean_ms, 5),
+                # the co-bound: two transcendentals (exp2, log2) per hidden unit and row
+                "valu": {"bound": "alu", "achieved": round(trans / (mean_ms * 1e-3) / 1e12, 3),
+                         "peak": round(PEAK_TRANS_PER_S / 1e12, 3), "unit": "T transcendentals/s",
+                         "frac": round(trans / (mean_ms * 1e-3) / PEAK_TRANS_PER_S, 4)}}
 
     result = {}
     prim = datagen.WORKLOADS[args.workload]
