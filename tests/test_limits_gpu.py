@@ -47,13 +47,16 @@ def _sample_rows(M, n, last, seed):
     return np.unique(np.concatenate([rng.integers(0, M, n), np.arange(M - last, M)]))
 
 
-def test_gemm_operand_beyond_4gib():
+@pytest.mark.parametrize("name", ["bf16_ffn_up_gelu", "fp32_gemm_gelu_512"])
+def test_gemm_operand_beyond_4gib(name):
+    w = datagen.WORKLOADS[name]
     P, N, K = 1000, 320, 1152
-    M = (1 << 21) + 300  # A spans 4.8 GB; the last rows start past 2^32 bytes
-    A, B, bias = datagen.gemm_inputs(datagen.BF16_FFN, M=P, N=N, K=K)
-    progress("gemm bf16 M=%d N=%d K=%d (A %.1f GB)" % (M, N, K, M * K * 2 / 1e9))
+    A, B, bias = datagen.gemm_inputs(w, M=P, N=N, K=K)
+    es = A.element_size()
+    M = (1 << 22) // es + 300  # A spans 4.8 GB; the last rows start past 2^32 bytes
+    progress("gemm %s M=%d N=%d K=%d (A %.1f GB)" % (name, M, N, K, M * K * es / 1e9))
     Ag = _periodic(A, M)
-    assert Ag.numel() * Ag.element_size() > GIB4
+    assert Ag.numel() * es > GIB4
     Y = mk.gemm_bias_act(Ag, B.to("cuda"), bias.to("cuda"), act="gelu")
     torch.cuda.synchronize()
     del Ag
@@ -64,7 +67,7 @@ def test_gemm_operand_beyond_4gib():
     rows = _sample_rows(M, 512, 300, 11)
     ref = oracle.gemm_bias_act(f64(A)[rows % P], f64(B), f64(bias), act="gelu")
     got = f64(Y[torch.from_numpy(rows).to("cuda")])
-    assert_close(got, ref, TOL[torch.bfloat16], "rows of a 4.8 GB A")
+    assert_close(got, ref, TOL[A.dtype], "rows of a 4.8 GB A (%s)" % name)
 
 
 def test_gemm_maximum_pitches():
