@@ -85,8 +85,16 @@ def _check(status: int):
                                                 lib.coalesce_last_error().decode()))
 
 
+# The current stream's raw handle without building a torch.cuda.Stream object
+# (that costs about 2.7 us a call, a third of the binding's host time on a
+# small launch); torch.cuda.current_stream() where this torch lacks the hook.
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
+        if _raw_current_stream is not None:
+            return _raw_current_stream(torch.cuda.current_device())
         stream = torch.cuda.current_stream()
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
@@ -99,14 +107,16 @@ def _ptr(t: Optional[torch.Tensor]):
 
 def _matrix(t: torch.Tensor, name: str):
     """(rows, cols, ld) of a 2-D device tensor with unit inner stride."""
-    if t.dim() != 2:
+    shape = t.shape
+    if len(shape) != 2:
         raise ValueError("%s must be 2-D" % name)
     if not t.is_cuda:
         raise ValueError("%s must be on the GPU" % name)
-    rows, cols = t.shape
-    if cols > 1 and t.stride(1) != 1:
+    rows, cols = shape
+    st = t.stride()
+    if cols > 1 and st[1] != 1:
         raise ValueError("%s must have unit inner stride (row-major)" % name)
-    ld = t.stride(0) if rows > 1 else max(t.stride(0), cols)
+    ld = st[0] if rows > 1 else max(st[0], cols)
     return rows, cols, ld
 
 
@@ -156,17 +166,41 @@ def _gemm_args(A, B, bias, out_dtype, out):
 def _chain_dims(x: torch.Tensor, weights: Sequence[torch.Tensor]):
     M, D0, ldx = _matrix(x, "x")
     dims = [D0]
+    xdt = x.dtype
     for i, w in enumerate(weights):
-        if w.dim() != 2 or not w.is_contiguous() or w.dtype != x.dtype or not w.is_cuda:
+        shape = w.shape
+        if len(shape) != 2 or w.dtype != xdt or not w.is_cuda or not w.is_contiguous():
             raise ValueError("weight %d must be a contiguous 2-D device tensor of x's dtype" % i)
-        if w.shape[0] != dims[-1]:
+        if shape[0] != dims[-1]:
             raise ValueError("layer widths do not chain")
-        dims.append(w.shape[1])
+        dims.append(shape[1])
     return M, ldx, dims
 
 
+# Host arrays of pointers and widths, cached by their values: building a
+# ctypes array costs about a microsecond, which matters when a small launch
+# is bound by the host.  The arrays hold only the values they are keyed by.
+_array_cache = {}
+
+
+def _c_array(ctype, values: tuple):
+    key = (ctype, values)
+    arr = _array_cache.get(key)
+    if arr is None:
+        if len(_array_cache) >= 512:
+            _array_cache.clear()
+        # the cast keeps a reference to the array it points into
+        arr = ctypes.cast((ctype * max(len(values), 1))(*values), ctypes.c_void_p)
+        _array_cache[key] = arr
+    return arr
+
+
 def _ptr_array(ts):
-    return ctypes.cast((ctypes.c_void_p * max(len(ts), 1))(*[t.data_ptr() for t in ts]), ctypes.c_void_p)
+    return _c_array(ctypes.c_void_p, tuple([t.data_ptr() for t in ts]))
+
+
+def _dims_array(dims):
+    return _c_array(ctypes.c_int64, tuple(dims))
 
 
 def mlp_forward(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_act="softplus",
@@ -180,10 +214,7 @@ def mlp_forward(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_act="so
     Mo, Do, ldo = _matrix(out, "out")
     if (Mo, Do) != (M, dims[-1]):
         raise ValueError("out must be M x dims[L]")
-    wp = (ctypes.c_void_p * max(L, 1))(*[w.data_ptr() for w in weights])
-    dp = (ctypes.c_int64 * (L + 1))(*dims)
-    _check(lib.coalesce_mlp_forward_grid(_ptr(x), ldx, ctypes.cast(wp, ctypes.c_void_p),
-                                         ctypes.cast(dp, ctypes.c_void_p), L, _ptr(out), ldo, M,
+    _check(lib.coalesce_mlp_forward_grid(_ptr(x), ldx, _ptr_array(weights), _dims_array(dims), L, _ptr(out), ldo, M,
                                          _DTYPES[x.dtype], _ACTS[hidden_act], int(num_workgroups), _stream(stream)))
     return out
 
@@ -220,8 +251,7 @@ def mlp_forward_train(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_a
     if len(acts) != L - 1:
         raise ValueError("need L - 1 activation buffers")
     lda = _acts_pitch(acts, M, dims)
-    dp = (ctypes.c_int64 * (L + 1))(*dims)
-    _check(lib.coalesce_mlp_forward_train(_ptr(x), ldx, _ptr_array(weights), ctypes.cast(dp, ctypes.c_void_p), L,
+    _check(lib.coalesce_mlp_forward_train(_ptr(x), ldx, _ptr_array(weights), _dims_array(dims), L,
                                           _ptr(out), ldo, _ptr_array(acts) if L > 1 else None, lda, M,
                                           _DTYPES[x.dtype], _ACTS[hidden_act], _stream(stream)))
     return out, list(acts)
@@ -230,8 +260,7 @@ def mlp_forward_train(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_a
 def mlp_backward_workspace_size(dims: Sequence[int]) -> int:
     """Bytes of workspace coalesce_mlp_backward needs for this chain here."""
     L = len(dims) - 1
-    dp = (ctypes.c_int64 * (L + 1))(*dims)
-    n = int(load_library().coalesce_mlp_backward_workspace_size(ctypes.cast(dp, ctypes.c_void_p), L))
+    n = int(load_library().coalesce_mlp_backward_workspace_size(_dims_array(dims), L))
     if n == 0:
         raise CoalesceError(ERR_UNSUPPORTED, "no backward for dims %s on this device" % (list(dims),))
     return n
@@ -270,8 +299,7 @@ def mlp_backward(x: torch.Tensor, weights: Sequence[torch.Tensor], acts: Sequenc
     need = mlp_backward_workspace_size(dims)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    dp = (ctypes.c_int64 * (L + 1))(*dims)
-    _check(lib.coalesce_mlp_backward(_ptr(x), ldx, _ptr_array(weights), ctypes.cast(dp, ctypes.c_void_p), L,
+    _check(lib.coalesce_mlp_backward(_ptr(x), ldx, _ptr_array(weights), _dims_array(dims), L,
                                      _ptr_array(acts) if L > 1 else None, lda, _ptr(dout), ldd, _ptr_array(dW),
                                      _ptr(dx), ldq, M, _DTYPES[x.dtype], _ACTS[hidden_act], _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)))
@@ -304,8 +332,7 @@ def weight_norm(vs: Sequence[torch.Tensor], gs: Sequence[torch.Tensor], Ws: Opti
     for W, v in zip(Ws, vs):
         if W.shape != v.shape or W.dtype != v.dtype or not W.is_contiguous():
             raise ValueError("every W must be a contiguous tensor shaped like its v")
-    dp = (ctypes.c_int64 * len(dims))(*dims)
-    _check(lib.coalesce_weight_norm(_ptr_array(vs), _ptr_array(gs), _ptr_array(Ws), ctypes.cast(dp, ctypes.c_void_p),
+    _check(lib.coalesce_weight_norm(_ptr_array(vs), _ptr_array(gs), _ptr_array(Ws), _dims_array(dims),
                                     len(vs), F16, _stream(stream)))
     return list(Ws)
 
@@ -321,9 +348,8 @@ def weight_norm_backward(vs: Sequence[torch.Tensor], gs: Sequence[torch.Tensor],
             raise ValueError("dW[%d] must be a contiguous float32 tensor shaped like v[%d]" % (i, i))
     dvs = [torch.empty(v.shape, dtype=torch.float32, device=v.device) for v in vs]
     dgs = [torch.empty(g.shape, dtype=torch.float32, device=g.device) for g in gs]
-    dp = (ctypes.c_int64 * len(dims))(*dims)
     _check(lib.coalesce_weight_norm_backward(_ptr_array(vs), _ptr_array(gs), _ptr_array(dWs), _ptr_array(dvs),
-                                             _ptr_array(dgs), ctypes.cast(dp, ctypes.c_void_p), len(vs), F16,
+                                             _ptr_array(dgs), _dims_array(dims), len(vs), F16,
                                              _stream(stream)))
     return dvs, dgs
 
@@ -374,8 +400,7 @@ def autotune_mlp_forward(x: torch.Tensor, weights: Sequence[torch.Tensor], hidde
         raise ValueError("out must be M x dims[L]")
     ws = _tune_workspace(M, dims[-1] * out.element_size(), x.device)
     rep = TuneReport()
-    dp = (ctypes.c_int64 * (L + 1))(*dims)
-    _check(lib.coalesce_autotune_mlp_forward(_ptr(x), ldx, _ptr_array(weights), ctypes.cast(dp, ctypes.c_void_p), L,
+    _check(lib.coalesce_autotune_mlp_forward(_ptr(x), ldx, _ptr_array(weights), _dims_array(dims), L,
                                              _ptr(out), ldo, M, _DTYPES[x.dtype], _ACTS[hidden_act], int(iters),
                                              _ptr(ws), ws.numel(), ctypes.byref(rep), _stream(stream)))
     return out, rep.as_dict()
