@@ -253,9 +253,9 @@ coalesce_status coalesce_flush_caches(const void* buf, size_t bytes, void* sink,
  * and post-tune correctness validation).  An autotune call takes the same
  * arguments as the entry point it tunes and computes the same output; it
  * runs every candidate launch configuration `iters` times on the caller's
- * data (the persistent grid size and the tile-group order of the bf16/fp16
- * GEMM, the tile shape and group order of the FP32 GEMM, the grid size of
- * the MLP megakernel), keeps the fastest whose output equals the default
+ * data (the tile shape, persistent grid size and tile-group order of the
+ * bf16/fp16 GEMM, the tile shape and group order of the FP32 GEMM, the grid
+ * size of the MLP megakernel), keeps the fastest whose output equals the default
  * configuration's bit for bit (every candidate performs the same arithmetic
  * per output element, so equality is the exact test; the default is kept
  * unless a candidate is more than 1 % faster), and records it: later
@@ -279,8 +279,9 @@ typedef struct {
   float best_us;       /* mean launch time of the chosen one */
   int32_t grid;        /* the chosen workgroup count (0: the launcher's default) */
   int32_t group_m;     /* the chosen tile-group height (0: default) */
-  int32_t variant;     /* FP32 GEMM tile shape: 0 heuristic, 1 = 128 x 128, 2 = 64 x 64, 3 = 32 x 32,
-                          4 = 64 x 32 */
+  int32_t variant;     /* GEMM tile shape, 0 = the launcher's heuristic.  FP32: 1 = 128 x 128,
+                          2 = 64 x 64, 3 = 32 x 32, 4 = 64 x 32; bf16 / fp16: 1 = 256 x 256,
+                          2 = 128 x 128 */
 } coalesce_tune_report;
 
 coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb,

@@ -765,12 +765,18 @@ coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, cons
     for (int variant : {1, 2, 3, 4})
       for (int gm : {4, 8, 16}) add_unique(cands, TuneCfg{0, gm, variant});
   } else {
-    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    std::vector<int> grids = {0, cus / 2, (3 * cus) / 4};
-    if (tiles <= 4 * (int64_t)cus) grids.push_back((int)tiles);
-    for (int g : grids)
-      for (int gm : {4, 8, 16})
-        if (g >= 0 && g <= tiles) add_unique(cands, TuneCfg{g, gm, 0});
+    // both tile shapes (1 = 256 x 256, one workgroup per CU; 2 = 128 x 128,
+    // two), each with persistent grids of all, half and three quarters of
+    // its workgroup slots, or one workgroup per tile
+    for (int variant : {1, 2}) {
+      const int64_t bt = variant == 1 ? 256 : 128, slots = (int64_t)cus * (variant == 1 ? 1 : 2);
+      const int64_t tiles = ((M + bt - 1) / bt) * ((N + bt - 1) / bt);
+      std::vector<int64_t> grids = {0, slots / 2, (3 * slots) / 4};
+      if (tiles <= 4 * slots) grids.push_back(tiles);
+      for (int64_t g : grids)
+        for (int gm : {4, 8, 16})
+          if (g >= 0 && g <= tiles) add_unique(cands, TuneCfg{(int)g, gm, variant});
+    }
   }
   const std::string key = gemm_key(current_device(), M, N, K, in_dtype, out_dtype, act, bias != nullptr);
   return tune(
