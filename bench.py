@@ -28,6 +28,7 @@ TFLOP/s.  The same line carries
     forward, backward, normalisation backward);
   * variants: two non-square chains (forward with its HBM roofline, and one
     training step), the FFN GEMM with the ReLU / softplus / no epilogue, the
+    bf16 GEMM + bias + GELU at five smaller sizes (1024^3 to 4096^3), the
     3 x 128 MLP with ReLU / no hidden activation, and the 3 x 128 MLP on small
     batches, launched eagerly and replayed from a HIP graph;
   * autotune: the ordinary entry points timed before and after per-shape
@@ -463,6 +464,23 @@ def main():
                         "frac_of_peak": round(g.flops() / (ev * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
         var["bf16_ffn_up_epilogues"] = epi
         del A, B, bias, Y
+        torch.cuda.empty_cache()
+        # the 16-bit GEMM (bias + GELU) at smaller sizes, where the launcher
+        # takes 128 x 128 tiles while all of them fit on the CUs at once
+        sizes = {}
+        for (M, N, K) in ((1024, 1024, 1024), (2048, 2048, 2048), (4096, 2048, 4096), (3072, 3072, 4096),
+                          (4096, 4096, 4096)):
+            print("bench: bf16 GEMM %dx%dx%d" % (M, N, K), file=sys.stderr, flush=True)
+            A, B, bias = datagen.gemm_inputs(g, M=M, N=N, K=K)
+            A, B, bias = A.to(dev), B.to(dev), bias.to(dev)
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            _, ev = timed_steps(lambda: mk.gemm_bias_act(A, B, bias, act="gelu", out=Y), max(20, args.steps), 5)
+            fl = 2.0 * M * N * K
+            sizes["%dx%dx%d" % (M, N, K)] = {"mean_launch_ms": round(ev, 5), "tflops": round(fl / (ev * 1e-3) / 1e12, 1),
+                                             "frac_of_peak": round(fl / (ev * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4),
+                                             "tiles_128": ((M + 127) // 128) * ((N + 127) // 128)}
+            del A, B, bias, Y
+        var["bf16_gemm_sizes"] = sizes
         torch.cuda.empty_cache()
         # the 3 x 128 MLP with the other hidden activations
         x, Ws = datagen.mlp_inputs(datagen.MLP3)
