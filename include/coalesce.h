@@ -281,7 +281,7 @@ typedef struct {
   int32_t group_m;     /* the chosen tile-group height (0: default) */
   int32_t variant;     /* GEMM tile shape, 0 = the launcher's heuristic.  FP32: 1 = 128 x 128,
                           2 = 64 x 64, 3 = 32 x 32, 4 = 64 x 32; bf16 / fp16: 1 = 256 x 256,
-                          2 = 128 x 128 */
+                          2 = 128 x 128, 3 = 64 x 64 */
 } coalesce_tune_report;
 
 coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb,

@@ -765,11 +765,12 @@ coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, cons
     for (int variant : {1, 2, 3, 4})
       for (int gm : {4, 8, 16}) add_unique(cands, TuneCfg{0, gm, variant});
   } else {
-    // both tile shapes (1 = 256 x 256, one workgroup per CU; 2 = 128 x 128,
-    // two), each with persistent grids of all, half and three quarters of
-    // its workgroup slots, or one workgroup per tile
-    for (int variant : {1, 2}) {
-      const int64_t bt = variant == 1 ? 256 : 128, slots = (int64_t)cus * (variant == 1 ? 1 : 2);
+    // every tile shape (1 = 256 x 256, one workgroup per CU; 2 = 128 x 128,
+    // two; 3 = 64 x 64, four), each with persistent grids of all, half and
+    // three quarters of its workgroup slots, or one workgroup per tile
+    for (int variant : {1, 2, 3}) {
+      const int64_t bt = variant == 1 ? 256 : variant == 2 ? 128 : 64;
+      const int64_t slots = (int64_t)cus * (variant == 1 ? 1 : variant == 2 ? 2 : 4);
       const int64_t tiles = ((M + bt - 1) / bt) * ((N + bt - 1) / bt);
       std::vector<int64_t> grids = {0, slots / 2, (3 * slots) / 4};
       if (tiles <= 4 * slots) grids.push_back(tiles);

@@ -53,6 +53,9 @@ constexpr int BK = 64;
 //     (64 KB of LDS each), again two waves per SIMD.  Four times the tiles of
 //     the 256 x 256 plan, for problems whose 256 x 256 tiles would leave CUs
 //     idle; it moves twice the operand bytes per flop.
+//   * 64 x 64, 4 waves of 32 x 32: four workgroups per CU (32 KB of LDS
+//     each), four waves per SIMD, for problems whose 128 x 128 tiles would
+//     still leave most CUs idle.
 //   * 256 x 256, 4 waves of 128 x 128 (one wave per SIMD, 256 accumulators):
 //     compiled for measurements only.
 // MINW is the launch-bounds floor of waves per SIMD, which caps the registers
@@ -69,12 +72,13 @@ struct Geo {
   static constexpr int CA = BM / 8 / NW;    // 1 KB A copies per wave per K step (8 rows of 64 k each)
   static constexpr int CB = BN / 8 / NW;    // 1 KB B copies per wave per K step
   static constexpr int CPRB = BN / 8;       // 16-byte chunks per B row
-  static constexpr int CPRB_LOG = CPRB == 32 ? 5 : 4;
+  static constexpr int CPRB_LOG = CPRB == 32 ? 5 : CPRB == 16 ? 4 : 3;
   static constexpr int BRPC = 64 / CPRB;    // B rows (k) per 1 KB copy
   static_assert((1 << CPRB_LOG) == CPRB && BRPC * CPRB == 64 && CA * NW * 8 == BM && CB * NW * BRPC == BK, "copy plan does not cover the tile");
 };
 typedef Geo<256, 256, 8, 1> Geo256;
 typedef Geo<128, 128, 4, 2> Geo128;
+typedef Geo<64, 64, 4, 4> Geo64;
 typedef Geo<256, 256, 4, 1> Geo256w4;
 
 // LDS layouts, 16-byte chunks XOR-swizzled so that every fragment read is
@@ -83,15 +87,22 @@ typedef Geo<256, 256, 4, 1> Geo256w4;
 //     c ^ swzA(m).  A 128-bit read by 16 lanes (rows m0..m0+15, one chunk)
 //     hits 16 distinct 16-byte slots of a 256-byte window, and any 8
 //     consecutive rows hit 8 distinct slots of a 128-byte window.
-//   B tile: 64 rows of BN n (512 or 256 B = 32 or 16 chunks); chunk c of row
-//     k sits at slot c ^ swzB(k) (swzB < 16, so a chunk stays in its 256-byte
-//     half of a row).  A transposing read by 32 lanes (rows k0..k0+3 and
-//     k0+8..k0+11, two chunks, two 8-byte halves) hits 32 distinct 8-byte
-//     slots of a 256-byte window.
+//   B tile: 64 rows of BN n (512, 256 or 128 B = 32, 16 or 8 chunks); chunk c
+//     of row k sits at slot c ^ swzB(k) (below the row's chunk count, and
+//     below 16, so a chunk stays in its 256-byte part of a row).  A
+//     transposing read by 32 lanes (rows k0..k0+3 and k0+8..k0+11, two chunks,
+//     two 8-byte halves) hits 32 distinct 8-byte slots of a 256-byte window
+//     (which holds two rows when they are 128 bytes long).
 // Neither swizzle depends on the sub-tile index s, the slice ks or the half of
 // a transposing read, so those stay immediate offsets of the LDS reads.
 __device__ __forceinline__ int swzA(int m) { return ((m >> 1) & 7) ^ ((m & 1) << 2); }
-__device__ __forceinline__ int swzB(int k) { return ((k & 3) << 1) | (((k >> 3) & 1) << 3); }
+template <typename G>
+__device__ __forceinline__ int swzB(int k) {
+  if constexpr (G::CPRB >= 16)
+    return ((k & 3) << 1) | (((k >> 3) & 1) << 3);
+  else  // 128-byte rows: a 256-byte window holds two rows, k and k ^ 1
+    return (((k >> 1) & 1) << 1) | (((k >> 3) & 1) << 2);
+}
 
 template <typename T>
 struct Stage {
@@ -129,7 +140,7 @@ __device__ __forceinline__ uint32_t dma_offset(const DmaPlan& d, int j) {
     const uint32_t ldb_b = (uint32_t)p.ldb * (uint32_t)sizeof(T);
     const int nlast = ((p.N - 1) >> 3) << 3;
     const int row = (d.w * G::CB + j - G::CA) * G::BRPC + (d.lane >> G::CPRB_LOG);
-    const int cB = (d.lane & (G::CPRB - 1)) ^ swzB(row);
+    const int cB = (d.lane & (G::CPRB - 1)) ^ swzB<G>(row);
     const int gn = min(d.n0 + cB * 8, nlast);
     return (uint32_t)row * ldb_b + (uint32_t)((gn - d.n0) * (int)sizeof(T));
   }
@@ -210,7 +221,7 @@ __device__ __forceinline__ void tail_fill(const GemmParams& p, int m0, int n0, i
 #pragma unroll
   for (int j = 0; j < G::CB; ++j) {
     const int row = (w * G::CB + j) * G::BRPC + (lane >> G::CPRB_LOG);
-    const int cB = (lane & (G::CPRB - 1)) ^ swzB(row);
+    const int cB = (lane & (G::CPRB - 1)) ^ swzB<G>(row);
     const int gn = min(n0 + cB * 8, nlast);
     i16x8 v = (i16x8){0, 0, 0, 0, 0, 0, 0, 0};
     if (k0 + row < p.K) v = *(const i16x8*)(B + (int64_t)(k0 + row) * p.ldb + gn);
@@ -244,7 +255,7 @@ __device__ __forceinline__ i16x4 read_af_half(Stage<T> st, int ks, int wn, int t
   const int q = lane & 15;
   const int n = wn * G::WN + 16 * t + 4 * (q & 3);
   const int k = 32 * ks + 8 * (lane >> 4) + 4 * half + (q >> 2);
-  return lds_read_tr16(st.b + k * G::BN + (((n >> 3) ^ swzB(k)) << 3) + (n & 7));
+  return lds_read_tr16(st.b + k * G::BN + (((n >> 3) ^ swzB<G>(k)) << 3) + (n & 7));
 }
 
 // One slice: NT groups of {2 copies of K step k + 2 when `copy` (a uniform
@@ -260,8 +271,9 @@ template <typename T, typename G>
 __device__ __forceinline__ void slice(const Frags<G>& cur, f32x4 (&acc)[G::NT][G::MT], Frags<G>& nxt, Stage<T> rst,
                                       int rks, int wm, int wn, int lane, bool copy, const DmaPlan& d, const void* ab,
                                       const void* bb, Stage<T> cst, int wu) {
-  static_assert(G::NT == 4 && (G::MT == 8 || G::MT == 4) && G::CA + G::CB == 2 * G::NT,
-                "the read plan assumes 4 x 8 or 4 x 4 sub-tiles and two copies per group");
+  static_assert(((G::NT == 4 && (G::MT == 8 || G::MT == 4)) || (G::NT == 2 && G::MT == 2)) &&
+                    G::CA + G::CB == 2 * G::NT,
+                "the read plan assumes 4 x 8, 4 x 4 or 2 x 2 sub-tiles and two copies per group");
   auto read_a = [&](int t) {
     const i16x4 lo = read_af_half<T, G>(rst, rks, wn, t, 0, lane);
     const i16x4 hi = read_af_half<T, G>(rst, rks, wn, t, 1, lane);
@@ -281,7 +293,7 @@ __device__ __forceinline__ void slice(const Frags<G>& cur, f32x4 (&acc)[G::NT][G
     if (t == 0) {
       read_a(0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) nxt.b[i] = read_bf<T, G>(rst, rks, wm, i, lane);
+      for (int i = 0; i < (G::MT < 4 ? G::MT : 4); ++i) nxt.b[i] = read_bf<T, G>(rst, rks, wm, i, lane);
     } else if (G::MT == 8) {
       if (t == 1) {
 #pragma unroll
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(G::THREADS, G::MINW) void gemm16_kernel(GemmParams 
     // stages are free once every wave is past its last fragment read) and
     // stores it as full rows.
     const int wr0 = m0 + wm * G::WM, wc0 = n0 + wn * G::WN;
-    constexpr bool STAGE = sizeof(TO) == 2;
+    constexpr bool STAGE = sizeof(TO) == 2 && G::WN >= 64;  // staging needs 128-byte rows
     const bool staged = STAGE && wr0 + G::WM <= p.M && wc0 + G::WN <= p.N;
     __syncthreads();
     if (staged) {
@@ -580,12 +592,13 @@ hipError_t launch_bias(const GemmParams& p, hipStream_t stream, int num_cus) {
   return launch_cfg<T, TO, ACT, false, G>(p, stream, num_cus);
 }
 
-// p.variant is resolved by launch_gemm16: 1 = 256 x 256, 2 = 128 x 128.
+// p.variant is resolved by launch_gemm16: 1 = 256 x 256, 2 = 128 x 128, 3 = 64 x 64.
 template <typename T, typename TO, int ACT>
 hipError_t launch_typed(const GemmParams& p, hipStream_t stream, int num_cus) {
 #ifdef GEMM16_WITH_W4
-  if (p.variant == 3) return launch_bias<T, TO, ACT, Geo256w4>(p, stream, num_cus);
+  if (p.variant == 4) return launch_bias<T, TO, ACT, Geo256w4>(p, stream, num_cus);
 #endif
+  if (p.variant == 3) return launch_bias<T, TO, ACT, Geo64>(p, stream, num_cus);
   if (p.variant == 2) return launch_bias<T, TO, ACT, Geo128>(p, stream, num_cus);
   return launch_bias<T, TO, ACT, Geo256>(p, stream, num_cus);
 }
@@ -603,16 +616,20 @@ hipError_t launch_act(const GemmParams& p, int act, hipStream_t stream, int num_
 }  // namespace
 
 hipError_t launch_gemm16(GemmParams p, DType in, DType out, int act, hipStream_t stream, int num_cus) {
-  // 128 x 128 tiles when all of them run at once (two workgroups per CU),
-  // else 256 x 256.  Measured, bf16 + bias + GELU: 128 x 128 is 1.3-2.2x
-  // faster on problems whose 128 x 128 tiles fit in one round (1024^3,
-  // 2048^2 x 8192, 4096 x 2048 x 4096, 16384 x 512 x 2048) and 0.82-0.86x on
-  // those that need more (3072^2 x 4096: 144 tiles of 256 x 256 but 576 of
-  // 128 x 128; 4096^2 x 4096), and the outputs are the same bits.  Variant
-  // 1 / 2 forces 256 x 256 / 128 x 128: an autotuning knob.
+  // 64 x 64 tiles while 128 x 128 ones would not give every CU one; 128 x 128
+  // while all of them run at once (two workgroups per CU); else 256 x 256.
+  // Measured, bf16 + bias + GELU, the outputs the same bits throughout:
+  // 128 x 128 is 1.3-2.2x faster than 256 x 256 on problems whose 128 x 128
+  // tiles fit in one round (1024^3, 2048^2 x 8192, 4096 x 2048 x 4096,
+  // 16384 x 512 x 2048) and 0.82-0.86x on those that need more (3072^2 x
+  // 4096: 144 tiles of 256 x 256 but 576 of 128 x 128; 4096^2 x 4096);
+  // 64 x 64 is 1.2-1.7x faster than 128 x 128 below one 128 x 128 tile per
+  // CU (512^3, 1024^3, 1024 x 2048 x 2048, 4096 x 512 x 1024) and even at
+  // one per CU (2048^3).  Variant 1 / 2 / 3 forces 256 x 256 / 128 x 128 /
+  // 64 x 64: an autotuning knob.
   if (p.variant == 0) {
     const long tiles128 = (long)((p.M + 127) / 128) * ((p.N + 127) / 128);
-    p.variant = tiles128 <= 2L * num_cus ? 2 : 1;
+    p.variant = tiles128 < num_cus ? 3 : tiles128 <= 2L * num_cus ? 2 : 1;
   }
   if (p.group_m <= 0) p.group_m = 8;
   if (in == DT_BF16) {

@@ -19,7 +19,7 @@ struct GemmParams {
   int group_m;        // tile rows per group of the tile order (0: the launcher's default)
   int grid_override;  // workgroups to launch (0: the launcher's default); persistent kernels walk the rest
   int variant;        // tile shape, 0 heuristic.  FP32: 1 = 128 x 128, 2 = 64 x 64, 3 = 32 x 32, 4 = 64 x 32;
-                      // bf16 / fp16: 1 = 256 x 256, 2 = 128 x 128
+                      // bf16 / fp16: 1 = 256 x 256, 2 = 128 x 128, 3 = 64 x 64
 };
 
 // Each launcher picks its tile configuration, fills tiles_* and launches on

@@ -217,11 +217,13 @@ def test_bf16_ffn_full_size():
 @pytest.mark.parametrize("in_dt,out_dt,act", [("bf16", "bf16", "gelu"), ("f16", "f32", "softplus"),
                                               ("bf16", "bf16", "none")])
 def test_tile_shapes_agree_bitwise(in_dt, out_dt, act):
-    # The 16-bit GEMM runs 128 x 128 tiles when all of them fit on the CUs at
-    # once and 256 x 256 tiles otherwise; both accumulate every output element
-    # in the same k order, so they must give the same bits.  The full problem
+    # The 16-bit GEMM runs 64 x 64 tiles while 128 x 128 ones number fewer
+    # than the CUs, 128 x 128 while all of them fit on the CUs at once (two
+    # per CU) and 256 x 256 otherwise; all accumulate every output element in
+    # the same k order, so they must give the same bits.  The full problem
     # (25 x 25 tiles of 128) takes 256 x 256 tiles with ragged edges in M, N
-    # and K; its first 300 rows alone (3 x 25 tiles of 128) take 128 x 128.
+    # and K; its first 1536 rows (12 x 25 tiles of 128) take 128 x 128, its
+    # first 300 rows (3 x 25) 64 x 64.
     w = datagen.BF16_FFN
     M, N, K = 3083, 3077, 200
     A, B, bias = datagen.gemm_inputs(w, M=M, N=N, K=K)
@@ -230,10 +232,11 @@ def test_tile_shapes_agree_bitwise(in_dt, out_dt, act):
     progress("tile shapes %s->%s %s M=%d N=%d K=%d" % (in_dt, out_dt, act, M, N, K))
     Ag, Bg, bg = to_gpu(A), to_gpu(B), bias.to("cuda")
     big = mk.gemm_bias_act(Ag, Bg, bg, act=act, out_dtype=DT[out_dt])
-    part = mk.gemm_bias_act(Ag[:300], Bg, bg, act=act, out_dtype=DT[out_dt])
-    torch.cuda.synchronize()
     view = torch.int16 if out_dt != "f32" else torch.int32
-    assert torch.equal(big[:300].contiguous().view(view), part.contiguous().view(view))
+    for rows in (1536, 300):
+        part = mk.gemm_bias_act(Ag[:rows], Bg, bg, act=act, out_dtype=DT[out_dt])
+        torch.cuda.synchronize()
+        assert torch.equal(big[:rows].contiguous().view(view), part.contiguous().view(view)), rows
     rows = np.array([0, 1, 299, 300, 1500, 2047, 3071, 3072, M - 1])
     ref = oracle.gemm_bias_act(f64(A), f64(B), f64(bias), act=act, rows=rows)
     assert_close(f64(big[torch.from_numpy(rows).to("cuda")]), ref, TOL[DT[in_dt]], "tile shapes")
