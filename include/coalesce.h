@@ -301,6 +301,16 @@ coalesce_status coalesce_autotune_clear(void);
 /* Number of compute units of the current device (cached per device). */
 int32_t coalesce_device_cu_count(void);
 
+/*
+ * Status reporting, after the status-checking helper of the vectorfold.studio
+ * GPU-compilation tutorial (every runtime call's status is checked and a
+ * failure is turned into a readable message naming the call):
+ * coalesce_status_string gives the enumerator's name for a status code
+ * (never NULL; "COALESCE_ERR_UNKNOWN" for a value outside the enum); coalesce_last_error gives
+ * the detail of the calling thread's last non-OK return ("" if there was
+ * none), valid until that thread's next call into the library.  Neither
+ * launches anything or touches the device.
+ */
 const char* coalesce_status_string(coalesce_status s);
 const char* coalesce_last_error(void);
 /* Library version, major * 10000 + minor * 100 + patch. */

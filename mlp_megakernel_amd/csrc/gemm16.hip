@@ -3,9 +3,10 @@
 // Y = act(A . B + bias) ("Coalesce" README, "Fusion study"): the bias add and
 // the activation run on the fp32 accumulators in registers and Y is written
 // once.  Tile plan (hand-budgeted against the 256 registers a lane has when
-// two waves share a SIMD), given for the 256 x 256 tile of large problems
-// (problems with fewer such tiles than CUs take 128 x 128 tiles, 4 waves of
-// 64 x 64, the same code at a smaller scale; see Geo):
+// two waves share a SIMD), given for the 256 x 256 tile of large problems;
+// smaller problems take 128 x 128 tiles (4 waves of 64 x 64) or 64 x 64
+// tiles (4 waves of 32 x 32), the same code at a smaller scale (see Geo and
+// the tile choice in launch_gemm16):
 //   * workgroup tile 256 (m) x 256 (n), K step 64, 8 waves in a 2 x 4 grid,
 //     each wave owning a 128 (m) x 64 (n) block of Y;
 //   * the wave computes Y^T blocks with v_mfma_f32_16x16x32 -- A operand =
@@ -234,7 +235,8 @@ __device__ __forceinline__ void tail_fill(const GemmParams& p, int m0, int n0, i
 }
 
 // Operand fragments of one 32-deep k slice (ks = 0 or 1 of a stage):
-//   b[s]: B operand = A^T, rows m = 128 wm + 16 s + (lane & 15), k = 8 (lane >> 4) + e;
+//   b[s]: B operand = A^T, rows m = WM wm + 16 s + (lane & 15), k = 8 (lane >> 4) + e
+//         (WM = 128 / 64 / 32 for the 256 / 128 / 64 tiles);
 //   a[t]: A operand = B^T, rows n = WN wn + 16 t + (lane & 15), same k, as two
 //         transposing reads of 4 k (lo: e = 0..3, hi: e = 4..7).
 template <typename G>
@@ -342,7 +344,9 @@ __device__ __forceinline__ void store4(TO* dst, f32x4 v, int valid) {
   }
 }
 
-// Epilogue through LDS for a wave's full 128 x WN block of a 16-bit Y.  The
+// Epilogue through LDS for a wave's full WM x WN block of a 16-bit Y (the
+// 256 x 256 and 128 x 128 tiles; the 64 x 64 tile stores from the
+// accumulators).  The
 // accumulator layout gives each lane 4 consecutive n of one row (8 bytes),
 // 32 contiguous bytes per row per store instruction; instead the wave writes
 // act(acc + bias), rounded, into its own LDS region (row-major, 16-byte
@@ -407,7 +411,8 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 #pragma clang diagnostic pop
 
 // Persistent kernel: the workgroups that fit on the CUs (one of 256 x 256,
-// whose two LDS stages take 128 KB, or two of 128 x 128) walk the tiles v = blockIdx.x, + gridDim.x, ...  Once a tile's Y stores
+// whose two LDS stages take 128 KB, two of 128 x 128, or four or five of
+// 64 x 64) walk the tiles v = blockIdx.x, + gridDim.x, ...  Once a tile's Y stores
 // are issued, the next tile's first two K steps are copied in without
 // waiting for them, so the copies' latency and the stores' drain overlap.
 // With gridDim.x a multiple of 8 a workgroup stays on one XCD, which is what
@@ -616,16 +621,17 @@ hipError_t launch_act(const GemmParams& p, int act, hipStream_t stream, int num_
 }  // namespace
 
 hipError_t launch_gemm16(GemmParams p, DType in, DType out, int act, hipStream_t stream, int num_cus) {
-  // 64 x 64 tiles while 128 x 128 ones would not give every CU one; 128 x 128
-  // while all of them run at once (two workgroups per CU); else 256 x 256.
-  // Measured, bf16 + bias + GELU, the outputs the same bits throughout:
-  // 128 x 128 is 1.3-2.2x faster than 256 x 256 on problems whose 128 x 128
-  // tiles fit in one round (1024^3, 2048^2 x 8192, 4096 x 2048 x 4096,
-  // 16384 x 512 x 2048) and 0.82-0.86x on those that need more (3072^2 x
-  // 4096: 144 tiles of 256 x 256 but 576 of 128 x 128; 4096^2 x 4096);
-  // 64 x 64 is 1.2-1.7x faster than 128 x 128 below one 128 x 128 tile per
-  // CU (512^3, 1024^3, 1024 x 2048 x 2048, 4096 x 512 x 1024) and even at
-  // one per CU (2048^3).  Variant 1 / 2 / 3 forces 256 x 256 / 128 x 128 /
+  // 64 x 64 tiles while 128 x 128 ones number fewer than the CUs; 128 x 128
+  // while all of them run at once (at most two workgroups per CU); else
+  // 256 x 256.  Measured, bf16 + bias + GELU, the outputs the same bits
+  // throughout: 128 x 128 is 1.3-2.2x faster than 256 x 256 on problems
+  // whose 128 x 128 tiles fit in one round (1024^3, 2048^2 x 8192, 4096 x
+  // 2048 x 4096, 16384 x 512 x 2048) and 0.82-0.86x on those that need more
+  // (3072^2 x 4096: 144 tiles of 256 x 256 but 576 of 128 x 128; 4096^2 x
+  // 4096); 64 x 64 is 1.2-1.7x faster than 128 x 128 below one 128 x 128
+  // tile per CU (512^3, 1024^3, 1024 x 2048 x 2048, 4096 x 512 x 1024) and
+  // level with it at exactly one per CU (2048^3: 611 against 591 TFLOP/s,
+  // within the run-to-run spread), where the threshold keeps 128 x 128.  Variant 1 / 2 / 3 forces 256 x 256 / 128 x 128 /
   // 64 x 64: an autotuning knob.
   if (p.variant == 0) {
     const long tiles128 = (long)((p.M + 127) / 128) * ((p.N + 127) / 128);

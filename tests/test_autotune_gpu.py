@@ -9,8 +9,8 @@ for bit: checked on the call that tunes, on later calls of the ordinary
 entry point (which now take the recorded configuration), after the record
 is cleared, and against the fp64 oracle on the exact integer and random
 cases.  The report must describe a search that happened: at least two
-candidates, the default among the valid ones, the chosen one no slower than
-the default.
+candidates, every one of them valid, the chosen one no slower than the
+default.
 """
 import numpy as np
 import pytest
@@ -34,8 +34,12 @@ def _fresh_cache():
 
 
 def _check_report(rep):
+    # every candidate is built to give the default's bits, so every one of
+    # them must be valid: a candidate that failed the bitwise check is a bug
+    # in that configuration (the persistent multi-tile paths of the smaller
+    # tile shapes run only through the reduced-grid candidates)
     assert rep["candidates"] >= 2, rep
-    assert 1 <= rep["valid"] <= rep["candidates"], rep
+    assert rep["valid"] == rep["candidates"], "a candidate configuration changed the output: %s" % rep
     assert 0 < rep["best_us"] <= rep["default_us"], rep
 
 

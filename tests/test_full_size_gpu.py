@@ -1,0 +1,97 @@
+"""Full-output parity at the workloads' own sizes, in the benchmark's launch
+configuration: every output element of every workload is compared with the
+fp64 oracle at the gate (max |y - o| / max(|o|, rms(o)) <= 1e-4 for fp32,
+2e-2 for bf16 / fp16), and the page's relative Frobenius norm is reported
+beside it ("Coalesce" README: "Kernel progression" and "Results / Fusion
+study" judge a kernel by its difference from a reference over the whole
+output).
+
+  * the fused GEMM + bias + GELU at 512^3 .. 4096^3 (fp32) and the bf16 FFN
+    up-projection (8192 x 4096 x 16384, 134M outputs);
+  * the softplus MLP megakernel: 3 x 128 on 2^20 rows, 5 x 64 on 2^22 rows
+    and the two non-square chains on 2^20 rows;
+  * the training pair at the two MLP workloads: the training forward's out and
+    every stored fp32 activation, the backward's dx and every weight gradient
+    (summed over all rows).
+
+The inputs are the workloads' own seeded inputs (no periodic or reduced
+stand-in).  The oracle runs on all host threads; the largest case (the FFN,
+5.5e11 fp64 multiply-adds) takes about 15 s on 16 cores.  The sampled
+full-size checks in the other test files stay as quick pre-checks.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import mlp_megakernel_amd as mk
+import oracle
+from helpers import assert_close, f64, progress
+from oracle.compare import rel_frobenius
+
+pytestmark = pytest.mark.gpu
+
+DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+TOL = {"f32": 1e-4, "bf16": 2e-2, "f16": 2e-2}
+
+
+def _report(what, y, o, tol):
+    e = assert_close(y, o, tol, what)
+    progress("%s: %d outputs, max rel err %.3e (gate %.0e), rel frobenius %.3e"
+             % (what, np.size(o), e, tol, rel_frobenius(y, o)))
+    return e
+
+
+@pytest.mark.parametrize("name", ["fp32_gemm_gelu_512", "fp32_gemm_gelu_1024", "fp32_gemm_gelu_2048",
+                                  "fp32_gemm_gelu_4096", "bf16_ffn_up_gelu"])
+def test_gemm_every_output(name):
+    w = datagen.WORKLOADS[name]
+    progress("full output %s (M=%d N=%d K=%d)" % (name, w.M, w.N, w.K))
+    A, B, bias = datagen.gemm_inputs(w)
+    Y = mk.gemm_bias_act(A.to("cuda"), B.to("cuda"), bias.to("cuda"), act="gelu", out_dtype=DT[w.out_dtype])
+    torch.cuda.synchronize()
+    y = f64(Y)
+    del Y
+    ref = oracle.gemm_bias_act(f64(A), f64(B), f64(bias), act="gelu")
+    _report(name, y, ref, TOL[w.in_dtype])
+
+
+@pytest.mark.parametrize("name", ["fp16_mlp3_d128", "fp16_mlp5_d64", "fp16_mlp_32_128_128_16",
+                                  "fp16_mlp_64_128_96_128_32"])
+def test_mlp_forward_every_output(name):
+    w = datagen.WORKLOADS[name]
+    progress("full output %s (M=%d dims=%s)" % (name, w.M, w.dims))
+    x, Ws = datagen.mlp_inputs(w)
+    out = mk.mlp_forward(x.to("cuda"), [t.to("cuda") for t in Ws])
+    torch.cuda.synchronize()
+    y = f64(out)
+    del out
+    ref = oracle.mlp_forward(f64(x), [f64(t) for t in Ws])
+    _report(name, y, ref, 2e-2)
+
+
+@pytest.mark.parametrize("name", ["fp16_mlp3_d128", "fp16_mlp5_d64"])
+def test_training_pair_every_output(name):
+    w = datagen.WORKLOADS[name]
+    L = w.L
+    progress("full training pair %s (M=%d dims=%s)" % (name, w.M, w.dims))
+    x, Ws = datagen.mlp_inputs(w)
+    g = datagen.mlp_grad_output(w)
+    xg, gg = x.to("cuda"), g.to("cuda")
+    wg = [t.to("cuda") for t in Ws]
+    out, acts = mk.mlp_forward_train(xg, wg)
+    dW, dx = mk.mlp_backward(xg, wg, acts, gg)
+    torch.cuda.synchronize()
+    x64, W64 = f64(x), [f64(t) for t in Ws]
+    o_out, o_acts = oracle.mlp_forward_train(x64, W64)
+    _report("%s training forward out" % name, f64(out), o_out, 2e-2)
+    del out, o_out
+    for l in range(L - 1):
+        # h_1 comes from exact fp16 products accumulated in fp32; deeper
+        # layers carry the fp16 rounding of their inputs
+        _report("%s stored activation h_%d" % (name, l + 1), f64(acts[l]), o_acts[l], 1e-4 if l == 0 else 2e-2)
+    del acts, o_acts
+    o_dW, o_dx = oracle.mlp_backward(x64, W64, f64(g))
+    _report("%s dx" % name, f64(dx), o_dx, 2e-2)
+    for l in range(L):
+        _report("%s dW_%d" % (name, l + 1), f64(dW[l]), o_dW[l], 2e-2)

@@ -70,8 +70,13 @@ def test_gemm_operand_beyond_4gib(name):
     assert_close(got, ref, TOL[A.dtype], "rows of a 4.8 GB A (%s)" % name)
 
 
-def test_gemm_maximum_pitches():
-    M, N, K = 300, 200, 72  # ragged in every dimension
+# N picks the tile shape the launcher takes for M = 300 (3 rows of 128 x 128
+# tiles on 256 CUs): 200 -> 6 tiles of 128, fewer than the CUs: 64 x 64;
+# 12000 -> 282, at most two per CU: 128 x 128; 22000 -> 516: 256 x 256, the
+# shape whose 256-row A tile puts in-tile offsets closest to 2^32 bytes.
+@pytest.mark.parametrize("N", [200, 12000, 22000])
+def test_gemm_maximum_pitches(N):
+    M, K = 300, 72  # ragged in every dimension
     lda, ldb, ldy = 1 << 23, 1 << 25, 1 << 23  # A 5.0 GB, B 4.8 GB, Y 5.0 GB
     A, B, bias = datagen.gemm_inputs(datagen.BF16_FFN, M=M, N=N, K=K)
     progress("gemm bf16 M=%d N=%d K=%d lda=2^23 ldb=2^25 ldy=2^23" % (M, N, K))
