@@ -185,6 +185,29 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
                                       size_t workspace_bytes, void* stream);
 
 /*
+ * coalesce_mlp_backward without the workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The per-workgroup partial weight
+ * gradients go to a scratch array of 64 MiB (67108864 bytes) that the library
+ * keeps in device memory, one per device, for the life of the process; the
+ * call itself allocates nothing and clears nothing (the backward overwrites
+ * every partial sum the reduction reads).  A chain whose partial sums
+ * (coalesce_mlp_backward_workspace_size) exceed 64 MiB is rejected with
+ * COALESCE_ERR_UNSUPPORTED before anything is launched; every chain
+ * coalesce_mlp_backward supports fits on a device of up to 256 compute
+ * units.  Every call on one device shares that device's scratch, which keeps
+ * the last call's contents: calls that can overlap on one device (streams
+ * without an order between them, several host threads) race and give wrong
+ * gradients, so order them on one stream.  Otherwise the arguments, the
+ * results (bit for bit the same as coalesce_mlp_backward's) and the errors
+ * are those of coalesce_mlp_backward.
+ */
+coalesce_status coalesce_mlp_backward_noalloc(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                              int32_t L, const float* const* acts, int64_t lda, const void* dout,
+                                              int64_t ldd, float* const* dW, void* dx, int64_t ldq, int64_t M,
+                                              coalesce_dtype dtype, coalesce_act hidden_act, void* stream);
+
+/*
  * Weight normalisation of every layer of a chain in ONE launch ("MLP
  * Megakernel" README, "Key ideas": the fused kernel normalises all weight
  * matrices, W = g * v / ||v||, so that per-layer launches do not dominate at

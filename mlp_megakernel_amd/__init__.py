@@ -36,6 +36,8 @@ SIGNATURES = {
     "coalesce_mlp_backward_workspace_size": (_sz, [_p, _i32]),
     "coalesce_mlp_backward": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _p, _i64, _p, _p, _i64, _i64, _i32, _i32,
                                      _p, _sz, _p]),
+    "coalesce_mlp_backward_noalloc": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _p, _i64, _p, _p, _i64, _i64, _i32,
+                                             _i32, _p]),
     "coalesce_weight_norm": (_i32, [_p, _p, _p, _p, _i32, _i32, _p]),
     "coalesce_weight_norm_backward": (_i32, [_p, _p, _p, _p, _p, _p, _i32, _i32, _p]),
     "coalesce_autotune_gemm_bias_act": (_i32, [_p, _i64, _p, _i64, _p, _p, _i64, _i64, _i64, _i64, _i32, _i32, _i32,
@@ -303,6 +305,36 @@ def mlp_backward(x: torch.Tensor, weights: Sequence[torch.Tensor], acts: Sequenc
                                      _ptr_array(acts) if L > 1 else None, lda, _ptr(dout), ldd, _ptr_array(dW),
                                      _ptr(dx), ldq, M, _DTYPES[x.dtype], _ACTS[hidden_act], _ptr(workspace),
                                      workspace.numel() * workspace.element_size(), _stream(stream)))
+    return list(dW), dx
+
+
+def mlp_backward_noalloc(x: torch.Tensor, weights: Sequence[torch.Tensor], acts: Sequence[torch.Tensor],
+                         dout: torch.Tensor, dW: Sequence[torch.Tensor], dx: Optional[torch.Tensor] = None,
+                         hidden_act="softplus", stream=None):
+    """The backward into caller-provided dW (and dx, or None to skip it)
+    through coalesce_mlp_backward_noalloc, whose partial sums live in the
+    library's own device scratch: the call allocates nothing."""
+    lib = load_library()
+    M, ldx, dims = _chain_dims(x, weights)
+    L = len(weights)
+    Md, Dd, ldd = _matrix(dout, "dout")
+    if (Md, Dd) != (M, dims[-1]) or dout.dtype != x.dtype:
+        raise ValueError("dout must be M x dims[L] of x's dtype")
+    if len(acts) != L - 1 or len(dW) != L:
+        raise ValueError("need the L - 1 stored activations and L weight-gradient tensors")
+    lda = _acts_pitch(acts, M, dims)
+    for l, g in enumerate(dW):
+        if g.shape != (dims[l], dims[l + 1]) or g.dtype != torch.float32 or not g.is_contiguous():
+            raise ValueError("dW[%d] must be a contiguous dims[l] x dims[l+1] float32 tensor" % l)
+    ldq = 0
+    if dx is not None:
+        Mq, Dq, ldq = _matrix(dx, "dx")
+        if (Mq, Dq) != (M, dims[0]) or dx.dtype != x.dtype:
+            raise ValueError("dx must be M x dims[0] of x's dtype")
+    _check(lib.coalesce_mlp_backward_noalloc(_ptr(x), ldx, _ptr_array(weights), _dims_array(dims), L,
+                                             _ptr_array(acts) if L > 1 else None, lda, _ptr(dout), ldd,
+                                             _ptr_array(dW), _ptr(dx), ldq, M, _DTYPES[x.dtype], _ACTS[hidden_act],
+                                             _stream(stream)))
     return list(dW), dx
 
 

@@ -433,6 +433,29 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
   return ok();
 }
 
+coalesce_status coalesce_mlp_backward_noalloc(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
+                                              int32_t L, const float* const* acts, int64_t lda, const void* dout,
+                                              int64_t ldd, float* const* dW, void* dx, int64_t ldq, int64_t M,
+                                              coalesce_dtype dtype, coalesce_act hidden_act, void* stream) {
+  int64_t P = 0;
+  bool square = true;
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square);
+  if (s != COALESCE_OK) return s;
+  int cus = 0;
+  if ((s = current_cus(&cus)) != COALESCE_OK) return s;
+  const size_t need = mlp_backward_workspace((int)P, (int)L, cus);
+  const size_t have = mlp_backward_scratch_bytes();
+  if (need > have)
+    return fail(COALESCE_ERR_UNSUPPORTED,
+                "this chain needs %zu bytes of partial sums, more than the %zu bytes of the library's scratch", need,
+                have);
+  void* scratch = nullptr;
+  hipError_t e = mlp_backward_scratch(&scratch);
+  if (e != hipSuccess) return device_fail(e, "scratch address (hipGetSymbolAddress)");
+  return coalesce_mlp_backward(x, ldx, W, dims, L, acts, lda, dout, ldd, dW, dx, ldq, M, dtype, hidden_act, scratch,
+                               have, stream);
+}
+
 coalesce_status coalesce_mlp_forward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims, int32_t L,
                                      void* out, int64_t ldo, int64_t M, coalesce_dtype dtype, coalesce_act hidden_act,
                                      void* stream) {

@@ -66,6 +66,12 @@ size_t mlp_backward_workspace(int D, int L, int num_cus);
 // Backward of the MLP chain: fills p.dW (and p.dx when set).  p.partial must
 // hold mlp_backward_workspace(D, L, num_cus) bytes.
 hipError_t launch_mlp_backward(MlpBwdParams p, int D, int L, int hidden_act, int num_cus, hipStream_t stream);
+// The library's own device-resident scratch for the backward's partial sums
+// (the no-allocation entry point): its size in bytes, and its address on the
+// current device (looked up with hipGetSymbolAddress on the first call per
+// device).
+size_t mlp_backward_scratch_bytes();
+hipError_t mlp_backward_scratch(void** ptr);
 
 constexpr int kMaxWnLayers = 16;
 struct WnParams {

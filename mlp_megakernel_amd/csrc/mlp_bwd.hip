@@ -40,6 +40,8 @@
 //     second kernel sums the partials in a fixed order: the result is
 //     deterministic for a given grid (the pages' design accumulates with
 //     atomics below 32K rows and calls GEMMs above).
+#include <mutex>
+
 #include "common.hpp"
 #include "launch.hpp"
 #include "mlp_common.hpp"
@@ -672,6 +674,38 @@ hipError_t launch_bwd_da(const MlpBwdParams& p, int L, int act, int cus, hipStre
 
 size_t mlp_backward_workspace(int D, int L, int num_cus) {
   return (size_t)num_cus * (size_t)L * (size_t)D * (size_t)D * sizeof(float);
+}
+
+// Scratch of the no-allocation backward entry point: the per-workgroup
+// partial weight gradients (mlp_backward_workspace bytes) in a file-scope
+// device array instead of a caller-lent workspace.  Every device the library
+// runs on holds its own copy until the process ends.  In host code the
+// array's name is only a host-side stand-in: the kernels get the address
+// that hipGetSymbolAddress returns on the current device (cached per device
+// below), never the name.  All calls on one device share it.
+constexpr size_t kBwdScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
+size_t mlp_backward_scratch_bytes() { return kBwdScratchBytes; }
+
+hipError_t mlp_backward_scratch(void** ptr) {
+  constexpr int kDevices = 64;
+  static std::mutex mutex;
+  static void* addr[kDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mutex);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_mlp_backward(MlpBwdParams p, int D, int L, int act, int num_cus, hipStream_t stream) {
