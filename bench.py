@@ -82,11 +82,26 @@ def parse():
     ap.add_argument("--calibrate-traffic", action="store_true",
                     help="also run a known-size read sweep and a known-size read+write kernel "
                          "(for scaling FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--fusion-traffic", action="store_true",
+                    help="run only the launch sequence whose FETCH_SIZE / WRITE_SIZE counters give the HBM "
+                         "traffic of every fused kernel and of its unfused baseline (see fusion_traffic)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn the rocprofv3 counter CSVs of two --fusion-traffic runs into profiles/traffic.json "
+                         "and print the tables (no GPU needed)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"),
+                    help="mean duration of the timed launches of each timed kernel in a rocprofv3 kernel trace "
+                         "of a bench.py run, beside that run's JSON line (no GPU needed)")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the workloads shard by rows with no exchange between GPUs, "
               "but runs on more than one GPU are not supported. Use --gpus 1.", file=sys.stderr)
@@ -249,11 +264,12 @@ def main():
 
     def roofline_gemm(w, mean_ms):
         flops = w.flops()
+        kern = "gemm32_kernel" if w.in_dtype == "f32" else "gemm16_kernel"
         ach = flops / (mean_ms * 1e-3) / 1e12
         peak = PEAK_TFLOPS[w.in_dtype]
         return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": measured_traffic("gemm16_kernel/" + w.name), "kernel": "gemm16_kernel" if w.in_dtype != "f32"
-                else "gemm32_kernel", "algorithmic_flop_per_launch": flops,
+                "frac": round(ach / peak, 4), "traffic": measured_traffic(kern + "/" + w.name), "kernel": kern,
+                "algorithmic_flop_per_launch": flops,
                 "algorithmic_bytes_per_launch": w.bytes(), "mean_launch_ms": round(mean_ms, 5)}
 
     def roofline_mlp(w, mean_ms):
@@ -269,6 +285,10 @@ def main():
                 "valu": {"bound": "alu", "achieved": round(trans / (mean_ms * 1e-3) / 1e12, 3),
                          "peak": round(PEAK_TRANS_PER_S / 1e12, 3), "unit": "T transcendentals/s",
                          "frac": round(trans / (mean_ms * 1e-3) / PEAK_TRANS_PER_S, 4)}}
+
+    if args.fusion_traffic:
+        fusion_traffic(gemm_case, mlp_case, train_case, flush)
+        return
 
     result = {}
     prim = datagen.WORKLOADS[args.workload]
@@ -607,6 +627,263 @@ def main():
         result["cpu_baseline"] = cpu_baseline(prim, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+# ----------------------------------------------------------------------------
+# HBM traffic of the fused kernels and of their unfused baselines
+# ----------------------------------------------------------------------------
+# The launch sequence of --fusion-traffic, in order, as (section, workload,
+# role, kernels launched).  Only the library's own kernels are listed; torch's
+# (input fills, copies) are skipped when the counters are matched to it.
+TRAFFIC_GEMMS = ("fp32_gemm_gelu_512", "fp32_gemm_gelu_1024", "fp32_gemm_gelu_2048", "fp32_gemm_gelu_4096",
+                 "bf16_ffn_up_gelu")
+TRAFFIC_MLPS = ("fp16_mlp3_d128", "fp16_mlp5_d64")
+WARM_LAUNCHES = 3
+
+
+def traffic_plan():
+    import datagen
+    plan = [("calibration", "flush_512MiB", "read", ["flush_kernel"]),
+            ("calibration", "activation_256MiB", "read+write", ["activation_kernel"])]
+    for name in TRAFFIC_GEMMS:
+        w = datagen.WORKLOADS[name]
+        g = "gemm32_kernel" if w.in_dtype == "f32" else "gemm16_kernel"
+        plan += [("fusion", name, "flush", ["flush_kernel"]), ("fusion", name, "fused_cold", [g]),
+                 ("fusion", name, "flush", ["flush_kernel"]),
+                 ("fusion", name, "unfused_cold", [g, "bias_add_kernel", "activation_kernel"])]
+        plan += [("warm", name, "fused_warm", [g])] * WARM_LAUNCHES
+    for name in TRAFFIC_MLPS:
+        w = datagen.WORKLOADS[name]
+        chain = []
+        for l in range(w.L):
+            chain.append("gemm16_kernel")
+            if l < w.L - 1:
+                chain.append("activation_kernel")
+        plan += [("fusion", name, "flush", ["flush_kernel"]), ("fusion", name, "fused_cold", ["mlp_kernel"]),
+                 ("fusion", name, "flush", ["flush_kernel"]), ("fusion", name, "unfused_cold", chain)]
+        plan += [("warm", name, "fused_warm", ["mlp_kernel"])] * WARM_LAUNCHES
+    for name in TRAFFIC_MLPS:
+        plan += [("warm", name, "forward_train_first", ["mlp_kernel"])]  # train_case's own first call
+        plan += [("warm", name, "forward_train_warm", ["mlp_kernel"]),
+                 ("warm", name, "backward_warm", ["mlp_bwd_kernel", "mlp_bwd_reduce"])] * WARM_LAUNCHES
+    return plan
+
+
+def fusion_traffic(gemm_case, mlp_case, train_case, flush):
+    """Launch exactly the sequence of traffic_plan(): the two calibration
+    kernels; then for every workload a flushed fused launch, a flushed
+    unfused chain (GEMM -> bias-add -> activation; for the MLPs the per-layer
+    GEMM -> softplus chain with fp16 intermediates) and WARM_LAUNCHES
+    back-to-back fused launches (the regime of the timed steps); then the
+    training pair of both MLPs back to back.  Under rocprofv3 --pmc
+    FETCH_SIZE (then WRITE_SIZE) every dispatch gets its own counter value;
+    summarize_counters matches them to this plan."""
+    import torch
+
+    import datagen
+    import mlp_megakernel_amd as mk
+
+    dev = torch.device("cuda:0")
+    flush()
+    t = torch.zeros((8192, 16384), dtype=torch.float16, device=dev)
+    mk.activation(t, "none", out=torch.empty_like(t))
+    torch.cuda.synchronize()
+    del t
+    for name in TRAFFIC_GEMMS + TRAFFIC_MLPS:
+        w = datagen.WORKLOADS[name]
+        print("bench: fusion traffic %s" % name, file=sys.stderr, flush=True)
+        fused, unfused = (mlp_case if name in TRAFFIC_MLPS else gemm_case)(w)
+        torch.cuda.synchronize()
+        flush()
+        fused()
+        flush()
+        unfused()
+        for _ in range(WARM_LAUNCHES):
+            fused()
+        torch.cuda.synchronize()
+        del fused, unfused
+        torch.cuda.empty_cache()
+    for name in TRAFFIC_MLPS:
+        w = datagen.WORKLOADS[name]
+        print("bench: training-pair traffic %s" % name, file=sys.stderr, flush=True)
+        fwd, bwd, step, _ = train_case(w)  # (its first training forward is in the plan)
+        torch.cuda.synchronize()
+        for _ in range(WARM_LAUNCHES):
+            fwd()
+            bwd()
+        torch.cuda.synchronize()
+        del fwd, bwd, step
+        torch.cuda.empty_cache()
+    print(json.dumps({"fusion_traffic_plan": traffic_plan()}), flush=True)
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _library_rows(rows):
+    """The library's dispatches (kernels in namespace coalesce), in dispatch order."""
+    out = [r for r in rows if "coalesce" in r["Kernel_Name"]]
+    out.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return out
+
+
+def _match_plan(rows, plan, what):
+    """Split the library's dispatches along the plan, checking each kernel name."""
+    out, i = [], 0
+    for sec, wl, role, kernels in plan:
+        vals = []
+        for k in kernels:
+            if i >= len(rows) or k not in rows[i]["Kernel_Name"]:
+                raise SystemExit("%s: dispatch %d is %r, the plan expects %s (%s %s)"
+                                 % (what, i, rows[i]["Kernel_Name"] if i < len(rows) else None, k, wl, role))
+            vals.append(float(rows[i]["Counter_Value"]))
+            i += 1
+        out.append((sec, wl, role, kernels, vals))
+    return out
+
+
+def summarize_counters(fetch_csv, write_csv):
+    """profiles/traffic.json from the FETCH_SIZE and WRITE_SIZE runs of
+    --fusion-traffic: calibration factors, per-workload fused and unfused
+    bytes with the model's prediction, and the per-launch traffic of the
+    timed kernels (back-to-back, as in the timed steps) that the bench line
+    reports while the kernels' sources are unchanged."""
+    import hashlib
+
+    import datagen
+
+    plan = traffic_plan()
+    fe = _match_plan(_library_rows(_read_csv(fetch_csv)), plan, "FETCH_SIZE")
+    wr = _match_plan(_library_rows(_read_csv(write_csv)), plan, "WRITE_SIZE")
+    KiB = 1024.0
+    f_fac = FLUSH_BYTES / (fe[0][4][0] * KiB)
+    w_fac = (8192 * 16384 * 2) / (wr[1][4][0] * KiB)
+    C = "mlp_megakernel_amd/csrc/"
+    srcs = {"gemm16_kernel": [C + "gemm16.hip", C + "common.hpp"], "gemm32_kernel": [C + "gemm32.hip", C + "common.hpp"],
+            "mlp_kernel": [C + "mlp.hip", C + "mlp_common.hpp", C + "common.hpp"],
+            "backward": [C + "mlp_bwd.hip", C + "mlp_common.hpp", C + "common.hpp"]}
+
+    def sha(files):
+        h = hashlib.sha256()
+        for fn in files:
+            with open(os.path.join(ROOT, fn), "rb") as f:
+                h.update(f.read())
+        return h.hexdigest()
+
+    def tot(entries, role, wl, fac):
+        vs = [sum(e[4]) for e in entries if e[1] == wl and e[2] == role]
+        return fac * KiB * sum(vs) / len(vs)
+
+    out = {"_comment": "HBM traffic per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs of "
+                       "'bench.py --fusion-traffic', scaled by the calibration factors (FETCH_SIZE x %.4f, "
+                       "WRITE_SIZE x %.4f: the 512 MiB read sweep and the 256 MiB read + 256 MiB write activation "
+                       "kernel).  Written by 'bench.py --summarize-counters'.  bench.py reports a kernel's traffic "
+                       "only while its sources still hash to source_sha256." % (f_fac, w_fac),
+           "fetch_factor": f_fac, "write_factor": w_fac, "fusion": {}}
+    print("| workload | fused read | fused write | unfused read | unfused write | unfused - fused | model | "
+          "measured / model |")
+    print("|---|---|---|---|---|---|---|---|")
+    for wl in TRAFFIC_GEMMS + TRAFFIC_MLPS:
+        w = datagen.WORKLOADS[wl]
+        fr, fw = tot(fe, "fused_cold", wl, f_fac), tot(wr, "fused_cold", wl, w_fac)
+        ur, uw = tot(fe, "unfused_cold", wl, f_fac), tot(wr, "unfused_cold", wl, w_fac)
+        if wl in TRAFFIC_MLPS:
+            # each hidden layer's z_l written by its GEMM, read and h_l written
+            # by the softplus kernel, h_l read by the next GEMM (fp16)
+            s_h = [2.0 * w.M * d for d in w.dims[1:-1]]
+            model = 4.0 * sum(s_h)
+            model_txt = "4 x sum of S_h (%d hidden layers of %.1f MB)" % (len(s_h), s_h[0] / 1e6)
+            kern = "mlp_kernel"
+        else:
+            # Z written by the GEMM, read by the bias add, Z2 written by it,
+            # read by the activation (intermediates in the input dtype,
+            # the size of the output here)
+            s_out = (4.0 if w.out_dtype == "f32" else 2.0) * w.M * w.N
+            model = 4.0 * s_out
+            model_txt = "4 x S_out (S_out %.1f MB)" % (s_out / 1e6)
+            kern = "gemm32_kernel" if w.in_dtype == "f32" else "gemm16_kernel"
+        delta = (ur + uw) - (fr + fw)
+        out["fusion"][wl] = {"fused_fetch_bytes": fr, "fused_write_bytes": fw, "unfused_fetch_bytes": ur,
+                             "unfused_write_bytes": uw, "delta_bytes": delta, "model_bytes": model,
+                             "model": model_txt, "ratio": delta / model,
+                             "algorithmic_bytes": w.bytes()}
+        print("| %s | %.1f MB | %.1f MB | %.1f MB | %.1f MB | %.1f MB | %.1f MB (%s) | %.3f |"
+              % (wl, fr / 1e6, fw / 1e6, ur / 1e6, uw / 1e6, delta / 1e6, model / 1e6, model_txt, delta / model))
+        warm_f, warm_w = tot(fe, "fused_warm", wl, f_fac), tot(wr, "fused_warm", wl, w_fac)
+        out["%s/%s" % (kern, wl)] = {"kernels": [kern], "sources": srcs[kern], "fetch_bytes": warm_f,
+                                     "write_bytes": warm_w, "source_sha256": sha(srcs[kern])}
+    print()
+    print("| timed kernel (back to back) | FETCH (scaled) | WRITE (scaled) | algorithmic |")
+    print("|---|---|---|---|")
+    for key, ent in out.items():
+        if "/" in key:
+            w = datagen.WORKLOADS[key.split("/")[1]]
+            print("| %s | %.1f MB | %.1f MB | %.1f MB |" % (key, ent["fetch_bytes"] / 1e6, ent["write_bytes"] / 1e6,
+                                                            w.bytes() / 1e6))
+    for wl in TRAFFIC_MLPS:
+        w = datagen.WORKLOADS[wl]
+        hidden = sum(w.dims[1:-1])
+        for role, key, kern, by in (("forward_train_warm", "forward_train", "mlp_kernel",
+                                     w.M * (2.0 * w.dims[0] + 2.0 * w.dims[-1] + 4.0 * hidden)),
+                                    ("backward_warm", "backward", "backward",
+                                     w.M * (4.0 * w.dims[0] + 2.0 * w.dims[-1] + 4.0 * hidden))):
+            f_, w_ = tot(fe, role, wl, f_fac), tot(wr, role, wl, w_fac)
+            out["%s/%s" % (key, wl)] = {"kernels": [kern], "sources": srcs[kern], "fetch_bytes": f_,
+                                        "write_bytes": w_, "source_sha256": sha(srcs[kern])}
+            print("| %s/%s | %.1f MB | %.1f MB | %.1f MB |" % (key, wl, f_ / 1e6, w_ / 1e6, by / 1e6))
+    print()
+    print("calibration: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f" % (f_fac, w_fac))
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=2)
+        f.write("\n")
+
+
+def summarize_trace(trace_csv, bench_json):
+    """For each kernel a bench.py run timed (its JSON line in bench_json),
+    the mean duration of its last K dispatches in the rocprofv3 kernel trace
+    of that run -- the timed launches, when the run skipped the sections that
+    launch the same kernel later (--no-harness --no-tune --no-variants) --
+    beside the mean the run measured with HIP events and the mean over all
+    of the kernel's dispatches (what --stats reports)."""
+    rows = _read_csv(trace_csv)
+    with open(bench_json) as f:
+        line = [l for l in f if l.startswith("{")][-1]
+    res = json.loads(line)
+    by_name = {}
+    for r in rows:
+        by_name.setdefault(r["Kernel_Name"], []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    timed = [("primary " + res["config"]["workload"], res["roofline"], res["steps"],
+              "mlp_kernel" if res["unit"] == "rows/s" else ("gemm32_kernel" if res["dtype"] == "f32" else "gemm16_kernel"))]
+    for wl, ent in (res.get("mlp") or {}).items():
+        timed.append((wl, ent["roofline"], max(20, res["steps"]), "mlp_kernel"))
+    print("| timed kernel | dispatches | mean of all | mean of the last K (K) | HIP-event mean of the run | "
+          "roofline frac from the trace | from the events |")
+    print("|---|---|---|---|---|---|---|")
+    for label, roof, K, pat in timed:
+        want = roof["mean_launch_ms"]
+        # the kernel instantiation whose last K dispatches best match the events
+        best = None
+        for name, ts in by_name.items():
+            if pat not in name or "coalesce" not in name or len(ts) < K:
+                continue
+            ts = sorted(ts)
+            last = [(e - s) / 1e6 for s, e in ts[-K:]]
+            m = sum(last) / K
+            if best is None or abs(m - want) < abs(best[1] - want):
+                best = (name, m, sum((e - s) / 1e6 for s, e in ts) / len(ts), len(ts))
+        if best is None:
+            continue
+        name, m, allm, n = best
+        if roof["unit"] == "TFLOP/s":
+            frac = roof["algorithmic_flop_per_launch"] / (m * 1e-3) / 1e12 / roof["peak"]
+        else:
+            frac = roof["algorithmic_bytes_per_launch"] / (m * 1e-3) / 1e9 / roof["peak"]
+        print("| %s: `%s` | %d | %.4f ms | %.4f ms (%d) | %.4f ms | %.4f | %.4f |"
+              % (label, name.replace("void coalesce::(anonymous namespace)::", "").split("(")[0], n, allm, m, K,
+                 want, frac, roof["frac"]))
 
 
 def measured_traffic(key):

@@ -1,0 +1,84 @@
+"""The fusion-traffic pin, checked on the committed counter runs.
+
+"Fuse Elementwise Ops" (required reasoning, step 2, and the review
+checklist: memory traffic quantified before and after fusion) counts HBM
+traffic of N separate elementwise kernels over a tensor of S bytes as 2 N S
+against 2 S fused.  For the GEMM + bias + GELU chain that is: the unfused
+GEMM writes Z, the bias add reads Z and writes Z2, the activation reads Z2
+and writes Y, so the unfused chain moves 4 S_out more than the fused kernel
+(S_out = the output's bytes; the intermediates have the output's size in
+every workload here).  For the MLP chain each hidden layer's z_l and h_l make
+one round trip each: 4 S_h per hidden layer (S_h = M x H x 2 bytes).
+
+profiles/traffic.json holds rocprofv3 FETCH_SIZE / WRITE_SIZE counts of one
+flushed fused launch and one flushed unfused chain per workload ("bench.py
+--fusion-traffic", scaled by the known-size calibration kernels of the same
+runs).  The measured saving must match the model within 10 %: what is left is
+L2 / MALL reuse of an intermediate between two kernels of the unfused chain
+(ratio below 1; largest at FP32 4096^3, whose 64 MiB intermediate partly stays
+in the 256 MB MALL) and the unfused per-layer MLP GEMMs reading their input
+once per 64-column tile (ratio above 1).  The fused kernels themselves must
+move their algorithmic output bytes (the MLP megakernel: x and out only, its
+activations never leave the chip).
+"""
+import json
+import os
+
+import pytest
+
+import datagen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
+    TRAFFIC = json.load(f)
+
+GEMMS = ["fp32_gemm_gelu_512", "fp32_gemm_gelu_1024", "fp32_gemm_gelu_2048", "fp32_gemm_gelu_4096",
+         "bf16_ffn_up_gelu"]
+MLPS = ["fp16_mlp3_d128", "fp16_mlp5_d64"]
+
+
+def test_calibration_factors():
+    # the 512 MiB read sweep and the 256 MiB + 256 MiB activation kernel
+    assert abs(TRAFFIC["fetch_factor"] - 2.0) < 0.01
+    assert abs(TRAFFIC["write_factor"] - 1.0) < 0.01
+
+
+@pytest.mark.parametrize("name", GEMMS)
+def test_gemm_fusion_saves_four_output_sizes(name):
+    w = datagen.WORKLOADS[name]
+    e = TRAFFIC["fusion"][name]
+    s_out = (4 if w.out_dtype == "f32" else 2) * w.M * w.N
+    model = 4.0 * s_out
+    assert e["model_bytes"] == pytest.approx(model)
+    delta = (e["unfused_fetch_bytes"] + e["unfused_write_bytes"]) - (e["fused_fetch_bytes"] + e["fused_write_bytes"])
+    assert 0.9 <= delta / model <= 1.1, (name, delta / model)
+    # the unfused chain writes Z and Z2 on top of Y
+    assert 0.85 <= (e["unfused_write_bytes"] - e["fused_write_bytes"]) / (2.0 * s_out) <= 1.15
+    # the fused kernel writes Y about once: the 16-bit kernel's staged
+    # epilogue stores whole 128-byte lines (1.09 S_out at the FFN); the FP32
+    # kernel's 128 x 128 tiles (4096^3) store 16 bytes per lane straight from
+    # the accumulators and write 1.24 S_out
+    assert 0.99 <= e["fused_write_bytes"] / s_out <= 1.3, (name, e["fused_write_bytes"] / s_out)
+
+
+@pytest.mark.parametrize("name", MLPS)
+def test_mlp_fusion_saves_four_hidden_sizes_per_layer(name):
+    w = datagen.WORKLOADS[name]
+    e = TRAFFIC["fusion"][name]
+    model = 4.0 * sum(2.0 * w.M * d for d in w.dims[1:-1])
+    assert e["model_bytes"] == pytest.approx(model)
+    delta = (e["unfused_fetch_bytes"] + e["unfused_write_bytes"]) - (e["fused_fetch_bytes"] + e["fused_write_bytes"])
+    assert 0.9 <= delta / model <= 1.1, (name, delta / model)
+    # the megakernel moves x in and out out, nothing else (within 1 %)
+    x_bytes, out_bytes = 2.0 * w.M * w.dims[0], 2.0 * w.M * w.dims[-1]
+    assert e["fused_fetch_bytes"] == pytest.approx(x_bytes, rel=0.01)
+    assert e["fused_write_bytes"] == pytest.approx(out_bytes, rel=0.01)
+
+
+def test_timed_kernels_have_traffic_records():
+    # one back-to-back traffic record per timed kernel, tied to its sources
+    for key in ["gemm16_kernel/bf16_ffn_up_gelu", "mlp_kernel/fp16_mlp3_d128", "mlp_kernel/fp16_mlp5_d64",
+                "forward_train/fp16_mlp3_d128", "backward/fp16_mlp3_d128"]:
+        e = TRAFFIC[key]
+        assert e["fetch_bytes"] > 0 and e["write_bytes"] > 0 and len(e["source_sha256"]) == 64
