@@ -85,8 +85,9 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
  * with no biases and a linear last layer, in ONE launch whose intermediate
  * activations stay on chip (fp16 MFMA operands, fp32 accumulation, the
  * activation in fp32, h_l rounded to fp16 only as the next layer's operand).
- * The grid is min(#CUs x occupancy, #tiles) workgroups that walk the row
- * tiles round-robin.
+ * The grid is min(#CUs x occupancy, #tiles) persistent workgroups: workgroup
+ * b of G owns the row tiles b, b + G, b + 2G, ..., which its waves take one
+ * at a time as they become free.
  *
  *   x     device, M x dims[0] fp16, leading dimension ldx >= dims[0]
  *   W     HOST array of L device pointers; W[l] is dims[l] x dims[l+1] fp16,
@@ -109,7 +110,7 @@ coalesce_status coalesce_mlp_forward(const void* x, int64_t ldx, const void* con
 /*
  * As coalesce_mlp_forward, with the persistent grid size chosen by the
  * caller: num_workgroups > 0 launches exactly that many workgroups (each
- * walks the tiles round-robin), 0 picks min(#CUs x occupancy, #tiles).  The
+ * owns every num_workgroups-th row tile), 0 picks min(#CUs x occupancy, #tiles).  The
  * result does not depend on the grid size, bit for bit.
  */
 coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,

@@ -1,17 +1,22 @@
 // Persistent softplus-MLP megakernel ("MLP Megakernel" README: all layers'
 // GEMMs and activations in one launch, intermediate activations kept in
 // registers, fp16 MFMA operands with fp32 accumulation, a persistent grid of
-// min(#CUs x occupancy, #tiles) workgroups walking the row tiles round-robin).
+// min(#CUs x occupancy, #tiles) workgroups walking the row tiles).
 //
 //   h_0 = x;  h_l = act(h_{l-1} W_l) (l < L);  out = h_{L-1} W_L
 //
 // Design for gfx950, widths D of 64 or 128:
 //   * a workgroup copies every W_l into LDS once (L * D * D fp16: 96 KB for
 //     3 x 128, 40 KB for 5 x 64) and reuses it for all of its row tiles;
-//   * a wave owns a tile of 32 rows; tiles go to
-//     waves round-robin, so every row goes through the same instruction
-//     sequence whatever the grid size (results are bit-identical for any
-//     grid);
+//   * a wave works on a tile of 32 rows at a time; workgroup b owns the
+//     tiles b, b + G, b + 2G, ... (G workgroups) and its waves claim them one
+//     at a time from a counter in LDS.  The SIMD issues from its oldest
+//     ready wave first, so waves sharing a SIMD progress at very different
+//     rates (with a fixed share each, the youngest finished ~2.7x later than
+//     the oldest and ran alone at the end); claiming on demand keeps all of
+//     them busy to the end.  Every row goes through the same instruction
+//     sequence whatever wave or grid takes it, so results are bit-identical
+//     for any grid and any timing;
 //   * each layer is computed transposed, z^T = W^T h^T, with
 //     v_mfma_f32_16x16x32_f16: the A operand is W^T read from LDS (one
 //     128-bit read per 16 output units and 32 k, shared by the wave's 16-row
@@ -238,12 +243,39 @@ __device__ __forceinline__ void load_x(const MlpParams& p, const Lane<D>& c, int
 // maximum fp16 output of each lane.  log2(1 + 2^a) >= a, so an argument
 // above the threshold (or +inf) shows as an output of at least 28 (a bound
 // below the threshold that the rounding of exp2, log2 and fp16 cannot cross);
-// a wave that sees one recomputes its tiles from x with the guarded form
-// (softplus_b2).  Both forms execute the same exp2/add/log2 instructions, so
-// every result equals what the guarded form gives.  NaN arguments give NaN
-// in both forms and are ignored by the maximum.
+// a workgroup any of whose waves saw one recomputes all of its tiles from x
+// with the guarded form (softplus_b2).  Both forms execute the same
+// exp2/add/log2 instructions, so every result equals what the guarded form
+// gives.  A NaN argument gives NaN in both forms; the maximum below
+// propagates NaN (IEEE maximum), so a NaN also triggers the recompute (a slow
+// path, not a different result).
 constexpr float SP_THRESHOLD_B2 = 28.853900817779268f;  // 20 log2(e)
-constexpr unsigned short SP_FLAG_B2_F16 = 0x4F00;  // 28.0 in fp16
+constexpr _Float16 SP_FLAG_B2_F16 = (_Float16)28.0f;
+
+// Maximum of n packed fp16 pairs and m, in a tree of three-input packed
+// maxima (v_pk_maximum3_f16: NaN in, NaN out): about n / 2 instructions with
+// a short dependency chain.
+template <int N>
+__device__ __forceinline__ f16x2 max_tree(const f16x2 (&v)[N], f16x2 m) {
+  if constexpr (N == 1) {
+    return __builtin_elementwise_maximum(m, v[0]);
+  } else if constexpr (N == 2) {
+    return __builtin_elementwise_maximum(m, __builtin_elementwise_maximum(v[0], v[1]));
+  } else {
+    constexpr int R = (N + 2) / 3;
+    f16x2 r[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      if (3 * i + 2 < N)
+        r[i] = __builtin_elementwise_maximum(v[3 * i], __builtin_elementwise_maximum(v[3 * i + 1], v[3 * i + 2]));
+      else if (3 * i + 1 < N)
+        r[i] = __builtin_elementwise_maximum(v[3 * i], v[3 * i + 1]);
+      else
+        r[i] = v[3 * i];
+    }
+    return max_tree<R>(r, m);
+  }
+}
 
 __device__ __forceinline__ float softplus_b2_fast(float a) {
   return __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(a));
@@ -273,7 +305,7 @@ __device__ __forceinline__ void interleave() {
 // folded into mx.
 template <int D, int l, int ACT, bool ST, bool PAD>
 __device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& c, const HTile<D>& hin,
-                                             HTile<D>& hout, u16x2& mx, int tile) {
+                                             HTile<D>& hout, f16x2& mx, int tile) {
   using G = Geo<D>;
   constexpr bool SP = ACT == ACT_SOFTPLUS;
   __amdgpu_buffer_rsrc_t ra[G::MT];
@@ -340,18 +372,15 @@ __device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& 
     for (int s = 0; s < G::MT; ++s) prv[s] = acc[s];
   }
   if constexpr (SP) {
-    // running maximum of the layer's fp16 outputs as unsigned 16-bit
-    // integers, two at a time: the outputs are >= +0 or NaN, and for those
-    // the integer order of the bit patterns is the numeric order with every
-    // NaN above +inf
+    // running maximum of the layer's fp16 outputs (two per dword)
+    f16x2 h[G::MT * G::KS * 4];
 #pragma unroll
     for (int s = 0; s < G::MT; ++s)
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) {
-        const u16x2x4 h = __builtin_bit_cast(u16x2x4, hout.v[s][ks]);  // one dword = two fp16
+      for (int ks = 0; ks < G::KS; ++ks)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mx = __builtin_elementwise_max(mx, h.v[i]);
-      }
+        for (int i = 0; i < 4; ++i) h[(s * G::KS + ks) * 4 + i] = __builtin_bit_cast(f16x2, hout.v[s][ks][i]);
+    mx = max_tree(h, mx);
     // here, not later: deferring the maximum would keep every layer's
     // outputs alive until the end of the tile
     asm volatile("" : "+v"(mx));
@@ -491,7 +520,7 @@ __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& 
 // mx collects the largest unguarded softplus output.
 template <int D, int L, int l, int ACT, bool ST, bool PAD>
 __device__ __forceinline__ void tile_chain(const MlpParams& p, const Lane<D>& c, int tile, HTile<D>& hin,
-                                           HTile<D>& hfree, u16x2& mx) {
+                                           HTile<D>& hfree, f16x2& mx) {
   if constexpr (l < L - 1) {
     hidden_layer<D, l, ACT, ST, PAD>(p, c, hin, hfree, mx, tile);
     tile_chain<D, L, l + 1, ACT, ST, PAD>(p, c, tile, hfree, hin, mx);
@@ -500,21 +529,35 @@ __device__ __forceinline__ void tile_chain(const MlpParams& p, const Lane<D>& c,
   }
 }
 
+// The next of the workgroup's tiles for the calling wave: one LDS atomic by
+// lane 0, its result broadcast to the wave.  Workgroup b's k-th tile is
+// b + k G.
+__device__ __forceinline__ int claim_tile(int* counter) {
+  int k = 0;
+  if ((threadIdx.x & 63) == 0) k = atomicAdd(counter, 1);
+  return (int)blockIdx.x + __builtin_amdgcn_readfirstlane(k) * (int)gridDim.x;
+}
+
 // Several waves per SIMD (MlpCfg::MINW) so that memory latency and the
 // dependent activation chains of some waves hide behind the work of others.
 template <int D, int L, int ACT, bool ST, bool PAD>
 __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(MlpParams p) {
   using G = Geo<D>;
   __shared__ __attribute__((aligned(16))) _Float16 sW[L * D * D];
+  __shared__ int s_next;      // the workgroup's next unclaimed tile (local index)
+  __shared__ unsigned s_flag;  // some wave saw a softplus argument past the guard
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (threadIdx.x == 0) {
+    s_next = G::WAVES;  // local tiles 0 .. WAVES - 1 are the waves' first ones
+    s_flag = 0;
+  }
   stage_weights<D, L, PAD>(p, sW);
   __syncthreads();
 
   const int lane = threadIdx.x & 63;
-  const int wave = blockIdx.x * G::WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nwaves = gridDim.x * G::WAVES;
   const Lane<D> c = lane_setup<D>(p, sW, lane);
-  u16x2 mx = (u16x2){0, 0};
-  int tile = wave;
+  f16x2 mx = (f16x2){0, 0};
+  int tile = (int)blockIdx.x + wv * (int)gridDim.x;
   // Three activation buffers in rotation: the x of the next tile is loaded
   // into the third one when a tile starts, a whole tile ahead of its use.
   // The load is issued even past the last tile (its buffer resources cover
@@ -524,30 +567,36 @@ __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(M
   HTile<D> ha, hb, hc;
   if (tile < p.num_tiles) load_x<D, PAD>(p, c, tile, ha);
   while (tile < p.num_tiles) {
-    int next = tile + nwaves;
+    int next = claim_tile(&s_next);
     load_x<D, PAD>(p, c, next, hc);
     tile_chain<D, L, 0, ACT, ST, PAD>(p, c, tile, ha, hb, mx);
     tile = next;
     if (tile >= p.num_tiles) break;
-    next = tile + nwaves;
+    next = claim_tile(&s_next);
     load_x<D, PAD>(p, c, next, hb);
     tile_chain<D, L, 0, ACT, ST, PAD>(p, c, tile, hc, ha, mx);
     tile = next;
     if (tile >= p.num_tiles) break;
-    next = tile + nwaves;
+    next = claim_tile(&s_next);
     load_x<D, PAD>(p, c, next, ha);
     tile_chain<D, L, 0, ACT, ST, PAD>(p, c, tile, hb, hc, mx);
     tile = next;
   }
   if constexpr (ACT == ACT_SOFTPLUS && L > 1) {
-    // Some softplus argument of this wave's tiles may have exceeded the
-    // guard threshold: recompute all of the wave's tiles with the guarded
-    // form.  Tiles without such an argument get the same bits again; the
-    // others are corrected.  The first results are complete in memory before
-    // they are overwritten.
-    if (__builtin_amdgcn_ballot_w64(max(mx[0], mx[1]) >= SP_FLAG_B2_F16) != 0) {
+    // Some softplus argument of the workgroup's tiles may have exceeded the
+    // guard threshold: then its waves recompute all of the workgroup's tiles
+    // with the guarded form.  Tiles without such an argument get the same
+    // bits again; the others are corrected.  Every wave's first results are
+    // complete in memory (its own wait, then the barrier) before any wave
+    // overwrites them.
+    const bool big = !(mx[0] < SP_FLAG_B2_F16 && mx[1] < SP_FLAG_B2_F16);  // also for NaN
+    if (__builtin_amdgcn_ballot_w64(big) != 0 && lane == 0) s_flag = 1u;
+    __syncthreads();
+    if (s_flag != 0u) {
       wait_vmcnt0();
-      for (int t = wave; t < p.num_tiles; t += nwaves) tile_guarded<D, L, ACT, ST, PAD>(p, c, t);
+      __syncthreads();
+      for (int t = (int)blockIdx.x + wv * (int)gridDim.x; t < p.num_tiles; t += G::WAVES * (int)gridDim.x)
+        tile_guarded<D, L, ACT, ST, PAD>(p, c, t);
     }
   }
 }

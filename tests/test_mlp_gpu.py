@@ -111,9 +111,10 @@ def test_grid_size_and_row_order_invariance(D, L):
 @pytest.mark.parametrize("D,L", [(64, 5), (128, 3), (128, 2)])
 def test_guard_recompute_mixed_rows(D, L):
     # A few rows with large inputs push softplus arguments past the guard at
-    # z = 20 and past the fp32 range of exp (z > 88.7); the waves that own
-    # them recompute their tiles with the guarded form.  Results must match
-    # the oracle, and be bit-identical whichever wave and grid gets the rows.
+    # z = 20 and past the fp32 range of exp (z > 88.7); the workgroups that
+    # own them recompute their tiles with the guarded form.  Results must
+    # match the oracle, and be bit-identical whichever wave and grid gets the
+    # rows.
     w = datagen.MLP3 if D == 128 else datagen.MLP5
     M = 64 * 150 + 5
     x, Ws = datagen.mlp_inputs(w, M=M, dims=(D,) * (L + 1))
@@ -129,6 +130,27 @@ def test_guard_recompute_mixed_rows(D, L):
     perm = torch.from_numpy(np.random.default_rng(11).permutation(M))
     outp = mk.mlp_forward(to_gpu(x[perm]), Wg).cpu()
     assert torch.equal(outp.view(torch.int16), out[perm].view(torch.int16))
+
+
+@pytest.mark.parametrize("D,L", [(64, 5), (128, 3)])
+def test_nan_rows_stay_in_their_rows(D, L):
+    # A NaN input row gives NaN outputs in that row only.  NaN also trips the
+    # softplus guard's check (the maximum propagates NaN), so its workgroup
+    # recomputes its tiles with the guarded form: every other row must keep
+    # the bits of the run without NaN.
+    w = datagen.MLP3 if D == 128 else datagen.MLP5
+    M = 64 * 150 + 5
+    x, Ws = datagen.mlp_inputs(w, M=M, dims=(D,) * (L + 1))
+    Wg = [t.to("cuda") for t in Ws]
+    clean = mk.mlp_forward(to_gpu(x), Wg).cpu()
+    nan_rows = [2, 901, M - 1]
+    xn = x.clone()
+    xn[nan_rows] = float("nan")
+    out = mk.mlp_forward(to_gpu(xn), Wg).cpu()
+    keep = torch.ones(M, dtype=torch.bool)
+    keep[nan_rows] = False
+    assert torch.isnan(out[nan_rows]).all()
+    assert torch.equal(out[keep].view(torch.int16), clean[keep].view(torch.int16))
 
 
 def test_unfused_baseline_matches_oracle():
