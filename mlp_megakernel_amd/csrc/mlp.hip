@@ -566,6 +566,15 @@ __global__ __launch_bounds__(Geo<D>::THREADS, MlpCfg<D>::MINW) void mlp_kernel(M
   // where the paths join, stores included.
   HTile<D> ha, hb, hc;
   if (tile < p.num_tiles) load_x<D, PAD>(p, c, tile, ha);
+  // The compiler's memory-counter waits at the loop head are those of the
+  // loop entry and of the back edge merged.  Entered with this load still in
+  // flight, the first use of ha waited as if it had just been issued -- on
+  // every pass, which then also waited for the previous tile's output stores
+  // (the counter completes in order).  Waiting here once leaves only the
+  // back edge's wait: for data loaded a whole tile earlier.  (The builtin,
+  // not inline asm: the compiler's wait insertion sees only the former.)
+  // Encoding: vmcnt 0, expcnt 7 and lgkmcnt 15 (no wait on those two).
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   while (tile < p.num_tiles) {
     int next = claim_tile(&s_next);
     load_x<D, PAD>(p, c, next, hc);
