@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void activation_kernel(const T* X, int64_t ldx
     float x[8];
     load8<T>(X + (int64_t)m * ldx + n, valid, x);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) x[r] = apply_act<ACT>(x[r]);
+    for (int r = 0; r < 8; ++r) x[r] = apply_act<ACT, sizeof(T) == 2>(x[r]);
     store8<T>(Y + (int64_t)m * ldy + n, valid, x);
   }
 }

@@ -386,7 +386,7 @@ __device__ __forceinline__ void epilogue_staged(const GemmParams& p, const f32x4
       const int row = 16 * s + q;
       to4 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = from_f32<TO>(apply_act<ACT>(acc[t][s][r] + bv[r]));
+      for (int r = 0; r < 4; ++r) o[r] = from_f32<TO>(apply_act<ACT, sizeof(TO) == 2>(acc[t][s][r] + bv[r]));
       *(to4*)(region + row * ROWB + ((chunk ^ stage_swz<ROWB>(row)) << 4) + ((b & 1) << 3)) = o;
     }
   }
@@ -543,7 +543,7 @@ __global__ __launch_bounds__(G::THREADS, G::MINW) void gemm16_kernel(GemmParams 
           if (m < p.M) {
             f32x4 o = acc[t][s];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = apply_act<ACT>(o[r] + bv[r]);
+            for (int r = 0; r < 4; ++r) o[r] = apply_act<ACT, sizeof(TO) == 2>(o[r] + bv[r]);
             store4<TO>(Y + (int64_t)m * p.ldy + n, o, valid);
           }
         }
