@@ -207,8 +207,8 @@ def _chain(x, weights):
     Ws = [_f64(w) for w in weights]
     if len(Ws) < 1:
         raise ValueError("need at least one layer")
-    if len(Ws) > 8:
-        raise ValueError("at most 8 layers")
+    if len(Ws) > 16:
+        raise ValueError("at most 16 layers")
     M, d0 = x.shape
     dims = [d0]
     for w in Ws:

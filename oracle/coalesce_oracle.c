@@ -303,8 +303,8 @@ int oracle_mlp_backward(const double* x, const double* const* W, const int64_t* 
   for (int l = 0; l < L; ++l) memset(dW[l], 0, (size_t)(dims[l] * dims[l + 1]) * sizeof(double));
   if (M == 0) return 0;
   /* per-row record: h_0..h_{L-1}, then dz_1..dz_L, then z_1..z_{L-1} */
-  int64_t hoff[9], doff[9], zoff[9], S = 0;
-  if (L > 8) return -1;
+  int64_t hoff[17], doff[17], zoff[17], S = 0;
+  if (L > 16) return -1;
   for (int l = 0; l < L; ++l) { hoff[l] = S; S += dims[l]; }
   for (int l = 1; l <= L; ++l) { doff[l] = S; S += dims[l]; }
   for (int l = 1; l < L; ++l) { zoff[l] = S; S += dims[l]; }

@@ -44,7 +44,7 @@ def _random_chain(seed, dims, M, scale=0.6):
 
 
 @pytest.mark.parametrize("act", ["softplus", "relu", "none"])
-@pytest.mark.parametrize("dims", [(6, 7, 5, 4), (5, 3), (4, 6, 6, 5, 3, 4)])
+@pytest.mark.parametrize("dims", [(6, 7, 5, 4), (5, 3), (4, 6, 6, 5, 3, 4), (3, 4, 2, 3, 4, 3, 2, 4, 3, 3, 2, 4, 3)])
 def test_backward_matches_central_differences(act, dims):
     M = 5
     x, Ws, g = _random_chain(1000 + len(dims), dims, M)
@@ -112,7 +112,7 @@ def test_single_layer_is_the_textbook_product():
         assert np.array_equal(dx, g @ W.T)
 
 
-@pytest.mark.parametrize("L", [2, 3, 5])
+@pytest.mark.parametrize("L", [2, 3, 5, 12, 16])
 def test_identity_weights_product_of_sigmoids(L):
     # W_l = I: out = softplus^(L-1)(x) elementwise, so dx = dout * prod_j sigmoid(z_j)
     # with z_1 = x, z_{j+1} = softplus(z_j); and dW_L = h_{L-1}^T dout.
@@ -217,6 +217,8 @@ def test_backward_rejects_bad_arguments():
     x, Ws, g = _random_chain(1, (4, 4), 3)
     with pytest.raises(ValueError):
         oracle.mlp_backward(x, Ws, g[:, :3])
+    with pytest.raises(ValueError):  # at most 16 layers
+        oracle.mlp_backward(x, [np.eye(4)] * 17, g)
     with pytest.raises(ValueError):
         oracle.mlp_backward(x, [np.ones((5, 4))], g)
     dWs, dx = oracle.mlp_backward(x[:0], Ws, g[:0])
