@@ -222,28 +222,33 @@ namespace {
 // chain runs at kernel width P = 64 if every width is at most 64, else 128
 // (then *square says whether every width equals P).  Depth: P = 128 holds at
 // most 4 layers of weights in LDS, P = 64 at most 8.
+// A chain the MLP kernels run: L = 1..16 layers, fp16, widths multiples of
+// 8 up to 256.  *P_out: the width class (64, 128 or 256) of its widest
+// layer; *resident: all weights fit in LDS at once (widths up to 128 and at
+// most 4 layers, or up to 64 and at most 8), so the resident megakernel
+// (mlp.hip, and the fused backward) runs it -- else the layer-streaming one.
 coalesce_status check_mlp_chain(const void* const* W, const int64_t* dims, int32_t L, int64_t M,
-                                coalesce_dtype dtype, coalesce_act hidden_act, int64_t* P_out, bool* square) {
+                                coalesce_dtype dtype, coalesce_act hidden_act, int64_t* P_out, bool* square,
+                                bool* resident) {
   if (L < 1) return fail(COALESCE_ERR_INVALID_ARGUMENT, "L must be at least 1 (got %d)", (int)L);
   if (!W || !dims) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W or dims is NULL");
   if (M < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative M");
   if (!valid_dtype(dtype)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown dtype");
   if (!valid_act(hidden_act)) return fail(COALESCE_ERR_INVALID_ARGUMENT, "unknown activation");
-  if (L > 8) return fail(COALESCE_ERR_UNSUPPORTED, "at most 8 layers (got %d)", (int)L);
+  if (L > kMaxStreamLayers) return fail(COALESCE_ERR_UNSUPPORTED, "at most %d layers (got %d)", kMaxStreamLayers, (int)L);
   int64_t mx = 0;
   for (int l = 0; l <= L; ++l) {
     if (dims[l] <= 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dims[%d] = %lld is not positive", l, (long long)dims[l]);
-    if (dims[l] % 8 || dims[l] > 128)
-      return fail(COALESCE_ERR_UNSUPPORTED, "MLP width %lld not supported (a multiple of 8, at most 128)",
+    if (dims[l] % 8 || dims[l] > 256)
+      return fail(COALESCE_ERR_UNSUPPORTED, "MLP width %lld not supported (a multiple of 8, at most 256)",
                   (long long)dims[l]);
     if (dims[l] > mx) mx = dims[l];
   }
   if (dtype != COALESCE_F16) return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel takes fp16 only");
   if (hidden_act == COALESCE_ACT_GELU_ERF)
     return fail(COALESCE_ERR_UNSUPPORTED, "the MLP megakernel supports softplus, relu or no hidden activation");
-  const int64_t P = mx <= 64 ? 64 : 128;
-  if (P == 128 && L > 4)
-    return fail(COALESCE_ERR_UNSUPPORTED, "%d layers of width up to 128 do not fit in LDS (at most 4)", (int)L);
+  const int64_t P = mx <= 64 ? 64 : mx <= 128 ? 128 : 256;
+  *resident = P == 64 ? L <= 8 : P == 128 ? L <= 4 : false;
   bool sq = true;
   for (int l = 0; l <= L; ++l) sq = sq && dims[l] == P;
   if (M > kMaxExtent - 256) return fail(COALESCE_ERR_UNSUPPORTED, "M must be below 2^31 - 256");
@@ -273,8 +278,8 @@ coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* 
                                  coalesce_dtype dtype, coalesce_act hidden_act, int64_t num_workgroups, bool train,
                                  bool use_cache, void* stream) {
   int64_t P = 0;
-  bool square = true;
-  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square);
+  bool square = true, resident = true;
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square, &resident);
   if (s != COALESCE_OK) return s;
   if (num_workgroups < 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "negative workgroup count");
   if (num_workgroups > (int64_t)INT32_MAX) return fail(COALESCE_ERR_UNSUPPORTED, "workgroup count too large");
@@ -285,12 +290,21 @@ coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* 
   const Range ro = span(out, M, O, ldo, 2);
   if (overlap(ro, span(x, M, D, ldx, 2))) return fail(COALESCE_ERR_INVALID_ARGUMENT, "out overlaps x");
   MlpParams p{};
+  MlpStreamParams q{};
   for (int l = 0; l < L; ++l) {
     if (overlap(ro, span(W[l], dims[l], dims[l + 1], dims[l + 1], 2)))
       return fail(COALESCE_ERR_INVALID_ARGUMENT, "out overlaps W[%d]", l);
-    p.W[l] = W[l];
+    if (resident)
+      p.W[l] = W[l];
+    else
+      q.W[l] = W[l];
   }
-  for (int l = 0; l <= L; ++l) p.dims[l] = (int)dims[l];
+  for (int l = 0; l <= L; ++l) {
+    if (resident)
+      p.dims[l] = (int)dims[l];
+    else
+      q.dims[l] = (int)dims[l];
+  }
   if (train && L > 1) {
     if (!acts) return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts is NULL");
     for (int l = 0; l + 1 < L; ++l) {
@@ -307,12 +321,32 @@ coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* 
       for (int j = 0; j < l; ++j)
         if (overlap(ra, span(acts[j], M, dims[j + 1], lda, 4)))
           return fail(COALESCE_ERR_INVALID_ARGUMENT, "acts[%d] overlaps acts[%d]", l, j);
-      p.acts[l] = acts[l];
+      if (resident)
+        p.acts[l] = acts[l];
+      else
+        q.acts[l] = acts[l];
     }
   }
   int cus = 0;
   s = current_cus(&cus);
   if (s != COALESCE_OK) return s;
+  if (!resident) {
+    q.x = x;
+    q.out = out;
+    q.ldx = ldx;
+    q.ldo = ldo;
+    q.lda = train ? lda : 0;
+    q.M = (int)M;
+    q.L = (int)L;
+    if (num_workgroups == 0 && !train && use_cache && g_tuned_any.load(std::memory_order_relaxed)) {
+      TuneCfg tc;
+      if (tuned_lookup(mlp_key(current_device(), dims, L, M, hidden_act), &tc)) num_workgroups = tc.grid;
+    }
+    hipError_t e = launch_mlp_stream(q, (int)P, act_code(hidden_act), train && L > 1, (int)num_workgroups, cus,
+                                     (hipStream_t)stream);
+    if (e != hipSuccess) return device_fail(e, "MLP (layer-streaming) launch");
+    return ok();
+  }
   p.x = x;
   p.out = out;
   p.ldx = ldx;
@@ -366,9 +400,12 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
                                       coalesce_dtype dtype, coalesce_act hidden_act, void* workspace,
                                       size_t workspace_bytes, void* stream) {
   int64_t P = 0;
-  bool square = true;
-  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square);
+  bool square = true, resident = true;
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square, &resident);
   if (s != COALESCE_OK) return s;
+  if (!resident)
+    return fail(COALESCE_ERR_UNSUPPORTED, "the backward covers chains whose weights fit in LDS (widths up to 128 "
+                                          "and at most 4 layers, or up to 64 and at most 8)");
   if (!dW) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW is NULL");
   const int64_t D = dims[0], O = dims[L];
   auto wspan = [&](const void* t, int l, int64_t es) { return span(t, dims[l], dims[l + 1], dims[l + 1], es); };
@@ -438,9 +475,12 @@ coalesce_status coalesce_mlp_backward_noalloc(const void* x, int64_t ldx, const 
                                               int64_t ldd, float* const* dW, void* dx, int64_t ldq, int64_t M,
                                               coalesce_dtype dtype, coalesce_act hidden_act, void* stream) {
   int64_t P = 0;
-  bool square = true;
-  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square);
+  bool square = true, resident = true;
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square, &resident);
   if (s != COALESCE_OK) return s;
+  if (!resident)  // (coalesce_mlp_backward rejects it the same way)
+    return coalesce_mlp_backward(x, ldx, W, dims, L, acts, lda, dout, ldd, dW, dx, ldq, M, dtype, hidden_act, nullptr, 0,
+                                 stream);
   int cus = 0;
   if ((s = current_cus(&cus)) != COALESCE_OK) return s;
   const size_t need = mlp_backward_workspace((int)P, (int)L, cus);
@@ -816,8 +856,8 @@ coalesce_status coalesce_autotune_mlp_forward(const void* x, int64_t ldx, const 
                                               coalesce_act hidden_act, int32_t iters, void* workspace,
                                               size_t workspace_bytes, coalesce_tune_report* report, void* stream) {
   int64_t P = 0;
-  bool square = true;
-  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square);
+  bool square = true, resident = true;
+  coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square, &resident);
   if (s != COALESCE_OK) return s;
   std::vector<Range> operands = {span(x, M, dims[0], ldx, 2), span(out, M, dims[L], ldo, 2)};
   for (int l = 0; l < L; ++l) operands.push_back(span(W[l], dims[l], dims[l + 1], dims[l + 1], 2));

@@ -47,6 +47,23 @@ struct MlpParams {
 hipError_t launch_mlp(const MlpParams& p, int D, int L, int hidden_act, bool store_acts, bool pad, int num_workgroups,
                       int num_cus, hipStream_t stream);
 
+// Chains for the layer-streaming megakernel (mlp_stream.hip): up to 16
+// layers of widths up to 256, weights streamed through LDS chunk by chunk.
+constexpr int kMaxStreamLayers = 16;
+struct MlpStreamParams {
+  const void* x;
+  void* out;
+  const void* W[kMaxStreamLayers];
+  float* acts[kMaxStreamLayers];  // training forward: acts[l] = h_{l+1}, fp32, pitch lda
+  int dims[kMaxStreamLayers + 1];
+  int64_t ldx, ldo, lda;
+  int M, L;
+  int num_tiles;  // batches of wave tiles (set by the launcher)
+};
+// P: the width class (64, 128 or 256) the chain's widest layer fits.
+hipError_t launch_mlp_stream(const MlpStreamParams& p, int P, int hidden_act, bool store_acts, int num_workgroups,
+                             int num_cus, hipStream_t stream);
+
 struct MlpBwdParams {
   const void* x;        // M x D fp16, pitch ldx
   const void* dout;     // M x D fp16, pitch ldd: dL/d(out)

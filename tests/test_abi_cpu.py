@@ -84,12 +84,21 @@ def mlp(D=128, L=3, dims=None, **kw):
     (dict(L=0), INV), (dict(M=-1), INV), (dict(g=-1), INV), (dict(dt=5), INV), (dict(act=4), INV),
     (dict(x=None), INV), (dict(out=None), INV), (dict(ldx=100), INV), (dict(ldo=127), INV),
     (dict(dt=mk.BF16), UNS), (dict(act=mk.ACT_GELU_ERF), UNS),
-    (dict(D=100), UNS), (dict(D=136), UNS), (dict(D=128, L=5), UNS), (dict(D=64, L=9), UNS),
-    (dict(dims=[128, 60, 128, 128]), UNS), (dict(L=5, dims=[64, 128, 64, 64, 64, 64]), UNS),
+    (dict(D=100), UNS), (dict(D=264, ldx=264, ldo=264), UNS), (dict(D=64, L=17), UNS),
+    (dict(dims=[128, 60, 128, 128]), UNS), (dict(L=3, dims=[256, 264, 64, 64]), UNS),
     (dict(x=P + 2), UNS), (dict(ldx=132), UNS),
 ])
 def test_mlp_rejects_before_launch(kw, status):
     assert mlp(**kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(D=136, ldx=136, ldo=136), dict(D=256, ldx=256, ldo=256), dict(D=128, L=5),
+                                dict(D=64, L=9), dict(D=64, L=16), dict(L=5, dims=[64, 128, 64, 64, 64, 64])])
+def test_mlp_accepts_chains_beyond_lds(kw):
+    # deeper or wider than the resident kernel holds: the layer-streaming
+    # kernel takes them, so validation passes and the call reaches the device
+    # query (which fails here, without a GPU)
+    assert mlp(**kw) == mk.ERR_DEVICE
 
 
 def test_mlp_empty_batch_is_ok():
@@ -126,7 +135,7 @@ def mlp_train(D=128, L=3, **kw):
     (dict(acts=[P * 256 + 4, P * 320]), UNS), (dict(lda=130), UNS), (dict(lda=(1 << 24) + 4), UNS),
     (dict(acts=[P * 64, P * 320]), INV),        # acts[0] overlaps out
     (dict(acts=[P * 256, P * 256 + 512]), INV),  # acts overlap each other
-    (dict(act=mk.ACT_GELU_ERF), UNS), (dict(D=128, L=5), UNS), (dict(x=None), INV),
+    (dict(act=mk.ACT_GELU_ERF), UNS), (dict(D=64, L=17), UNS), (dict(x=None), INV),
 ])
 def test_mlp_forward_train_rejects_before_launch(kw, status):
     assert mlp_train(**kw) == status
