@@ -177,7 +177,7 @@ def main():
         acts = [torch.empty((w.M, d), dtype=torch.float32, device=dev) for d in w.dims[1:-1]]
         dW = [torch.empty((w.dims[l], w.dims[l + 1]), dtype=torch.float32, device=dev) for l in range(w.L)]
         dx = torch.empty_like(x)
-        ws = torch.empty(mk.mlp_backward_workspace_size(w.dims), dtype=torch.uint8, device=dev)
+        ws = torch.empty(mk.mlp_backward_workspace_size(w.dims, w.M), dtype=torch.uint8, device=dev)
 
         def fwd():
             mk.mlp_forward_train(x, Ws, out=out, acts=acts)
@@ -411,7 +411,7 @@ def main():
             out = torch.empty((w.M, w.dims[-1]), dtype=torch.float16, device=dev)
             dW = [torch.empty(v.shape, dtype=torch.float32, device=dev) for v in vs]
             dx = torch.empty_like(x)
-            wsp = torch.empty(mk.mlp_backward_workspace_size(w.dims), dtype=torch.uint8, device=dev)
+            wsp = torch.empty(mk.mlp_backward_workspace_size(w.dims, w.M), dtype=torch.uint8, device=dev)
 
             def wn_step():
                 mk.weight_norm(vs, gs, Ws)
@@ -444,7 +444,7 @@ def main():
             acts = [torch.empty((w.M, H), dtype=torch.float32, device=dev)[:, :d] for d in w.dims[1:-1]]
             dW = [torch.empty(t.shape, dtype=torch.float32, device=dev) for t in Ws]
             dx = torch.empty_like(x)
-            wsp = torch.empty(mk.mlp_backward_workspace_size(w.dims), dtype=torch.uint8, device=dev)
+            wsp = torch.empty(mk.mlp_backward_workspace_size(w.dims, w.M), dtype=torch.uint8, device=dev)
 
             def fwd():
                 mk.mlp_forward(x, Ws, out=out)

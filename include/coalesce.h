@@ -138,10 +138,15 @@ coalesce_status coalesce_mlp_forward_train(const void* x, int64_t ldx, const voi
 
 /*
  * Device workspace in bytes that coalesce_mlp_backward needs for this chain
- * on the current device (one partial weight gradient per compute unit).
- * Returns 0 for an unsupported width or depth or a failed device query.
+ * and M rows on the current device.  Chains whose weights fit in LDS (widths
+ * up to 64 and at most 8 layers, or up to 128 and at most 4) need one
+ * partial weight gradient per compute unit, whatever M; the others (run
+ * layer by layer) need the partial sums of their largest layer plus, for
+ * L >= 2, one (L == 2) or two fp16 buffers of M x max(dims[1..L-1]) for the
+ * hidden gradients.  Returns 0 for an unsupported width or depth, a negative
+ * or too large M, or a failed device query.
  */
-size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L);
+size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L, int64_t M);
 
 /*
  * Backward of the MLP chain ("MLP Megakernel" README, "Key ideas": the
@@ -165,19 +170,24 @@ size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L);
  *   dW        HOST array of L device pointers, each dims[l] x dims[l+1] fp32,
  *             dense row-major (the x @ W orientation of W[l]), overwritten
  *   dx        device, M x dims[0] fp16 (ldq), written; or NULL to skip it
- *   workspace device, at least coalesce_mlp_backward_workspace_size(dims, L)
- *             bytes, 16-byte aligned; its contents on entry are ignored
+ *   workspace device, at least coalesce_mlp_backward_workspace_size(dims, L, M)
+ *             bytes, 16-byte aligned, not overlapping any other argument;
+ *             its contents on entry are ignored
  * Pitches are at least the operand's width and at most 2^24, with 16-byte
- * aligned rows.  Two kernels run
- * on `stream`: the fused backward (one persistent workgroup per compute
- * unit; each sums its rows' weight-gradient terms in registers) and a
- * reduction that adds the per-workgroup sums in a fixed order, so repeated
- * calls give identical bits.  M == 0 gives dW = 0.  Supported chains as
- * coalesce_mlp_forward (non-square ones run padded and write only the true
- * dims[l] x dims[l+1] of each dW and the true columns of dx).  Outputs must
- * not overlap the inputs, each other or
- * the workspace.  Calls that share a workspace must be ordered on one
- * stream.
+ * aligned rows.  Chains whose weights fit in LDS (widths up to 64 and at most
+ * 8 layers, or up to 128 and at most 4) run two kernels on `stream`: the
+ * fused backward over all layers (one persistent workgroup per compute unit;
+ * each sums its rows' weight-gradient terms in registers) and a reduction
+ * that adds the per-workgroup sums in a fixed order.  The other chains that
+ * coalesce_mlp_forward supports (up to 16 layers, widths up to 256) run
+ * layer by layer, l = L-1 .. 0: one fused kernel per layer computes dz_l (or
+ * dx) and the per-workgroup sums of dW[l] from the same row tiles, with dz_l
+ * kept as fp16 in the workspace (the precision in which the next layer uses
+ * it either way), then the reduction of dW[l].  Either way repeated calls
+ * give identical bits.  M == 0 gives dW = 0.  Non-square chains write only
+ * the true dims[l] x dims[l+1] of each dW and the true columns of dx.
+ * Outputs must not overlap the inputs, each other or the workspace.  Calls
+ * that share a workspace must be ordered on one stream.
  */
 coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
                                       int32_t L, const float* const* acts, int64_t lda, const void* dout,
@@ -188,15 +198,19 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
 /*
  * coalesce_mlp_backward without the workspace argument, for callers that
  * cannot allocate device memory: code under HIP graph capture, tight serving
- * loops, harnesses that forbid allocation.  The per-workgroup partial weight
- * gradients go to a scratch array of 64 MiB (67108864 bytes) that the library
- * keeps in device memory, one per device, for the life of the process; the
- * call itself allocates nothing and clears nothing (the backward overwrites
- * every partial sum the reduction reads).  A chain whose partial sums
- * (coalesce_mlp_backward_workspace_size) exceed 64 MiB is rejected with
- * COALESCE_ERR_UNSUPPORTED before anything is launched; every chain
- * coalesce_mlp_backward supports fits on a device of up to 256 compute
- * units.  Every call on one device shares that device's scratch, which keeps
+ * loops, harnesses that forbid allocation.  The workspace (the per-workgroup
+ * partial weight gradients, and for chains run layer by layer the fp16
+ * hidden gradients) is a scratch array of 64 MiB (67108864 bytes) that the
+ * library keeps in device memory, one per device, for the life of the
+ * process; the call itself allocates nothing and clears nothing (the
+ * backward overwrites every value it reads back).  A call whose workspace
+ * (coalesce_mlp_backward_workspace_size(dims, L, M)) exceeds 64 MiB is
+ * rejected with COALESCE_ERR_UNSUPPORTED before anything is launched: every
+ * chain whose weights fit in LDS fits on a device of up to 256 compute
+ * units, whatever M; a chain run layer by layer fits while its partial sums
+ * and hidden-gradient buffers do (e.g. 6 layers 128 wide up to 98304
+ * rows on 256 compute units).  Every call on one device shares that
+ * device's scratch, which keeps
  * the last call's contents: calls that can overlap on one device (streams
  * without an order between them, several host threads) race and give wrong
  * gradients, so order them on one stream.  Otherwise the arguments, the

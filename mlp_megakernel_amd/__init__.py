@@ -33,7 +33,7 @@ SIGNATURES = {
     "coalesce_mlp_forward": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _i64, _i32, _i32, _p]),
     "coalesce_mlp_forward_grid": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _i64, _i32, _i32, _i64, _p]),
     "coalesce_mlp_forward_train": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _p, _i64, _i64, _i32, _i32, _p]),
-    "coalesce_mlp_backward_workspace_size": (_sz, [_p, _i32]),
+    "coalesce_mlp_backward_workspace_size": (_sz, [_p, _i32, _i64]),
     "coalesce_mlp_backward": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _p, _i64, _p, _p, _i64, _i64, _i32, _i32,
                                      _p, _sz, _p]),
     "coalesce_mlp_backward_noalloc": (_i32, [_p, _i64, _p, _p, _i32, _p, _i64, _p, _i64, _p, _p, _i64, _i64, _i32,
@@ -259,10 +259,11 @@ def mlp_forward_train(x: torch.Tensor, weights: Sequence[torch.Tensor], hidden_a
     return out, list(acts)
 
 
-def mlp_backward_workspace_size(dims: Sequence[int]) -> int:
-    """Bytes of workspace coalesce_mlp_backward needs for this chain here."""
+def mlp_backward_workspace_size(dims: Sequence[int], M: int = 0) -> int:
+    """Bytes of workspace coalesce_mlp_backward needs for this chain and M
+    rows here (chains whose weights fit in LDS need the same for every M)."""
     L = len(dims) - 1
-    n = int(load_library().coalesce_mlp_backward_workspace_size(_dims_array(dims), L))
+    n = int(load_library().coalesce_mlp_backward_workspace_size(_dims_array(dims), L, int(M)))
     if n == 0:
         raise CoalesceError(ERR_UNSUPPORTED, "no backward for dims %s on this device" % (list(dims),))
     return n
@@ -273,8 +274,9 @@ def mlp_backward(x: torch.Tensor, weights: Sequence[torch.Tensor], acts: Sequenc
                  dW: Optional[Sequence[torch.Tensor]] = None, dx: Optional[torch.Tensor] = None,
                  workspace: Optional[torch.Tensor] = None, stream=None):
     """(dW list (fp32), dx or None): the backward of the chain from the
-    stored activations, one fused kernel plus a fixed-order reduction
-    (coalesce_mlp_backward)."""
+    stored activations (coalesce_mlp_backward): one fused kernel plus a
+    fixed-order reduction, or for chains whose weights do not fit in LDS one
+    fused kernel and one reduction per layer."""
     lib = load_library()
     M, ldx, dims = _chain_dims(x, weights)
     L = len(weights)
@@ -298,7 +300,7 @@ def mlp_backward(x: torch.Tensor, weights: Sequence[torch.Tensor], acts: Sequenc
             raise ValueError("dx must be M x dims[0] of x's dtype")
     else:
         dx = None
-    need = mlp_backward_workspace_size(dims)
+    need = mlp_backward_workspace_size(dims, M)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     _check(lib.coalesce_mlp_backward(_ptr(x), ldx, _ptr_array(weights), _dims_array(dims), L,

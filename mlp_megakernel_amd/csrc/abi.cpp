@@ -380,18 +380,28 @@ coalesce_status coalesce_mlp_forward_train(const void* x, int64_t ldx, const voi
   return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, acts, lda, M, dtype, hidden_act, 0, true, false, stream);
 }
 
-size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L) {
-  if (!dims || L < 1 || L > 8) return 0;
+// Workspace of the backward: the fused kernel's per-workgroup partial sums
+// (chains whose weights fit in LDS), or the layer-by-layer kernels' partial
+// sums of one layer plus the fp16 dz buffers of M rows.
+size_t backward_workspace(const int64_t* dims, int L, int64_t M, int64_t P, bool resident, int cus) {
+  if (resident) return mlp_backward_workspace((int)P, L, cus);
+  int d[kMaxStreamLayers + 1];
+  for (int l = 0; l <= L; ++l) d[l] = (int)dims[l];
+  return mlp_backward_stream_workspace(d, L, M, cus);
+}
+
+size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L, int64_t M) {
+  if (!dims || L < 1 || L > kMaxStreamLayers || M < 0 || M > kMaxExtent - 256) return 0;
   int64_t mx = 0;
   for (int l = 0; l <= L; ++l) {
-    if (dims[l] <= 0 || dims[l] % 8 || dims[l] > 128) return 0;
+    if (dims[l] <= 0 || dims[l] % 8 || dims[l] > 256) return 0;
     if (dims[l] > mx) mx = dims[l];
   }
-  const int64_t P = mx <= 64 ? 64 : 128;  // the kernel width the chain runs at
-  if (P == 128 && L > 4) return 0;
+  const int64_t P = mx <= 64 ? 64 : mx <= 128 ? 128 : 256;
+  const bool resident = P == 64 ? L <= 8 : P == 128 ? L <= 4 : false;
   int cus = 0;
   if (current_cus(&cus) != COALESCE_OK) return 0;
-  return mlp_backward_workspace((int)P, (int)L, cus);
+  return backward_workspace(dims, L, M, P, resident, cus);
 }
 
 coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
@@ -403,20 +413,13 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
   bool square = true, resident = true;
   coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square, &resident);
   if (s != COALESCE_OK) return s;
-  if (!resident)
-    return fail(COALESCE_ERR_UNSUPPORTED, "the backward covers chains whose weights fit in LDS (widths up to 128 "
-                                          "and at most 4 layers, or up to 64 and at most 8)");
   if (!dW) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW is NULL");
   const int64_t D = dims[0], O = dims[L];
   auto wspan = [&](const void* t, int l, int64_t es) { return span(t, dims[l], dims[l + 1], dims[l + 1], es); };
-  MlpBwdParams p{};
   for (int l = 0; l < L; ++l) {
     if (!dW[l]) return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW[%d] is NULL", l);
     if (((uintptr_t)dW[l]) & 3u) return fail(COALESCE_ERR_UNSUPPORTED, "dW[%d] must be 4-byte aligned", l);
-    p.W[l] = W[l];
-    p.dW[l] = dW[l];
   }
-  for (int l = 0; l <= L; ++l) p.dims[l] = (int)dims[l];
   if (M > 0) {
     if ((s = check_rows(x, ldx, D, 2, "x")) != COALESCE_OK) return s;
     if ((s = check_rows(dout, ldd, O, 2, "dout")) != COALESCE_OK) return s;
@@ -426,7 +429,6 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
         char name[16];
         snprintf(name, sizeof(name), "acts[%d]", l);
         if ((s = check_rows(acts[l], lda, dims[l + 1], 4, name)) != COALESCE_OK) return s;
-        p.acts[l] = acts[l];
       }
     }
     if (dx) {
@@ -441,7 +443,7 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
   int cus = 0;
   s = current_cus(&cus);
   if (s != COALESCE_OK) return s;
-  const size_t need = mlp_backward_workspace((int)P, (int)L, cus);
+  const size_t need = backward_workspace(dims, L, M, P, resident, cus);
   if (!workspace) return fail(COALESCE_ERR_INVALID_ARGUMENT, "workspace is NULL");
   if (!aligned16(workspace)) return fail(COALESCE_ERR_UNSUPPORTED, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)
@@ -454,18 +456,53 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
     for (int j = 0; j < L; ++j)
       if ((j != l && overlap(rg, wspan(dW[j], j, 4))) || overlap(rg, wspan(W[j], j, 2)))
         return fail(COALESCE_ERR_INVALID_ARGUMENT, "dW[%d] overlaps another weight or gradient", l);
+    if (overlap(rw, wspan(W[l], l, 2))) return fail(COALESCE_ERR_INVALID_ARGUMENT, "W[%d] overlaps the workspace", l);
   }
-  p.x = x;
-  p.dout = dout;
-  p.dx = M > 0 ? dx : nullptr;
-  p.partial = (float*)workspace;
-  p.ldx = ldx;
-  p.ldd = ldd;
-  p.lda = lda;
-  p.ldq = ldq;
-  p.M = (int)M;
-  (void)square;
-  hipError_t e = launch_mlp_backward(p, (int)P, (int)L, act_code(hidden_act), cus, (hipStream_t)stream);
+  if (M > 0) {
+    bool bad = overlap(rw, span(x, M, D, ldx, 2)) || overlap(rw, span(dout, M, O, ldd, 2)) ||
+               (dx && overlap(rw, span(dx, M, D, ldq, 2)));
+    for (int l = 0; l + 1 < L; ++l) bad = bad || overlap(rw, span(acts[l], M, dims[l + 1], lda, 4));
+    if (bad) return fail(COALESCE_ERR_INVALID_ARGUMENT, "the workspace overlaps x, dout, dx or an activation");
+  }
+  hipError_t e;
+  if (resident) {
+    MlpBwdParams p{};
+    for (int l = 0; l < L; ++l) {
+      p.W[l] = W[l];
+      p.dW[l] = dW[l];
+    }
+    for (int l = 0; l <= L; ++l) p.dims[l] = (int)dims[l];
+    for (int l = 0; M > 0 && l + 1 < L; ++l) p.acts[l] = acts[l];
+    p.x = x;
+    p.dout = dout;
+    p.dx = M > 0 ? dx : nullptr;
+    p.partial = (float*)workspace;
+    p.ldx = ldx;
+    p.ldd = ldd;
+    p.lda = lda;
+    p.ldq = ldq;
+    p.M = (int)M;
+    (void)square;
+    e = launch_mlp_backward(p, (int)P, (int)L, act_code(hidden_act), cus, (hipStream_t)stream);
+  } else {
+    MlpStreamBwdParams q{};
+    for (int l = 0; l < L; ++l) {
+      q.W[l] = W[l];
+      q.dW[l] = dW[l];
+    }
+    for (int l = 0; l <= L; ++l) q.dims[l] = (int)dims[l];
+    for (int l = 0; M > 0 && l + 1 < L; ++l) q.acts[l] = acts[l];
+    q.x = x;
+    q.dout = dout;
+    q.dx = M > 0 ? dx : nullptr;
+    q.ldx = ldx;
+    q.ldd = ldd;
+    q.lda = lda;
+    q.ldq = ldq;
+    q.M = (int)M;
+    q.L = L;
+    e = launch_mlp_backward_stream(q, (int)P, act_code(hidden_act), cus, workspace, (hipStream_t)stream);
+  }
   if (e != hipSuccess) return device_fail(e, "MLP backward launch");
   return ok();
 }
@@ -478,16 +515,13 @@ coalesce_status coalesce_mlp_backward_noalloc(const void* x, int64_t ldx, const 
   bool square = true, resident = true;
   coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square, &resident);
   if (s != COALESCE_OK) return s;
-  if (!resident)  // (coalesce_mlp_backward rejects it the same way)
-    return coalesce_mlp_backward(x, ldx, W, dims, L, acts, lda, dout, ldd, dW, dx, ldq, M, dtype, hidden_act, nullptr, 0,
-                                 stream);
   int cus = 0;
   if ((s = current_cus(&cus)) != COALESCE_OK) return s;
-  const size_t need = mlp_backward_workspace((int)P, (int)L, cus);
+  const size_t need = backward_workspace(dims, L, M, P, resident, cus);
   const size_t have = mlp_backward_scratch_bytes();
   if (need > have)
     return fail(COALESCE_ERR_UNSUPPORTED,
-                "this chain needs %zu bytes of partial sums, more than the %zu bytes of the library's scratch", need,
+                "this chain needs %zu bytes of workspace, more than the %zu bytes of the library's scratch", need,
                 have);
   void* scratch = nullptr;
   hipError_t e = mlp_backward_scratch(&scratch);

@@ -90,6 +90,26 @@ hipError_t launch_mlp_backward(MlpBwdParams p, int D, int L, int hidden_act, int
 size_t mlp_backward_scratch_bytes();
 hipError_t mlp_backward_scratch(void** ptr);
 
+// Backward of a chain the layer-streaming forward runs (weights beyond LDS):
+// one launch per layer, l = L-1 .. 0, each followed by the reduction of its
+// per-workgroup weight-gradient sums.
+struct MlpStreamBwdParams {
+  const void* x;                         // M x dims[0] fp16 (ldx)
+  const void* dout;                      // M x dims[L] fp16 (ldd)
+  const void* W[kMaxStreamLayers];       // dims[l] x dims[l+1] fp16, dense
+  const float* acts[kMaxStreamLayers];   // acts[l] = h_{l+1}, M x dims[l+1] fp32 (lda)
+  void* dx;                              // M x dims[0] fp16 (ldq), or nullptr
+  float* dW[kMaxStreamLayers];           // dims[l] x dims[l+1] fp32, dense
+  int dims[kMaxStreamLayers + 1];
+  int64_t ldx, ldd, lda, ldq;
+  int M, L;
+};
+// Workspace (bytes) of launch_mlp_backward_stream: the per-workgroup partial
+// sums of the largest layer and up to two M-row fp16 buffers for dz.
+size_t mlp_backward_stream_workspace(const int* dims, int L, int64_t M, int num_cus);
+hipError_t launch_mlp_backward_stream(const MlpStreamBwdParams& p, int P, int hidden_act, int num_cus,
+                                      void* workspace, hipStream_t stream);
+
 constexpr int kMaxWnLayers = 16;
 struct WnParams {
   const void* v[kMaxWnLayers];  // fp16 din x dout, dense

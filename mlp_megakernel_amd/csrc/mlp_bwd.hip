@@ -207,16 +207,6 @@ __device__ __forceinline__ void load_acts(const float* base, int64_t ld, uint32_
   }
 }
 
-__device__ __forceinline__ void lds_write64(uint32_t addr, u32x2 v) {
-  *(__attribute__((address_space(3))) u32x2*)(uintptr_t)addr = v;
-}
-__device__ __forceinline__ void lds_write128(uint32_t addr, u32x4 v) {
-  *(__attribute__((address_space(3))) u32x4*)(uintptr_t)addr = v;
-}
-__device__ __forceinline__ i16x4 lds_tr(uint32_t addr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)addr);
-}
-
 // Stage a B-layout fp16 tile (dout or x) into a staging buffer.
 template <int D>
 __device__ __forceinline__ void stage_b(uint32_t buf, const BLane<D>& c, const FragB<D>& f) {
@@ -250,25 +240,6 @@ __device__ __forceinline__ void pack_rows(const RowsF32<D>& a, FragB<D>& f) {
       f.v[s][t >> 1][(t & 1) * 2] = pack_f16(a.v[s][t][0], a.v[s][t][1]);
       f.v[s][t >> 1][(t & 1) * 2 + 1] = pack_f16(a.v[s][t][2], a.v[s][t][3]);
     }
-}
-
-// dz = g * act'(z) from the stored output h = act(z), in fp32:
-//   softplus: act'(z) = sigmoid(z) = 1 - e^{-h} (e^{-h} = 1 / (1 + e^z) for
-//     h = ln(1 + e^z)).  The hardware 2^x on -h log2(e) gives e^{-h} to about
-//     one ulp, and 1 - e^{-h} is then exact, so the derivative is off by at
-//     most 2^-23 in absolute terms: below the resolution of the fp16 dz it
-//     feeds wherever dz is a normal fp16 number;
-//   relu: g where h > 0, else 0 (a select, so an infinite g gives 0 there);
-//   none: g.
-template <int ACT>
-__device__ __forceinline__ float apply_grad(float g, float h) {
-  if constexpr (ACT == ACT_SOFTPLUS) {
-    return g * (1.0f - __builtin_amdgcn_exp2f(h * -1.44269504088896341f));
-  } else if constexpr (ACT == ACT_RELU) {
-    return h > 0.0f ? g : 0.0f;
-  } else {
-    return g;
-  }
 }
 
 // Issue order of one pipeline step (as in the forward megakernel): NM MFMAs,

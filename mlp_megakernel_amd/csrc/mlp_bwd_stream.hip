@@ -1,0 +1,415 @@
+// Layer-by-layer backward of the MLP chains whose weights do not all fit in
+// LDS at once (the chains the layer-streaming forward runs: up to 16 layers,
+// widths up to 256, each layer at its own width).  The quantities are those
+// of the fused backward ("MLP Megakernel" README, "Key ideas": the fp32
+// activations of the training forward, the softplus derivative recovered
+// from them, fp16 only for the matrix-core operands, fp32 accumulation),
+// computed one layer per launch, l = L-1 .. 0, with dz_L = dout:
+//   dW_l = h_l^T dz_{l+1}                    (summed over all rows)
+//   dz_l = (dz_{l+1} W_l^T) * act'(z_l)      (l > 0, stored as fp16)
+//   dx   =  dz_1 W_0^T                       (l = 0, optional)
+// Both products of a layer read the same two row tiles (dz_{l+1} and h_l),
+// so one kernel computes them together and reads each tile from HBM once.
+// dz_l goes to a workspace in fp16, the precision in which the next layer's
+// MFMAs take it anyway: the results are those of one fused pass over all
+// layers, up to the order in which per-workgroup dW sums are added.  (The
+// README's own backward switches to per-layer GEMMs for large row counts;
+// here each layer is one fused kernel instead of two GEMMs and an
+// elementwise pass.)
+//
+// Design for gfx950 (one workgroup of 8 waves per CU, persistent over
+// 32-row tiles; I = dims[l], J = dims[l+1]):
+//   * W_l (I x J fp16, at most 128 KiB) sits in LDS for the whole launch in
+//     its natural layout: a row of W_l is the A operand of the data product
+//     dz_l^T = W_l dz_{l+1}^T, read as 16-byte pieces;
+//   * each wave owns TI 16-unit tiles of the I units: it computes dz_l of
+//     those units for the tile's rows (B = dz_{l+1} rows, from LDS) and sums
+//     dW_l over the same units and all J in registers;
+//   * the weight-gradient contraction runs over rows, so dz_{l+1} and h_l
+//     (as fp16) are staged in LDS and read back with the transposing
+//     ds_read_b64_tr_b16.  Computing dW^T = dz^T h leaves 4 consecutive j of
+//     one i in each lane, so the partial sums leave in 16-byte stores;
+//   * the next tile's dz_{l+1} and h_l are loaded into registers while the
+//     current tile is computed; h_l's fp32 registers sit in the data
+//     product's result layout (4 units of one row per lane), so the
+//     derivative needs no data movement, and the same registers give the
+//     fp16 copy staged for the weight gradient;
+//   * each workgroup writes its partial dW_l; a second kernel adds the
+//     partials in a fixed order, so repeated calls give the same bits.
+#include <algorithm>
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+#include "mlp_common.hpp"
+
+namespace coalesce {
+namespace {
+
+// Geometry per width class P (the chain's widest layer, 128 or 256; chains
+// up to 64 wide run at 128 with the units past their widths skipped).
+template <int P>
+struct LGeo {
+  static constexpr int WAVES = 8;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int TI = P / 128;                    // 16-unit i tiles per wave: 8 waves cover P units
+  static constexpr int R = 32;                          // rows per tile: one 32-deep weight-gradient k step
+  static constexpr int ROWB = 2 * P;                    // bytes of a staged LDS row (W_l, dz, h)
+  static constexpr int PIECES = P / 8;                  // 16-byte pieces per staged row
+  static constexpr int KS = P / 32;                     // 32-deep data-product k steps at most
+  static constexpr int NJ = P / 16;                     // 16-unit j tiles at most
+  static constexpr int ZP = R * PIECES / THREADS;       // dz pieces a thread loads per tile
+};
+
+struct LayerArgs {
+  const void* dz;    // M x J fp16 (ldz): dLoss/dz_{l+1}
+  const void* h;     // M x I: h_l in fp32 (l > 0) or x in fp16 (l = 0), pitch ldh
+  const void* W;     // I x J fp16, dense
+  void* out;         // M x I fp16 (ldo): dz_l (l > 0), dx (l = 0), or nullptr
+  float* partial;    // grid x I x J fp32
+  int64_t ldz, ldh, ldo;
+  int I, J, M, num_tiles;
+};
+
+// Staged dz_{l+1} / h_l rows: 16-byte piece c of row r sits at c ^ zsw(r).
+// zsw depends on r mod 16 only; it takes 16 distinct values over any 16
+// consecutive rows (the 16-byte reads of the data product: 16 rows, one
+// piece), and zsw >> 1 takes 8 distinct values over any 8 consecutive rows
+// (a transposing read covers 8 consecutive rows, two neighbouring pieces
+// each).  Weight rows use c ^ (i mod 16): 16 consecutive rows, one piece.
+__device__ __forceinline__ int zsw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
+constexpr uint32_t L_OFF_NONE = 0x80000000u;  // past every resource (all span less than 2^31 bytes)
+__device__ __forceinline__ uint32_t lmask(bool ok, uint32_t off) { return ok ? off : L_OFF_NONE; }
+
+// Buffer resource over rows [first, first + n) of a matrix (pitch ld
+// elements of es bytes, M rows): rows past M read as zero, stores to them
+// are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* base, int M, int64_t first, int n, int64_t ld,
+                                                            int es) {
+  const int64_t rows = min((int64_t)n, max((int64_t)0, (int64_t)M - first));
+  const char* p = (const char*)base + first * ld * es;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)((uint32_t)rows * (uint32_t)(ld * es)),
+                                           0x00020000);
+}
+
+template <int P, int MODE>
+struct TileRegs {
+  // dz_{l+1}: pieces threadIdx.x + THREADS e of the tile (row-major, PIECES per row)
+  u32x4 z[LGeo<P>::ZP];
+  // h_l of the wave's units: rows 16 nt + q, units 16 it + 4 g .. + 3; fp32
+  // for hidden layers, fp16 (x) for the first layer
+  typename std::conditional<MODE == 1, f32x4, u32x2>::type h[LGeo<P>::TI][2];
+};
+
+template <int P, int MODE>
+__device__ __forceinline__ void load_tile(const LayerArgs& a, int tile, int w, int q, int g, TileRegs<P, MODE>& r) {
+  using G = LGeo<P>;
+  const int64_t row0 = (int64_t)tile * G::R;
+  const __amdgpu_buffer_rsrc_t rz = rows_rsrc(a.dz, a.M, row0, G::R, a.ldz, 2);
+#pragma unroll
+  for (int e = 0; e < G::ZP; ++e) {
+    const int idx = threadIdx.x + G::THREADS * e;
+    const int row = idx / G::PIECES, c = idx % G::PIECES;
+    r.z[e] = __builtin_amdgcn_raw_buffer_load_b128(
+        rz, lmask(8 * c < a.J, (uint32_t)row * (uint32_t)(a.ldz * 2) + 16u * (uint32_t)c), 0, 0);
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const __amdgpu_buffer_rsrc_t rh = rows_rsrc(a.h, a.M, row0 + 16 * nt, 16, a.ldh, MODE == 1 ? 4 : 2);
+#pragma unroll
+    for (int t = 0; t < G::TI; ++t) {
+      const int u = 16 * (G::TI * w + t) + 4 * g;  // the lane's first unit
+      if constexpr (MODE == 1)
+        r.h[t][nt] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rh, lmask(u < a.I, (uint32_t)q * (uint32_t)(a.ldh * 4) + 4u * (uint32_t)u), 0, 0));
+      else
+        r.h[t][nt] = __builtin_amdgcn_raw_buffer_load_b64(
+            rh, lmask(u < a.I, (uint32_t)q * (uint32_t)(a.ldh * 2) + 2u * (uint32_t)u), 0, 0);
+    }
+  }
+}
+
+// MODE 1: hidden layer l > 0 (dz_l with the derivative, h_l in fp32);
+// MODE 2: first layer with dx (no derivative, h_0 = x in fp16);
+// MODE 0: first layer, weight gradient only.
+template <int P, int ACT, int MODE>
+__global__ __launch_bounds__(LGeo<P>::THREADS, 1) void mlp_layer_bwd_kernel(LayerArgs a) {
+  using G = LGeo<P>;
+  constexpr int TI = G::TI, R = G::R, ROWB = G::ROWB, PIECES = G::PIECES, KS = G::KS, NJ = G::NJ;
+  constexpr bool DATA = MODE != 0;
+  constexpr int WROWS = DATA ? P : 0;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[(WROWS + 2 * R) * ROWB];
+  const uint32_t sW = lds_addr(lds), sZ = sW + WROWS * ROWB, sH = sZ + R * ROWB;
+  const int I = a.I, J = a.J;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, q = lane & 15, g = lane >> 4;
+
+  if constexpr (DATA) {
+    // W_l rows (zero past I up to the next 16, and past J up to P)
+    const int rows = (I + 15) & ~15;
+    for (int idx = threadIdx.x; idx < rows * PIECES; idx += G::THREADS) {
+      const int i = idx / PIECES, c = idx % PIECES;
+      u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+      if (i < I && 8 * c < J) v = *(const u32x4*)((const _Float16*)a.W + (int64_t)i * J + 8 * c);
+      lds_write128(sW + (uint32_t)(i * ROWB + ((c ^ (i & 15)) << 4)), v);
+    }
+  }
+
+  const int ksn = (J + 31) >> 5;  // data-product k steps
+  const int njn = (J + 15) >> 4;  // j tiles
+  bool on[TI];                    // the wave's i tiles that hold units below I
+#pragma unroll
+  for (int t = 0; t < TI; ++t) on[t] = 16 * (TI * w + t) < I;
+
+  // per-lane LDS offsets
+  const uint32_t zrow = (uint32_t)(q * ROWB);
+  const uint32_t bz = zrow + (uint32_t)((g ^ zsw(q)) << 4);           // data-product B piece, k step 0
+  const int rt = 4 * g + (q >> 2);                                    // transposing read: row of a 32-row chunk
+  const uint32_t trk = (uint32_t)(rt * ROWB + ((((q & 3) >> 1) ^ zsw(rt)) << 4) + ((q & 1) << 3));
+  const uint32_t hst = zrow + (uint32_t)((((g >> 1) ^ zsw(q)) << 4) + ((g & 1) << 3));  // h staging, i tile 0
+
+  f32x4 dw[TI][NJ];
+#pragma unroll
+  for (int t = 0; t < TI; ++t)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) dw[t][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  TileRegs<P, MODE> nx;
+  int tile = blockIdx.x;
+  if (tile < a.num_tiles) load_tile<P, MODE>(a, tile, w, q, g, nx);
+  // nothing of the prologue stays in flight into the loop
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  for (; tile < a.num_tiles; tile += gridDim.x) {
+    const int next = tile + gridDim.x;
+    __syncthreads();  // the previous tile's reads of sZ are done (and W_l is staged)
+#pragma unroll
+    for (int e = 0; e < G::ZP; ++e) {
+      const int idx = threadIdx.x + G::THREADS * e;
+      const int row = idx / PIECES, c = idx % PIECES;
+      lds_write128(sZ + (uint32_t)(row * ROWB + ((c ^ zsw(row)) << 4)), nx.z[e]);
+    }
+    // the wave's own h columns (only this wave reads them back)
+    typename std::conditional<MODE == 1, f32x4, u32x2>::type hc[TI][2];
+#pragma unroll
+    for (int t = 0; t < TI; ++t)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        hc[t][nt] = nx.h[t][nt];
+        u32x2 v;
+        if constexpr (MODE == 1)
+          v = (u32x2){pack_f16(hc[t][nt][0], hc[t][nt][1]), pack_f16(hc[t][nt][2], hc[t][nt][3])};
+        else
+          v = hc[t][nt];
+        lds_write64(sH + ((hst + (uint32_t)(16 * nt * ROWB)) ^ (uint32_t)((TI * w + t) << 5)), v);
+      }
+    if (next < a.num_tiles) load_tile<P, MODE>(a, next, w, q, g, nx);
+    __syncthreads();  // sZ holds the tile
+
+    if constexpr (DATA) {
+      // dz_l^T (or dx^T) of the wave's units: C[16 it + 4 g + e][16 nt + q]
+      f32x4 acc[TI][2];
+#pragma unroll
+      for (int t = 0; t < TI; ++t)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) acc[t][nt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks < ksn) {
+          const i16x8 b0 = lds_read128(sZ + (bz ^ (uint32_t)(ks << 6)));
+          const i16x8 b1 = lds_read128(sZ + (bz ^ (uint32_t)(ks << 6)) + 16 * ROWB);
+#pragma unroll
+          for (int t = 0; t < TI; ++t) {
+            if (!on[t]) continue;
+            const int i = 16 * (TI * w + t) + q;
+            const i16x8 av = lds_read128(sW + (uint32_t)(i * ROWB) + ((uint32_t)((g ^ q) << 4) ^ (uint32_t)(ks << 6)));
+            acc[t][0] = mfma16x16x32(av, b0, acc[t][0], _Float16{});
+            acc[t][1] = mfma16x16x32(av, b1, acc[t][1], _Float16{});
+          }
+        }
+      }
+      // derivative, fp16, store: rows 16 nt + q, units 16 it + 4 g .. + 3
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        u32x2 pk[TI];
+#pragma unroll
+        for (int t = 0; t < TI; ++t) {
+          f32x4 v = acc[t][nt];
+          if constexpr (MODE == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = apply_grad<ACT>(v[e], hc[t][nt][e]);
+          }
+          pk[t] = (u32x2){pack_f16(v[0], v[1]), pack_f16(v[2], v[3])};
+        }
+        const __amdgpu_buffer_rsrc_t ro = rows_rsrc(a.out, a.M, (int64_t)tile * R + 16 * nt, 16, a.ldo, 2);
+        const uint32_t rowoff = (uint32_t)q * (uint32_t)(a.ldo * 2);
+        if constexpr (TI == 2) {
+          // i tiles 2 w and 2 w + 1 are neighbours: one 16-byte store per lane
+          const int u = 32 * w + 16 * (g & 1) + 8 * (g >> 1);
+          store_pair(ro, lmask(u < I, rowoff + 2u * (uint32_t)u), pk[0], pk[1]);
+        } else {
+          const int u = 16 * w + 4 * g;
+          __builtin_amdgcn_raw_buffer_store_b64(pk[0], ro, lmask(u < I, rowoff + 2u * (uint32_t)u), 0, 0);
+        }
+      }
+    }
+
+    // dW^T += dz_{l+1}^T h_l over the tile's 32 rows: C[16 jt + 4 g + e][16 it + q]
+    i16x8 hb[TI];
+#pragma unroll
+    for (int t = 0; t < TI; ++t) {
+      const uint32_t ad = sH + (trk ^ (uint32_t)((TI * w + t) << 5));
+      const i16x4 lo = lds_tr(ad), hi = lds_tr(ad + 16 * ROWB);
+      hb[t] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) {
+      if (jt < njn) {
+        const uint32_t ad = sZ + (trk ^ (uint32_t)(jt << 5));
+        const i16x4 lo = lds_tr(ad), hi = lds_tr(ad + 16 * ROWB);
+        const i16x8 za = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int t = 0; t < TI; ++t)
+          if (on[t]) dw[t][jt] = mfma16x16x32(za, hb[t], dw[t][jt], _Float16{});
+      }
+    }
+  }
+
+  // this workgroup's partial dW_l: row i = 16 it + q, columns 16 jt + 4 g .. + 3
+  float* part = a.partial + (size_t)blockIdx.x * (size_t)I * (size_t)J;
+#pragma unroll
+  for (int t = 0; t < TI; ++t) {
+    const int i = 16 * (TI * w + t) + q;
+    if (i >= I) continue;
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) {
+      const int j = 16 * jt + 4 * g;
+      if (j < J) *(f32x4*)(part + (size_t)i * J + j) = dw[t][jt];
+    }
+  }
+}
+
+// dW = sum of nparts partials of E float4 groups each (row-major, as dW).  A
+// workgroup owns 32 groups and splits the partial index over 8 slices (slice
+// s adds partials s, s + 8, ... in order), then adds the slice sums in slice
+// order: a fixed order for a given grid.
+constexpr int LRED_GROUPS = 32, LRED_SLICES = 8;
+
+__global__ __launch_bounds__(LRED_GROUPS* LRED_SLICES) void layer_bwd_reduce(const float* __restrict__ partial,
+                                                                              int nparts, int E, float* __restrict__ dW) {
+  __shared__ f32x4 red[LRED_SLICES][LRED_GROUPS];
+  const int gi = threadIdx.x % LRED_GROUPS, slice = threadIdx.x / LRED_GROUPS;
+  const int e = blockIdx.x * LRED_GROUPS + gi;
+  f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (e < E) {
+    const f32x4* src = (const f32x4*)partial + e;
+#pragma unroll 8
+    for (int b = slice; b < nparts; b += LRED_SLICES) acc += src[(size_t)b * E];
+  }
+  red[slice][gi] = acc;
+  __syncthreads();
+  if (slice != 0 || e >= E) return;
+  f32x4 sum = red[0][gi];
+#pragma unroll
+  for (int k = 1; k < LRED_SLICES; ++k) sum += red[k][gi];
+  float* d = dW + 4 * (size_t)e;  // dW is only 4-byte aligned
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d[i] = sum[i];
+}
+
+template <int P, int ACT, int MODE>
+hipError_t launch_layer(const LayerArgs& a, int nwg, hipStream_t stream) {
+  hipLaunchKernelGGL((mlp_layer_bwd_kernel<P, ACT, MODE>), dim3(nwg), dim3(LGeo<P>::THREADS), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int P>
+hipError_t launch_layer_p(const LayerArgs& a, int mode, int act, int nwg, hipStream_t stream) {
+  if (mode == 0) return launch_layer<P, ACT_NONE, 0>(a, nwg, stream);
+  if (mode == 2) return launch_layer<P, ACT_NONE, 2>(a, nwg, stream);
+  if (act == ACT_SOFTPLUS) return launch_layer<P, ACT_SOFTPLUS, 1>(a, nwg, stream);
+  if (act == ACT_RELU) return launch_layer<P, ACT_RELU, 1>(a, nwg, stream);
+  return launch_layer<P, ACT_NONE, 1>(a, nwg, stream);
+}
+
+constexpr int kRowsPerTile = 32;
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+struct StreamBwdLayout {
+  size_t partial_bytes, dz_bytes;
+  int ldz;
+};
+
+StreamBwdLayout stream_bwd_layout(const int* dims, int L, int64_t M, int num_cus) {
+  StreamBwdLayout s{};
+  size_t maxij = 0;
+  int ldz = 8;
+  for (int l = 0; l < L; ++l) maxij = std::max(maxij, (size_t)dims[l] * (size_t)dims[l + 1]);
+  for (int l = 1; l < L; ++l) ldz = std::max(ldz, dims[l]);
+  s.partial_bytes = align256((size_t)std::max(num_cus, 1) * maxij * sizeof(float));
+  s.dz_bytes = align256((size_t)std::max<int64_t>(M, 0) * (size_t)ldz * 2);
+  s.ldz = ldz;
+  return s;
+}
+
+}  // namespace
+
+size_t mlp_backward_stream_workspace(const int* dims, int L, int64_t M, int num_cus) {
+  const StreamBwdLayout s = stream_bwd_layout(dims, L, M, num_cus);
+  const int nbuf = L >= 3 ? 2 : L - 1;  // dz_l for l = L-1 .. 1, alternating between two buffers
+  return s.partial_bytes + (size_t)nbuf * s.dz_bytes;
+}
+
+hipError_t launch_mlp_backward_stream(const MlpStreamBwdParams& p, int P, int hidden_act, int num_cus,
+                                      void* workspace, hipStream_t stream) {
+  const StreamBwdLayout s = stream_bwd_layout(p.dims, p.L, p.M, num_cus);
+  const int tiles = (int)(((int64_t)p.M + kRowsPerTile - 1) / kRowsPerTile);
+  const int nwg = std::max(1, std::min(tiles, num_cus));
+  char* ws = (char*)workspace;
+  float* partial = (float*)ws;
+  // dz_l lives in buffer (L - 1 - l) % 2: layer l reads dz_{l+1} from one and
+  // writes dz_l to the other
+  void* zbuf[2] = {ws + s.partial_bytes, ws + s.partial_bytes + s.dz_bytes};
+  for (int l = p.L - 1; l >= 0; --l) {
+    LayerArgs a{};
+    a.I = p.dims[l];
+    a.J = p.dims[l + 1];
+    a.M = p.M;
+    a.num_tiles = tiles;
+    a.W = p.W[l];
+    a.partial = partial;
+    if (l == p.L - 1) {
+      a.dz = p.dout;
+      a.ldz = p.ldd;
+    } else {
+      a.dz = zbuf[(p.L - 2 - l) & 1];
+      a.ldz = s.ldz;
+    }
+    int mode;
+    if (l > 0) {
+      mode = 1;
+      a.h = p.acts[l - 1];
+      a.ldh = p.lda;
+      a.out = zbuf[(p.L - 1 - l) & 1];
+      a.ldo = s.ldz;
+    } else {
+      mode = p.dx ? 2 : 0;
+      a.h = p.x;
+      a.ldh = p.ldx;
+      a.out = p.dx;
+      a.ldo = p.ldq;
+    }
+    hipError_t e = P == 256 ? launch_layer_p<256>(a, mode, hidden_act, nwg, stream)
+                            : launch_layer_p<128>(a, mode, hidden_act, nwg, stream);
+    if (e != hipSuccess) return e;
+    const int groups = a.I * a.J / 4;
+    hipLaunchKernelGGL(layer_bwd_reduce, dim3((groups + LRED_GROUPS - 1) / LRED_GROUPS),
+                       dim3(LRED_GROUPS * LRED_SLICES), 0, stream, (const float*)partial, nwg, groups, p.dW[l]);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace coalesce

@@ -71,4 +71,35 @@ __device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t rs, uint32_t o
   __builtin_amdgcn_raw_buffer_store_b128((u32x4){s0[0], s1[0], s0[1], s1[1]}, rs, off, 0, 0);
 }
 
+// LDS stores of 8 and 16 bytes and the transposing 8-byte read at a byte
+// address.
+__device__ __forceinline__ void lds_write64(uint32_t addr, u32x2 v) {
+  *(__attribute__((address_space(3))) u32x2*)(uintptr_t)addr = v;
+}
+__device__ __forceinline__ void lds_write128(uint32_t addr, u32x4 v) {
+  *(__attribute__((address_space(3))) u32x4*)(uintptr_t)addr = v;
+}
+__device__ __forceinline__ i16x4 lds_tr(uint32_t addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(uintptr_t)addr);
+}
+
+// dz = g * act'(z) from the stored output h = act(z), in fp32:
+//   softplus: act'(z) = sigmoid(z) = 1 - e^{-h} (e^{-h} = 1 / (1 + e^z) for
+//     h = ln(1 + e^z)).  The hardware 2^x on -h log2(e) gives e^{-h} to about
+//     one ulp, and 1 - e^{-h} is then exact, so the derivative is off by at
+//     most 2^-23 in absolute terms: below the resolution of the fp16 dz it
+//     feeds wherever dz is a normal fp16 number;
+//   relu: g where h > 0, else 0 (a select, so an infinite g gives 0 there);
+//   none: g.
+template <int ACT>
+__device__ __forceinline__ float apply_grad(float g, float h) {
+  if constexpr (ACT == ACT_SOFTPLUS) {
+    return g * (1.0f - __builtin_amdgcn_exp2f(h * -1.44269504088896341f));
+  } else if constexpr (ACT == ACT_RELU) {
+    return h > 0.0f ? g : 0.0f;
+  } else {
+    return g;
+  }
+}
+
 }  // namespace coalesce

@@ -166,7 +166,7 @@ def mlp_bwd(D=128, L=3, **kw):
     (dict(dW=None), INV), (dict(dW=[P * 1024, None, P * 1032]), INV), (dict(dW=[P * 1024 + 2, P * 1028, P * 1032]), UNS),
     (dict(x=None), INV), (dict(dout=None), INV), (dict(acts=None), INV), (dict(ldd=100), INV), (dict(ldq=64), INV),
     (dict(dout=P * 128 + 8), UNS), (dict(lda=129), UNS), (dict(dx=P + 64), INV),  # dx overlaps x
-    (dict(act=mk.ACT_GELU_ERF), UNS), (dict(dt=mk.F32), UNS), (dict(D=64, L=9), UNS), (dict(D=136), UNS),
+    (dict(act=mk.ACT_GELU_ERF), UNS), (dict(dt=mk.F32), UNS), (dict(D=64, L=17), UNS), (dict(D=264), UNS),
     (dict(D=100), UNS),
     (dict(L=0), INV), (dict(M=-5), INV), (dict(act=11), INV),
 ])
@@ -175,12 +175,20 @@ def test_mlp_backward_rejects_before_launch(kw, status):
     assert len(mk.load_library().coalesce_last_error()) > 0
 
 
+@pytest.mark.parametrize("kw", [dict(D=136), dict(D=256), dict(D=128, L=5), dict(D=64, L=9), dict(D=64, L=16)])
+def test_mlp_backward_accepts_chains_beyond_lds(kw):
+    # run layer by layer: validation passes and the call reaches the device
+    # query (which fails here, without a GPU)
+    D = kw["D"]
+    assert mlp_bwd(ldx=D, lda=D, ldd=D, ldq=D, **kw) == mk.ERR_DEVICE
+
+
 def test_mlp_backward_workspace_size_of_unsupported_chain_is_zero():
     lib = mk.load_library()
-    for dims in ([96, 96], [128] * 6, [64] * 10):
+    for dims, M in (([96, 264], 10), ([64] * 18, 10), ([100, 64], 10), ([64, 64], -1), ([256] * 4, 2 ** 31)):
         d = (ctypes.c_int64 * len(dims))(*dims)
-        assert lib.coalesce_mlp_backward_workspace_size(ctypes.cast(d, ctypes.c_void_p), len(dims) - 1) == 0
-    assert lib.coalesce_mlp_backward_workspace_size(None, 3) == 0
+        assert lib.coalesce_mlp_backward_workspace_size(ctypes.cast(d, ctypes.c_void_p), len(dims) - 1, M) == 0
+    assert lib.coalesce_mlp_backward_workspace_size(None, 3, 10) == 0
 
 
 def wn(L=3, dims=None, back=False, **kw):

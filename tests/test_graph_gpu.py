@@ -33,7 +33,7 @@ def test_graph_replays_match_eager():
     dout = datagen.mlp_grad_output(w, M=M).to("cuda")
     dW = [torch.empty((128, 128), dtype=torch.float32, device="cuda") for _ in range(w.L)]
     dx = torch.empty_like(x)
-    ws = torch.empty(mk.mlp_backward_workspace_size(w.dims), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(mk.mlp_backward_workspace_size(w.dims, w.M), dtype=torch.uint8, device="cuda")
 
     def work():
         mk.gemm_bias_act(A, B, bias, act="gelu", out=Y)
