@@ -322,6 +322,11 @@ __device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& 
   uint32_t wk[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) wk[ks] = opaque(c.wk[ks]) + 2u * (uint32_t)(l * D * D);
+  // The first layer of a narrower chain runs only the k steps that hold
+  // input units (k0 of them; the others would add products of zeros): k step
+  // 0 inside the pipelined step, the rest in a branch after it.
+  constexpr bool SKIPK = PAD && l == 0 && G::KS > 1;
+  const int k0 = SKIPK ? (p.dims[0] + 31) >> 5 : G::KS;
   i16x8 wa[G::KS];
   f32x4 acc[G::MT], prv[G::MT];
 #pragma unroll
@@ -332,7 +337,7 @@ __device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& 
 #pragma unroll
       for (int s = 0; s < G::MT; ++s) acc[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) {
+      for (int ks = 0; ks < (SKIPK ? 1 : G::KS); ++ks) {
 #pragma unroll
         for (int s = 0; s < G::MT; ++s) acc[s] = mfma16x16x32(wa[ks], __builtin_bit_cast(i16x8, hin.v[s][ks]), acc[s], _Float16());
         if (t + 1 < G::NT) wa[ks] = lds_read128(wk[ks] + 2u * (uint32_t)(16 * D * (t + 1)));
@@ -368,6 +373,19 @@ __device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& 
     }
     if (MLP_INTERLEAVE && t > 0 && t < G::NT) interleave<G::KS * G::MT, VPM, true, G::MT, ST, G::KS>();
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SKIPK) {
+      if (t < G::NT && k0 > 1) {
+#pragma unroll
+        for (int ks = 1; ks < G::KS; ++ks) {
+          if (ks < k0) {
+#pragma unroll
+            for (int s = 0; s < G::MT; ++s)
+              acc[s] = mfma16x16x32(wa[ks], __builtin_bit_cast(i16x8, hin.v[s][ks]), acc[s], _Float16());
+            if (t + 1 < G::NT) wa[ks] = lds_read128(wk[ks] + 2u * (uint32_t)(16 * D * (t + 1)));
+          }
+        }
+      }
+    }
 #pragma unroll
     for (int s = 0; s < G::MT; ++s) prv[s] = acc[s];
   }
@@ -404,6 +422,11 @@ __device__ __forceinline__ void last_layer(const MlpParams& p, const Lane<D>& c,
   uint32_t wk[G::KS];
 #pragma unroll
   for (int ks = 0; ks < G::KS; ++ks) wk[ks] = opaque(c.wk[ks]) + 2u * (uint32_t)(l * D * D);
+  // A narrower chain computes only the pairs of 16-unit sub-tiles that hold
+  // output units (nt of them), and a single-layer one only the k steps that
+  // hold input units.
+  const int nt = PAD ? 2 * ((p.dims[l + 1] + 31) >> 5) : G::NT;
+  const int k0 = PAD && l == 0 ? (p.dims[0] + 31) >> 5 : G::KS;
   i16x8 wa[G::KS];
   f32x4 acc[G::MT], prv[G::MT];
   u32x2 ev[G::MT];  // packed output of the even sub-tile of a pair
@@ -411,17 +434,18 @@ __device__ __forceinline__ void last_layer(const MlpParams& p, const Lane<D>& c,
   for (int ks = 0; ks < G::KS; ++ks) wa[ks] = lds_read128(wk[ks]);
 #pragma unroll
   for (int t = 0; t <= G::NT; ++t) {
-    if (t < G::NT) {
+    if (t < G::NT && (!PAD || t < nt)) {
 #pragma unroll
       for (int s = 0; s < G::MT; ++s) acc[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < G::KS; ++ks) {
+        if (PAD && l == 0 && ks >= k0) continue;
 #pragma unroll
         for (int s = 0; s < G::MT; ++s) acc[s] = mfma16x16x32(wa[ks], __builtin_bit_cast(i16x8, hin.v[s][ks]), acc[s], _Float16());
         if (t + 1 < G::NT) wa[ks] = lds_read128(wk[ks] + 2u * (uint32_t)(16 * D * (t + 1)));
       }
     }
-    if (t > 0) {
+    if (t > 0 && (!PAD || t - 1 < nt)) {
       const int u = t - 1;
 #pragma unroll
       for (int s = 0; s < G::MT; ++s) {
@@ -464,14 +488,20 @@ __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& 
     for (int ks = 0; ks < G::KS; ++ks)
       h[ks] = __builtin_amdgcn_raw_buffer_load_b128(
           rx, PAD ? masked(32 * ks + 8 * lane_group() < p.dims[0], xoff + 64u * ks) : xoff + 64u * ks, 0, 0);
+    // the k steps and output sub-tiles the pipelined path computes (it skips
+    // products of zeros), so that both paths give the same bits
+    const int k0 = PAD ? (p.dims[0] + 31) >> 5 : G::KS;
+    const int ntl = PAD ? 2 * ((p.dims[L] + 31) >> 5) : G::NT;
 #pragma unroll 1
     for (int l = 0; l < L; ++l) {
       const bool in_b2 = SP && l > 0;
 #pragma unroll
       for (int t = 0; t < G::NT; ++t) {
+        if (l == L - 1 && t >= ntl) continue;
         f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < G::KS; ++ks) {
+          if (l == 0 && ks >= k0) continue;
           const i16x8 wa = lds_read128(opaque(c.wk[ks]) + 2u * (uint32_t)(l * D * D + 16 * D * t));
           acc = mfma16x16x32(wa, __builtin_bit_cast(i16x8, h[ks]), acc, _Float16());
         }

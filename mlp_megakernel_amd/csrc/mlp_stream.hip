@@ -50,7 +50,7 @@ namespace {
 // 256): MT 16-row sub-tiles per wave tile, KSM 32-deep k steps at most.
 template <int P>
 struct SGeo {
-  static constexpr int MT = P == 256 ? 1 : 2;
+  static constexpr int MT = 2;            // 16-row sub-tiles per wave tile: one weight read feeds two MFMAs
   static constexpr int TR = 16 * MT;      // rows per wave tile
   static constexpr int KSM = P / 32;      // k steps of the widest layer
   static constexpr int WAVES = 8;         // two per SIMD
@@ -322,8 +322,154 @@ __device__ __forceinline__ int chunk(const MlpStreamParams& p, int l, uint32_t s
   return stores;
 }
 
+// Issue order of one pipeline step of chunk_full: NM MFMAs, a transposing
+// LDS read after each of the first NR, VPM VALU instructions (the
+// transcendentals included) after each, and a buffer store after every
+// ST_EVERY-th when NS stores are due.
+template <int NM, int NR, int VPM, int NS, int ST_EVERY>
+__device__ __forceinline__ void interleave_stream() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (NS > 0 && i % ST_EVERY == ST_EVERY - 1 && i / ST_EVERY < NS) __builtin_amdgcn_sched_group_barrier(0x040, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x402, VPM, 0);
+  }
+}
+
+// A chunk that spans the slot: all KSM k steps and 8 output sub-tiles, with
+// the layer's role (first: input x in natural order; last: output to out)
+// fixed at compile time.  Nothing inside depends on a run-time condition, so
+// the steps are software-pipelined as in the resident kernel: step t issues
+// the MFMAs of sub-tile t (their weight fragments read one step ahead)
+// interleaved with the activation and stores of sub-tile t - 1.  Every unit
+// of such a chunk lies inside the layer, so no column is masked.  The same
+// arithmetic as chunk(), per element, so both give the same bits.
+template <int P, int ACT, bool ST, int CC, bool FIRST, bool LAST>
+__device__ __forceinline__ int chunk_full(const MlpStreamParams& p, int l, uint32_t slot, const STile<P>& hin,
+                                          STile<P>& hout, int tile, int lane) {
+  using G = SGeo<P>;
+  constexpr int KS = G::KSM, MT = G::MT, NT = 8;
+  constexpr bool SP = ACT == ACT_SOFTPLUS;
+  constexpr float pre = SP && FIRST && !LAST ? 1.44269504088896341f : 1.0f;
+  constexpr float post = SP && !FIRST && LAST ? 0.693147180559945309f : 1.0f;
+  constexpr bool STORE = LAST || ST;
+  // VALU issue slots per element (a transcendental counts twice): the
+  // activation, the pre-scale, the fp32 copy's scale, half a pack
+  constexpr int VPE2 = LAST ? 4 : (SP ? 15 : 3) + (pre != 1.0f ? 2 : 0) + (ST ? 2 : 0);
+  constexpr int VPM = (MT * 4 * VPE2 / 2 + KS * MT - 1) / (KS * MT);
+  const int g = lane >> 4;
+  __amdgpu_buffer_rsrc_t ro[MT];
+  uint32_t ooff = 0;
+  if constexpr (STORE) {
+#pragma unroll
+    for (int s = 0; s < MT; ++s)
+      ro[s] = LAST ? tile_rsrc<P>(p.out, p.M, tile, s, p.ldo, 2) : tile_rsrc<P>(p.acts[l], p.M, tile, s, p.lda, 4);
+    // the lane's row, and its units of sub-tile 0 (of the pair, for out)
+    ooff = LAST ? (uint32_t)(lane & 15) * (uint32_t)(p.ldo * 2) + 2u * (128u * CC) + 32u * (uint32_t)(g & 1) +
+                      16u * (uint32_t)(g >> 1)
+                : (uint32_t)(lane & 15) * (uint32_t)(p.lda * 4) + 4u * (128u * CC + 4u * (uint32_t)g);
+    ooff = opaque(ooff);
+  }
+  // weight-fragment addresses of sub-tile 0 (halves 0 and 1, see tbase);
+  // sub-tile t is the same XOR 32 t (the column term 16 (t ^ f) in fp16 units)
+  const uint32_t w0 = opaque(tbase(slot, 0, FIRST, lane));
+  const uint32_t w1 = FIRST ? (w0 ^ 128u) : w0;
+  i16x8 wa[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) wa[ks] = read_w(w0, w1, ks, FIRST);
+  f32x4 acc[MT], prv[MT];
+  u32x2 ev[MT];
+#pragma unroll
+  for (int t = 0; t <= NT; ++t) {
+    if (t < NT) {
+      const uint32_t n0 = opaque(w0 ^ (uint32_t)(32 * (t + 1))), n1 = FIRST ? (n0 ^ 128u) : n0;
+#pragma unroll
+      for (int s = 0; s < MT; ++s) acc[s] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int s = 0; s < MT; ++s)
+          acc[s] = mfma16x16x32(wa[ks], __builtin_bit_cast(i16x8, hin.v[s][ks]), acc[s], _Float16());
+        if (t + 1 < NT) wa[ks] = read_w(n0, n1, ks, FIRST);
+      }
+    }
+    if (t > 0) {
+      const int u = t - 1;
+#pragma unroll
+      for (int s = 0; s < MT; ++s) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float a = prv[s][r] * pre;
+          if constexpr (LAST)
+            v[r] = prv[s][r] * post;
+          else if constexpr (SP)
+            v[r] = softplus_b2_exact(a);
+          else if constexpr (ACT == ACT_RELU)
+            v[r] = relu(a);
+          else
+            v[r] = a;
+        }
+        const u32x2 o = (u32x2){pack_f16(v[0], v[1]), pack_f16(v[2], v[3])};
+        if constexpr (LAST) {
+          if ((u & 1) == 0)
+            ev[s] = o;
+          else
+            store_pair(ro[s], ooff + 32u * (uint32_t)(u - 1), ev[s], o);
+        } else {
+          const int kk = (128 * CC + 16 * u) >> 5;  // the next layer's k step holding these units
+          hout.v[s][kk][(u & 1) * 2] = o[0];
+          hout.v[s][kk][(u & 1) * 2 + 1] = o[1];
+          if constexpr (ST) {
+            const float sc = SP ? 0.693147180559945309f : 1.0f;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4, (f32x4){v[0] * sc, v[1] * sc, v[2] * sc, v[3] * sc}), ro[s],
+                ooff + 64u * (uint32_t)u, 0, 0);
+          }
+        }
+      }
+    }
+    if (t > 0 && t < NT) {
+      constexpr int NR = 2 * KS;
+      if constexpr (LAST) {
+        if ((t - 1) & 1)
+          interleave_stream<KS * MT, NR, VPM, MT, KS>();
+        else
+          interleave_stream<KS * MT, NR, VPM, 0, KS>();
+      } else if constexpr (ST) {
+        interleave_stream<KS * MT, NR, VPM, MT, KS>();
+      } else {
+        interleave_stream<KS * MT, NR, VPM, 0, KS>();
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < MT; ++s) prv[s] = acc[s];
+  }
+  return LAST ? MT * NT / 2 : ST ? MT * NT : 0;
+}
+
+// One chunk of layer l: the pipelined form when the chunk spans the slot,
+// else the general one.
+template <int P, int ACT, bool ST, int CC>
+__device__ __forceinline__ int run_chunk(const MlpStreamParams& p, int l, uint32_t slot, const STile<P>& hin,
+                                         STile<P>& hout, int tile, int lane) {
+  using G = SGeo<P>;
+  const bool full = ceil_div(p.dims[l], 32) == G::KSM && p.dims[l + 1] - 128 * CC >= 128;
+  if (full) {
+    const bool first = l == 0, last = l == p.L - 1;
+    if (first)
+      return last ? chunk_full<P, ACT, ST, CC, true, true>(p, l, slot, hin, hout, tile, lane)
+                  : chunk_full<P, ACT, ST, CC, true, false>(p, l, slot, hin, hout, tile, lane);
+    return last ? chunk_full<P, ACT, ST, CC, false, true>(p, l, slot, hin, hout, tile, lane)
+                : chunk_full<P, ACT, ST, CC, false, false>(p, l, slot, hin, hout, tile, lane);
+  }
+  return chunk<P, ACT, ST, CC>(p, l, slot, hin, hout, tile, lane);
+}
+
 template <int P, int ACT, bool ST>
-__global__ __launch_bounds__(SGeo<P>::THREADS, P == 256 ? 1 : 2) void mlp_stream_kernel(MlpStreamParams p) {
+__global__ __launch_bounds__(SGeo<P>::THREADS, 2) void mlp_stream_kernel(MlpStreamParams p) {
   using G = SGeo<P>;
   __shared__ __attribute__((aligned(1024))) _Float16 sW[2 * G::SLOT];
   const int lane = threadIdx.x & 63;
@@ -341,7 +487,12 @@ __global__ __launch_bounds__(SGeo<P>::THREADS, P == 256 ? 1 : 2) void mlp_stream
   ChunkPos cur{0, 0};
   int js = 0;  // slot of cur
   copy_chunk<P>(p, cur, slot0, wu, lane);
-  STile<P> ha, hb, xn;
+  // Two activation buffers: every layer reads ha and writes hb, which is
+  // then copied into ha (a few register moves per layer, where alternating
+  // the roles at run time would make the compiler address the buffers
+  // indirectly).  The last layer writes to memory, so hb is free while it
+  // runs: the next batch's x is loaded into it there.
+  STile<P> ha, hb;
   load_x<P>(p, batch * G::WAVES + wu, lane, ha);
   int after = G::MT * G::KSM;
   while (batch < nbatch) {
@@ -358,16 +509,12 @@ __global__ __launch_bounds__(SGeo<P>::THREADS, P == 256 ? 1 : 2) void mlp_stream
       const ChunkPos nxt = next_chunk(p, cur);
       if (!(nxt.l == 0 && nxt.cc == 0 && nextb >= nbatch)) copy_chunk<P>(p, nxt, js ? slot0 : slot1, wu, lane);
       after = 0;
-      if (l == 0 && CC == 0) {
+      if (l == p.L - 1 && CC == 0) {
         // the next batch's x (a zero-row tile past the last batch reads nothing)
-        load_x<P>(p, nextb * G::WAVES + wu, lane, xn);
+        load_x<P>(p, nextb * G::WAVES + wu, lane, hb);
         after = G::MT * G::KSM;
       }
-      const uint32_t slot = js ? slot1 : slot0;
-      if ((l & 1) == 0)
-        after += chunk<P, ACT, ST, CC>(p, l, slot, ha, hb, tile, lane);
-      else
-        after += chunk<P, ACT, ST, CC>(p, l, slot, hb, ha, tile, lane);
+      after += run_chunk<P, ACT, ST, CC>(p, l, js ? slot1 : slot0, ha, hb, tile, lane);
       cur = nxt;
       js ^= 1;
     };
@@ -375,8 +522,8 @@ __global__ __launch_bounds__(SGeo<P>::THREADS, P == 256 ? 1 : 2) void mlp_stream
       step(std::integral_constant<int, 0>{}, l);
       if constexpr (P == 256)
         if (p.dims[l + 1] > 128) step(std::integral_constant<int, 1>{}, l);
+      ha = hb;
     }
-    ha = xn;
     batch = nextb;
   }
 }
