@@ -26,8 +26,10 @@ TFLOP/s.  The same line carries
     layers in one launch) and its backward, against per-layer eager torch
     ops, and the weight-normalised training step (normalise, training
     forward, backward, normalisation backward);
-  * variants: two non-square chains (forward with its HBM roofline, and one
-    training step), the FFN GEMM with the ReLU / softplus / no epilogue, the
+  * variants: four general chains -- two non-square ones and two whose
+    weights exceed the LDS (6 x 128, 3 x 256) -- each with the forward, the
+    training forward and the backward against their HBM, MFMA and
+    transcendental bounds, and one training step; the FFN GEMM with the ReLU / softplus / no epilogue, the
     bf16 GEMM + bias + GELU at five smaller sizes (1024^3 to 4096^3), the
     3 x 128 MLP with ReLU / no hidden activation, and the 3 x 128 MLP on small
     batches, launched eagerly and replayed from a HIP graph;
@@ -286,6 +288,82 @@ def main():
                          "peak": round(PEAK_TRANS_PER_S / 1e12, 3), "unit": "T transcendentals/s",
                          "frac": round(trans / (mean_ms * 1e-3) / PEAK_TRANS_PER_S, 4)}}
 
+    def bounds(ms, by, flop, trans):
+        """Lower-bound times of one launch (HBM bytes, MFMA flops at the fp16
+        dense peak, transcendentals at PEAK_TRANS_PER_S) against the measured
+        mean: each as achieved / peak, and the largest as the roofline."""
+        kinds = {"hbm": (by / (PEAK_HBM_GBS * 1e9), by / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"),
+                 "mfma": (flop / (PEAK_TFLOPS["f16"] * 1e12), flop / (ms * 1e-3) / 1e12, PEAK_TFLOPS["f16"], "TFLOP/s"),
+                 "alu": (trans / PEAK_TRANS_PER_S, trans / (ms * 1e-3) / 1e12, round(PEAK_TRANS_PER_S / 1e12, 3),
+                         "T transcendentals/s")}
+        out = {k: {"achieved": round(v[1], 2), "peak": v[2], "unit": v[3], "frac": round(v[1] / v[2], 4)}
+               for k, v in kinds.items()}
+        top = max(kinds, key=lambda k: kinds[k][0])
+        out["bound"] = top
+        out["frac"] = out[top]["frac"]
+        out["mean_launch_ms"] = round(ms, 5)
+        out["algorithmic_bytes_per_launch"] = by
+        out["algorithmic_flop_per_launch"] = flop
+        return out
+
+    def chain_case(w):
+        """Forward, training forward, backward and one training step of a
+        general chain, each with its bounds (bytes: x, out, the fp32
+        activations and dx at their true widths; flops at the true widths)."""
+        x, Ws = datagen.mlp_inputs(w)
+        x, Ws = x.to(dev), [t.to(dev) for t in Ws]
+        g_out = datagen.mlp_grad_output(w).to(dev)
+        out = torch.empty((w.M, w.dims[-1]), dtype=torch.float16, device=dev)
+        H = max(w.dims[1:-1])  # the activations share one pitch
+        acts = [torch.empty((w.M, H), dtype=torch.float32, device=dev)[:, :d] for d in w.dims[1:-1]]
+        dW = [torch.empty(t.shape, dtype=torch.float32, device=dev) for t in Ws]
+        dx = torch.empty_like(x)
+        wsp = torch.empty(mk.mlp_backward_workspace_size(w.dims, w.M), dtype=torch.uint8, device=dev)
+        mx = max(w.dims)
+        P = 64 if mx <= 64 else 128 if mx <= 128 else 256
+        resident = (P == 64 and w.L <= 8) or (P == 128 and w.L <= 4)
+        hidden = sum(w.dims[1:-1])
+        trans = 2.0 * w.M * hidden  # exp2 and log2 per hidden unit and row
+
+        def fwd():
+            mk.mlp_forward(x, Ws, out=out)
+
+        def fwd_train():
+            mk.mlp_forward_train(x, Ws, out=out, acts=acts)
+
+        def bwd():
+            mk.mlp_backward(x, Ws, acts, g_out, dW=dW, dx=dx, workspace=wsp)
+
+        def step():
+            fwd_train()
+            bwd()
+
+        res = {"dims": list(w.dims), "rows": w.M, "kernel_width": P,
+               "forward_kernel": "mlp_kernel" if resident else "mlp_stream_kernel",
+               "backward_kernels": ("mlp_bwd_kernel + mlp_bwd_reduce" if resident else
+                                    "per layer: mlp_layer_bwd_kernel + layer_bwd_reduce")}
+        if resident:
+            res["padded_flop_factor"] = round(2.0 * w.M * w.L * P * P / w.flops(), 3)
+        f_ms, f_ev = timed_steps(fwd, max(20, args.steps), 10)
+        res["forward_ms"] = round(f_ms, 5)
+        res["forward_rows_per_s"] = round(w.M / (f_ms * 1e-3), 1)
+        res["forward_roofline"] = bounds(f_ev, w.bytes(), w.flops(), trans)
+        t_ms, t_ev = timed_steps(fwd_train, max(20, args.steps), 10)
+        res["forward_train_ms"] = round(t_ms, 5)
+        res["forward_train_roofline"] = bounds(t_ev, w.bytes() + 4.0 * w.M * hidden, w.flops(), trans)
+        b_ms, b_ev = timed_steps(bwd, max(20, args.steps), 10)
+        bb = w.M * (2.0 * w.dims[0] + 2.0 * w.dims[-1] + 4.0 * hidden + 2.0 * w.dims[0])
+        res["backward_ms"] = round(b_ms, 5)
+        res["backward_roofline"] = bounds(b_ev, bb, 2.0 * w.flops(), 0.0)
+        if not resident:
+            # the fp16 dz_l each layer writes and the next one reads back
+            res["backward_roofline"]["dz_roundtrip_bytes"] = 4.0 * w.M * hidden
+        res["backward_workspace_bytes"] = wsp.numel()
+        s_ms, _ = timed_steps(step, max(20, args.steps), 10)
+        res["train_step_ms"] = round(s_ms, 5)
+        res["train_step_rows_per_s"] = round(w.M / (s_ms * 1e-3), 1)
+        return res
+
     if args.fusion_traffic:
         fusion_traffic(gemm_case, mlp_case, train_case, flush)
         return
@@ -434,42 +512,12 @@ def main():
     # ------------------------------- non-square chains, other epilogues
     if not args.no_variants:
         var = {}
-        for w in (datagen.MLP_NS1, datagen.MLP_NS2):
-            print("bench: non-square chain %s" % w.name, file=sys.stderr, flush=True)
-            x, Ws = datagen.mlp_inputs(w)
-            x, Ws = x.to(dev), [t.to(dev) for t in Ws]
-            g_out = datagen.mlp_grad_output(w).to(dev)
-            out = torch.empty((w.M, w.dims[-1]), dtype=torch.float16, device=dev)
-            H = max(w.dims[1:-1])  # the activations share one pitch
-            acts = [torch.empty((w.M, H), dtype=torch.float32, device=dev)[:, :d] for d in w.dims[1:-1]]
-            dW = [torch.empty(t.shape, dtype=torch.float32, device=dev) for t in Ws]
-            dx = torch.empty_like(x)
-            wsp = torch.empty(mk.mlp_backward_workspace_size(w.dims, w.M), dtype=torch.uint8, device=dev)
-
-            def fwd():
-                mk.mlp_forward(x, Ws, out=out)
-
-            def step():
-                mk.mlp_forward_train(x, Ws, out=out, acts=acts)
-                mk.mlp_backward(x, Ws, acts, g_out, dW=dW, dx=dx, workspace=wsp)
-
-            f_ms, f_ev = timed_steps(fwd, max(20, args.steps), 10)
-            s_ms, _ = timed_steps(step, max(20, args.steps), 10)
-            P = 64 if max(w.dims) <= 64 else 128
-            # algorithmic bytes: x read, out written (true widths); the kernel
-            # computes at the padded width P
-            ach = w.bytes() / (f_ev * 1e-3) / 1e9
-            padded = 2.0 * w.M * w.L * P * P
-            var[w.name] = {"dims": list(w.dims), "rows": w.M, "kernel_width": P,
-                           "mfma_tflops": round(w.flops() / (f_ev * 1e-3) / 1e12, 1),
-                           "padded_flop_factor": round(padded / w.flops(), 3),
-                           "forward_ms": round(f_ms, 5), "forward_rows_per_s": round(w.M / (f_ms * 1e-3), 1),
-                           "forward_roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                                                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                                                "algorithmic_bytes_per_launch": w.bytes(),
-                                                "mean_launch_ms": round(f_ev, 5)},
-                           "train_step_ms": round(s_ms, 5), "train_step_rows_per_s": round(w.M / (s_ms * 1e-3), 1)}
-            del x, Ws, g_out, out, acts, dW, dx, wsp
+        # the general chains: non-square (narrow input / output) ones that the
+        # resident megakernel runs padded, and chains whose weights exceed the
+        # LDS (layer-streaming forward, layer-by-layer backward)
+        for w in (datagen.MLP_NS1, datagen.MLP_NS2, datagen.MLP6, datagen.MLP3W):
+            print("bench: general chain %s" % w.name, file=sys.stderr, flush=True)
+            var[w.name] = chain_case(w)
             torch.cuda.empty_cache()
         # the FFN GEMM with the other epilogues (GELU is the primary line)
         g = datagen.BF16_FFN

@@ -170,6 +170,12 @@ MLP_NS1 = _reg(MlpWorkload("fp16_mlp_32_128_128_16", 6, 1 << 20, (32, 128, 128, 
                            description="fp16 3-layer softplus MLP 32 -> 128 -> 128 -> 16, 2^20 rows"))
 MLP_NS2 = _reg(MlpWorkload("fp16_mlp_64_128_96_128_32", 7, 1 << 20, (64, 128, 96, 128, 32), "f16",
                            description="fp16 4-layer softplus MLP 64 -> 128 -> 96 -> 128 -> 32, 2^20 rows"))
+# Chains whose weights exceed the LDS (the N-layer generalisation: deeper and
+# wider than the resident megakernel holds), same value recipe.
+MLP6 = _reg(MlpWorkload("fp16_mlp6_d128", 8, 1 << 20, (128,) * 7, "f16",
+                        description="fp16 6-layer softplus MLP, D=H=out=128 (192 KB of weights), 2^20 rows"))
+MLP3W = _reg(MlpWorkload("fp16_mlp3_d256", 9, 1 << 20, (256,) * 4, "f16",
+                         description="fp16 3-layer softplus MLP, D=H=out=256 (384 KB of weights), 2^20 rows"))
 
 
 def gemm_inputs(w: GemmWorkload, M: Optional[int] = None, N: Optional[int] = None, K: Optional[int] = None):
