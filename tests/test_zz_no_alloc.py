@@ -6,7 +6,9 @@ library's own device scratch, so its weight gradients and dx must equal the
 workspace entry point's bit for bit.  Two calls in a row share the scratch;
 the second, on fewer rows (fewer workgroups, fewer partial sums), must not
 see anything the first left behind.  Both calls are also held to the oracle
-at the 2e-2 gate.
+at the 2e-2 gate.  Chains run layer by layer keep their hidden gradients in
+the scratch too, so they fit only up to a row count; beyond it the call is
+rejected before anything is launched.
 """
 import numpy as np
 import pytest
@@ -74,3 +76,50 @@ def test_noalloc_backward_without_dx_and_nonsquare():
         assert dx is None
         for l in range(len(Ws)):
             assert _same(dW[l], dW_ref[l]), "dW[%d] M=%d" % (l, M)
+
+
+@pytest.mark.parametrize("dims,rows", [((128,) * 7, (20000, 777)), ((256, 128, 40, 136), (9000, 33))],
+                         ids=["6x128", "256_128_40_136"])
+def test_noalloc_backward_layer_by_layer_chains(dims, rows):
+    # chains whose weights exceed the LDS: the scratch holds one layer's
+    # partial sums and the fp16 hidden gradients of all M rows; two calls in
+    # a row, the second on fewer rows
+    w = datagen.MLP3
+    L = len(dims) - 1
+    for M in rows:
+        progress("noalloc layer-by-layer backward %s M=%d" % (dims, M))
+        x, Ws = datagen.mlp_inputs(w, M=M, dims=dims)
+        g = datagen.mlp_grad_output(w, M=M, dims=dims)
+        xg, gg = to_gpu(x), to_gpu(g)
+        wg = [t.to("cuda") for t in Ws]
+        _, acts = mk.mlp_forward_train(xg, wg)
+        dW_ref, dx_ref = mk.mlp_backward(xg, wg, acts, gg)
+        dW = [torch.full_like(t, float("nan")) for t in dW_ref]
+        dx = torch.full_like(dx_ref, float("nan"))
+        mk.mlp_backward_noalloc(xg, wg, acts, gg, dW=dW, dx=dx)
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert _same(dW[l], dW_ref[l]), "dW[%d] %s M=%d" % (l, dims, M)
+        assert _same(dx, dx_ref), "dx %s M=%d" % (dims, M)
+        if M <= 5000:
+            o_dW, o_dx = oracle.mlp_backward(f64(x), [f64(t) for t in Ws], f64(g))
+            for l in range(L):
+                assert_close(f64(dW[l]), o_dW[l], 2e-2, "dW[%d]" % l)
+            assert_close(f64(dx), o_dx, 2e-2, "dx")
+
+
+def test_noalloc_backward_rejects_a_workspace_beyond_its_scratch():
+    # 6 x 128 on 2^20 rows needs 2 x 256 MiB of hidden gradients: rejected
+    # before anything is launched, the outputs untouched
+    dims = (128,) * 7
+    M = 1 << 20
+    assert mk.mlp_backward_workspace_size(dims, M) > (64 << 20)
+    x = torch.zeros((M, 128), dtype=torch.float16, device="cuda")
+    Ws = [torch.zeros((128, 128), dtype=torch.float16, device="cuda") for _ in range(6)]
+    acts = [torch.zeros((M, 128), dtype=torch.float32, device="cuda") for _ in range(5)]
+    dW = [torch.full((128, 128), 7.0, device="cuda") for _ in range(6)]
+    with pytest.raises(mk.CoalesceError) as e:
+        mk.mlp_backward_noalloc(x, Ws, acts, x, dW=dW, dx=None)
+    assert e.value.status == mk.ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert all(bool((t == 7.0).all()) for t in dW)
