@@ -591,11 +591,19 @@ def main():
         # configuration) and after it (the recorded winner), both as
         # sustained back-to-back launches; the record is cleared afterwards so
         # that nothing else in this run depends on it.
-        tune_res = {}
+        tune_res = {"search_space": {
+            "gemm_bf16_fp16": "compiled tiles 256x256 (8 waves), 128x128, 64x64 x persistent grid (occupancy, 1/2 "
+                              "and 3/4 of the tile's workgroup slots, one per tile) x tile-group height 4/8/16",
+            "gemm_fp32": "compiled tiles 128x128, 64x64, 32x32, 64x32 x tile-group height 4/8/16",
+            "mlp_resident": "both compiled launch configurations (width 128: 12 waves / 3 per SIMD or 8 / 2; "
+                            "width 64: 16 / 4 or 12 / 3) x grid (default, CUs/4, /2, x1, x2, x3)",
+            "mlp_streamed": "grid (default, CUs/4, /2, x1, x2, x3)",
+            "validation": "bitwise equality with the default configuration's output"}}
         cases = [("gemm", datagen.BF16_FFN, None), ("gemm", datagen.FP32_1024, None),
                  ("gemm", datagen.FP32_2048, None)]
         cases += [("mlp", datagen.MLP3, m) for m in (1 << 12, 1 << 14, 1 << 16, 1 << 20)]
         cases += [("mlp", datagen.MLP5, m) for m in (1 << 14, 1 << 22)]
+        cases += [("mlp", datagen.MLP_NS1, 1 << 20), ("mlp", datagen.MLP6, 1 << 20)]
         for kind, w, m in cases:
             label = w.name if m is None else "%s_M%d" % (w.name, m)
             print("bench: autotune %s" % label, file=sys.stderr, flush=True)

@@ -85,9 +85,10 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
  * with no biases and a linear last layer, in ONE launch whose intermediate
  * activations stay on chip (fp16 MFMA operands, fp32 accumulation, the
  * activation in fp32, h_l rounded to fp16 only as the next layer's operand).
- * The grid is min(#CUs x occupancy, #tiles) persistent workgroups: workgroup
- * b of G owns the row tiles b, b + G, b + 2G, ..., which its waves take one
- * at a time as they become free.
+ * The grid is G persistent workgroups: enough to give each of their waves a
+ * row tile, and at least min(#tiles, #CUs) so that a small batch spreads over
+ * the CUs, at most #CUs x occupancy; workgroup b owns the row tiles b, b + G,
+ * b + 2G, ..., which its waves take one at a time as they become free.
  *
  *   x     device, M x dims[0] fp16, leading dimension ldx >= dims[0]
  *   W     HOST array of L device pointers; W[l] is dims[l] x dims[l+1] fp16,
@@ -110,7 +111,7 @@ coalesce_status coalesce_mlp_forward(const void* x, int64_t ldx, const void* con
 /*
  * As coalesce_mlp_forward, with the persistent grid size chosen by the
  * caller: num_workgroups > 0 launches exactly that many workgroups (each
- * owns every num_workgroups-th row tile), 0 picks min(#CUs x occupancy, #tiles).  The
+ * owns every num_workgroups-th row tile), 0 picks the default grid above.  The
  * result does not depend on the grid size, bit for bit.
  */
 coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
@@ -291,9 +292,12 @@ coalesce_status coalesce_flush_caches(const void* buf, size_t bytes, void* sink,
  * and post-tune correctness validation).  An autotune call takes the same
  * arguments as the entry point it tunes and computes the same output; it
  * runs every candidate launch configuration `iters` times on the caller's
- * data (the tile shape, persistent grid size and tile-group order of the
- * bf16/fp16 GEMM, the tile shape and group order of the FP32 GEMM, the grid
- * size of the MLP megakernel), keeps the fastest whose output equals the default
+ * data (the tile shape -- three compiled tile configurations --, persistent
+ * grid size and tile-group order of the bf16/fp16 GEMM; the tile shape -- four
+ * compiled ones -- and group order of the FP32 GEMM; for the MLP megakernel
+ * its two compiled launch configurations (waves per workgroup and the register
+ * budget that goes with them) and the grid size), keeps the fastest whose
+ * output equals the default
  * configuration's bit for bit (every candidate performs the same arithmetic
  * per output element, so equality is the exact test; the default is kept
  * unless a candidate is more than 1 % faster), and records it: later
@@ -319,7 +323,9 @@ typedef struct {
   int32_t group_m;     /* the chosen tile-group height (0: default) */
   int32_t variant;     /* GEMM tile shape, 0 = the launcher's heuristic.  FP32: 1 = 128 x 128,
                           2 = 64 x 64, 3 = 32 x 32, 4 = 64 x 32; bf16 / fp16: 1 = 256 x 256,
-                          2 = 128 x 128, 3 = 64 x 64 */
+                          2 = 128 x 128, 3 = 64 x 64.  MLP (chains whose
+                          weights fit in LDS): 0 = the default launch configuration (12 waves per
+                          workgroup at width 128, 16 at 64), 1 = the other (8 / 12 waves) */
 } coalesce_tune_report;
 
 coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb,

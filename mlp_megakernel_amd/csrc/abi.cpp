@@ -273,10 +273,13 @@ coalesce_status check_rows(const void* t, int64_t ld, int64_t D, int64_t es, con
   return COALESCE_OK;
 }
 
+// variant: the resident kernel's launch configuration (0 default, 1 the
+// alternative; inference forward only).  num_workgroups == 0 and variant ==
+// 0 let a tuned record of this shape, if any, choose both.
 coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* W, const int64_t* dims, int32_t L,
                                  void* out, int64_t ldo, float* const* acts, int64_t lda, int64_t M,
-                                 coalesce_dtype dtype, coalesce_act hidden_act, int64_t num_workgroups, bool train,
-                                 bool use_cache, void* stream) {
+                                 coalesce_dtype dtype, coalesce_act hidden_act, int64_t num_workgroups, int variant,
+                                 bool train, bool use_cache, void* stream) {
   int64_t P = 0;
   bool square = true, resident = true;
   coalesce_status s = check_mlp_chain(W, dims, L, M, dtype, hidden_act, &P, &square, &resident);
@@ -353,12 +356,18 @@ coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* 
   p.ldo = ldo;
   p.lda = train ? lda : 0;
   p.M = (int)M;
-  if (num_workgroups == 0 && !train && use_cache && g_tuned_any.load(std::memory_order_relaxed)) {
+  if (num_workgroups == 0 && variant == 0 && !train && use_cache && g_tuned_any.load(std::memory_order_relaxed)) {
     TuneCfg tc;
-    if (tuned_lookup(mlp_key(current_device(), dims, L, M, hidden_act), &tc)) num_workgroups = tc.grid;
+    if (tuned_lookup(mlp_key(current_device(), dims, L, M, hidden_act), &tc)) {
+      num_workgroups = tc.grid;
+      variant = tc.variant;
+    }
   }
-  hipError_t e = launch_mlp(p, (int)P, (int)L, act_code(hidden_act), train && L > 1, !square, (int)num_workgroups,
-                            cus, (hipStream_t)stream);
+  hipError_t e = variant == 1 && !train
+                     ? launch_mlp_alt(p, (int)P, (int)L, act_code(hidden_act), !square, (int)num_workgroups, cus,
+                                      (hipStream_t)stream)
+                     : launch_mlp(p, (int)P, (int)L, act_code(hidden_act), train && L > 1, !square,
+                                  (int)num_workgroups, cus, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "MLP launch");
   return ok();
 }
@@ -370,14 +379,14 @@ extern "C" {
 coalesce_status coalesce_mlp_forward_grid(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
                                           int32_t L, void* out, int64_t ldo, int64_t M, coalesce_dtype dtype,
                                           coalesce_act hidden_act, int64_t num_workgroups, void* stream) {
-  return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, num_workgroups, false, true,
+  return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, num_workgroups, 0, false, true,
                           stream);
 }
 
 coalesce_status coalesce_mlp_forward_train(const void* x, int64_t ldx, const void* const* W, const int64_t* dims,
                                            int32_t L, void* out, int64_t ldo, float* const* acts, int64_t lda,
                                            int64_t M, coalesce_dtype dtype, coalesce_act hidden_act, void* stream) {
-  return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, acts, lda, M, dtype, hidden_act, 0, true, false, stream);
+  return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, acts, lda, M, dtype, hidden_act, 0, 0, true, false, stream);
 }
 
 // Workspace of the backward: the fused kernel's per-workgroup partial sums
@@ -897,20 +906,25 @@ coalesce_status coalesce_autotune_mlp_forward(const void* x, int64_t ldx, const 
   for (int l = 0; l < L; ++l) operands.push_back(span(W[l], dims[l], dims[l + 1], dims[l + 1], 2));
   if (M > 0 && (s = check_tune_args(iters, workspace, workspace_bytes, M, dims[L] * 2, operands)) != COALESCE_OK)
     return s;
-  s = mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, 0, false, false, stream);
+  s = mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, 0, 0, false, false, stream);
   if (s != COALESCE_OK) return s;
   if (M == 0) return ok();
   int cus = 0;
   if ((s = current_cus(&cus)) != COALESCE_OK) return s;
+  // both compiled launch configurations of the resident kernel (variant 0:
+  // the default wave count, 1: fewer waves with more registers each), each
+  // with its occupancy-derived grid and fixed grids around one workgroup per
+  // CU; the layer-streaming kernel has one configuration (grids only)
   std::vector<TuneCfg> cands;
   cands.push_back(TuneCfg{});
-  for (int g : {cus / 4, cus / 2, cus, 2 * cus, 3 * cus}) add_unique(cands, TuneCfg{g, 0, 0});
+  for (int v : resident ? std::vector<int>{0, 1} : std::vector<int>{0})
+    for (int g : {0, cus / 4, cus / 2, cus, 2 * cus, 3 * cus}) add_unique(cands, TuneCfg{g, 0, v});
   const std::string key = mlp_key(current_device(), dims, L, M, hidden_act);
   return tune(
       cands,
       [&](const TuneCfg& c) {
-        return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, c.grid, false, false,
-                                stream);
+        return mlp_forward_impl(x, ldx, W, dims, L, out, ldo, nullptr, 0, M, dtype, hidden_act, c.grid, c.variant,
+                                false, false, stream);
       },
       iters, stream, out, ldo * 2, M, dims[L] * 2, workspace, workspace_bytes, operands, key, report);
 }

@@ -57,8 +57,6 @@ constexpr int BK = 64;
 //   * 64 x 64, 4 waves of 32 x 32: four workgroups per CU (32 KB of LDS
 //     each), four waves per SIMD, for problems whose 128 x 128 tiles would
 //     still leave most CUs idle.
-//   * 256 x 256, 4 waves of 128 x 128 (one wave per SIMD, 256 accumulators):
-//     compiled for measurements only.
 // MINW is the launch-bounds floor of waves per SIMD, which caps the registers
 // a wave may use (256 at two waves per SIMD).
 template <int BM_, int BN_, int NW_, int MINW_>
@@ -80,7 +78,6 @@ struct Geo {
 typedef Geo<256, 256, 8, 1> Geo256;
 typedef Geo<128, 128, 4, 2> Geo128;
 typedef Geo<64, 64, 4, 4> Geo64;
-typedef Geo<256, 256, 4, 1> Geo256w4;
 
 // LDS layouts, 16-byte chunks XOR-swizzled so that every fragment read is
 // free of bank conflicts whether the LDS serves 128 or 256 bytes per clock:
@@ -600,9 +597,6 @@ hipError_t launch_bias(const GemmParams& p, hipStream_t stream, int num_cus) {
 // p.variant is resolved by launch_gemm16: 1 = 256 x 256, 2 = 128 x 128, 3 = 64 x 64.
 template <typename T, typename TO, int ACT>
 hipError_t launch_typed(const GemmParams& p, hipStream_t stream, int num_cus) {
-#ifdef GEMM16_WITH_W4
-  if (p.variant == 4) return launch_bias<T, TO, ACT, Geo256w4>(p, stream, num_cus);
-#endif
   if (p.variant == 3) return launch_bias<T, TO, ACT, Geo64>(p, stream, num_cus);
   if (p.variant == 2) return launch_bias<T, TO, ACT, Geo128>(p, stream, num_cus);
   return launch_bias<T, TO, ACT, Geo256>(p, stream, num_cus);

@@ -41,11 +41,15 @@ struct MlpParams {
 // for 128).  pad = false: every width equals D; pad = true: p.dims holds the
 // true widths (multiples of 8, at most D) and the kernel runs the chain with
 // the weights zero-padded to D x D in LDS, x loads and out / activation stores
-// masked to the true columns.  num_workgroups <= 0: min(#CUs x occupancy,
-// workgroups with work).  store_acts: also write the hidden activations to
+// masked to the true columns.  num_workgroups <= 0: a workgroup per #WAVES
+// tiles, at least min(#tiles, #CUs), at most #CUs x occupancy.  store_acts: also write the hidden activations to
 // p.acts (training forward).
 hipError_t launch_mlp(const MlpParams& p, int D, int L, int hidden_act, bool store_acts, bool pad, int num_workgroups,
                       int num_cus, hipStream_t stream);
+// The same kernels in the second launch configuration (inference forward
+// only; an autotuning candidate, identical results).
+hipError_t launch_mlp_alt(const MlpParams& p, int D, int L, int hidden_act, bool pad, int num_workgroups, int num_cus,
+                          hipStream_t stream);
 
 // Chains for the layer-streaming megakernel (mlp_stream.hip): up to 16
 // layers of widths up to 256, weights streamed through LDS chunk by chunk.
