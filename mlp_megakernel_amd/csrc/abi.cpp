@@ -226,7 +226,7 @@ namespace {
 // 8 up to 256.  *P_out: the width class (64, 128 or 256) of its widest
 // layer; *resident: all weights fit in LDS at once (widths up to 128 and at
 // most 4 layers, or up to 64 and at most 8), so the resident megakernel
-// (mlp.hip, and the fused backward) runs it -- else the layer-streaming one.
+// (mlp_kernel.hpp, and the fused backward) runs it -- else the layer-streaming one.
 coalesce_status check_mlp_chain(const void* const* W, const int64_t* dims, int32_t L, int64_t M,
                                 coalesce_dtype dtype, coalesce_act hidden_act, int64_t* P_out, bool* square,
                                 bool* resident) {

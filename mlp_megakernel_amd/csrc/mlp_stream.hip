@@ -5,7 +5,7 @@
 // whose layers it computes at their own widths (README: generalising the
 // megakernel to N layers and to D != H != out).
 //
-// The resident kernel (mlp.hip) keeps every W_l in LDS for the whole launch
+// The resident kernel (mlp_kernel.hpp) keeps every W_l in LDS for the whole launch
 // and lets each wave run its row tiles through the chain on its own.  Here
 // the weights pass through LDS one chunk at a time instead:
 //   * a chunk is the slice of one layer's W_l that produces up to 128 output
