@@ -209,7 +209,7 @@ coalesce_status coalesce_mlp_backward(const void* x, int64_t ldx, const void* co
  * rejected with COALESCE_ERR_UNSUPPORTED before anything is launched: every
  * chain whose weights fit in LDS fits on a device of up to 256 compute
  * units, whatever M; a chain run layer by layer fits while its partial sums
- * and hidden-gradient buffers do (e.g. 6 layers 128 wide up to 98304
+ * and hidden-gradient buffers do (e.g. 6 layers 128 wide up to 65536
  * rows on 256 compute units).  Every call on one device shares that
  * device's scratch, which keeps
  * the last call's contents: calls that can overlap on one device (streams

@@ -340,15 +340,21 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 struct StreamBwdLayout {
   size_t partial_bytes, dz_bytes;
   int ldz;
+  int max_groups;  // workgroups of a layer launch at most
 };
 
 StreamBwdLayout stream_bwd_layout(const int* dims, int L, int64_t M, int num_cus) {
   StreamBwdLayout s{};
   size_t maxij = 0;
-  int ldz = 8;
+  int ldz = 8, mx = 0;
   for (int l = 0; l < L; ++l) maxij = std::max(maxij, (size_t)dims[l] * (size_t)dims[l + 1]);
   for (int l = 1; l < L; ++l) ldz = std::max(ldz, dims[l]);
-  s.partial_bytes = align256((size_t)std::max(num_cus, 1) * maxij * sizeof(float));
+  for (int l = 0; l <= L; ++l) mx = std::max(mx, dims[l]);
+  // Width 128 takes 48 KB of LDS and under 128 VGPRs a lane, so two
+  // workgroups share a CU (twice the row tiles in flight); width 256 fills
+  // the LDS with its weights.
+  s.max_groups = std::max(num_cus, 1) * (mx > 128 ? 1 : 2);
+  s.partial_bytes = align256((size_t)s.max_groups * maxij * sizeof(float));
   s.dz_bytes = align256((size_t)std::max<int64_t>(M, 0) * (size_t)ldz * 2);
   s.ldz = ldz;
   return s;
@@ -366,7 +372,7 @@ hipError_t launch_mlp_backward_stream(const MlpStreamBwdParams& p, int P, int hi
                                       void* workspace, hipStream_t stream) {
   const StreamBwdLayout s = stream_bwd_layout(p.dims, p.L, p.M, num_cus);
   const int tiles = (int)(((int64_t)p.M + kRowsPerTile - 1) / kRowsPerTile);
-  const int nwg = std::max(1, std::min(tiles, num_cus));
+  const int nwg = std::max(1, std::min(tiles, s.max_groups));
   char* ws = (char*)workspace;
   float* partial = (float*)ws;
   // dz_l lives in buffer (L - 1 - l) % 2: layer l reads dz_{l+1} from one and
