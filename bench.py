@@ -348,9 +348,12 @@ def main():
         res["forward_ms"] = round(f_ms, 5)
         res["forward_rows_per_s"] = round(w.M / (f_ms * 1e-3), 1)
         res["forward_roofline"] = bounds(f_ev, w.bytes(), w.flops(), trans)
+        res["forward_roofline"]["traffic"] = None if resident else measured_traffic("stream_forward/" + w.name)
         t_ms, t_ev = timed_steps(fwd_train, max(20, args.steps), 10)
         res["forward_train_ms"] = round(t_ms, 5)
         res["forward_train_roofline"] = bounds(t_ev, w.bytes() + 4.0 * w.M * hidden, w.flops(), trans)
+        res["forward_train_roofline"]["traffic"] = (None if resident else
+                                                    measured_traffic("stream_forward_train/" + w.name))
         b_ms, b_ev = timed_steps(bwd, max(20, args.steps), 10)
         bb = w.M * (2.0 * w.dims[0] + 2.0 * w.dims[-1] + 4.0 * hidden + 2.0 * w.dims[0])
         res["backward_ms"] = round(b_ms, 5)
@@ -358,6 +361,7 @@ def main():
         if not resident:
             # the fp16 dz_l each layer writes and the next one reads back
             res["backward_roofline"]["dz_roundtrip_bytes"] = 4.0 * w.M * hidden
+        res["backward_roofline"]["traffic"] = None if resident else measured_traffic("stream_backward/" + w.name)
         res["backward_workspace_bytes"] = wsp.numel()
         s_ms, _ = timed_steps(step, max(20, args.steps), 10)
         res["train_step_ms"] = round(s_ms, 5)
@@ -694,6 +698,7 @@ def main():
 TRAFFIC_GEMMS = ("fp32_gemm_gelu_512", "fp32_gemm_gelu_1024", "fp32_gemm_gelu_2048", "fp32_gemm_gelu_4096",
                  "bf16_ffn_up_gelu")
 TRAFFIC_MLPS = ("fp16_mlp3_d128", "fp16_mlp5_d64")
+TRAFFIC_CHAINS = ("fp16_mlp6_d128", "fp16_mlp3_d256")  # the layer-streaming forward and per-layer backward
 WARM_LAUNCHES = 3
 
 
@@ -722,6 +727,12 @@ def traffic_plan():
         plan += [("warm", name, "forward_train_first", ["mlp_kernel"])]  # train_case's own first call
         plan += [("warm", name, "forward_train_warm", ["mlp_kernel"]),
                  ("warm", name, "backward_warm", ["mlp_bwd_kernel", "mlp_bwd_reduce"])] * WARM_LAUNCHES
+    for name in TRAFFIC_CHAINS:
+        w = datagen.WORKLOADS[name]
+        plan += [("warm", name, "stream_forward_warm", ["mlp_stream_kernel"])] * WARM_LAUNCHES
+        plan += [("warm", name, "stream_forward_train_warm", ["mlp_stream_kernel"]),
+                 ("warm", name, "stream_backward_warm", ["mlp_layer_bwd_kernel", "layer_bwd_reduce"] * w.L)] \
+            * WARM_LAUNCHES
     return plan
 
 
@@ -769,6 +780,26 @@ def fusion_traffic(gemm_case, mlp_case, train_case, flush):
             bwd()
         torch.cuda.synchronize()
         del fwd, bwd, step
+        torch.cuda.empty_cache()
+    for name in TRAFFIC_CHAINS:
+        w = datagen.WORKLOADS[name]
+        print("bench: streamed-chain traffic %s" % name, file=sys.stderr, flush=True)
+        x, Ws = datagen.mlp_inputs(w)
+        x, Ws = x.to(dev), [t.to(dev) for t in Ws]
+        g = datagen.mlp_grad_output(w).to(dev)
+        out = torch.empty((w.M, w.dims[-1]), dtype=torch.float16, device=dev)
+        acts = [torch.empty((w.M, d), dtype=torch.float32, device=dev) for d in w.dims[1:-1]]
+        dW = [torch.empty(t.shape, dtype=torch.float32, device=dev) for t in Ws]
+        dx = torch.empty_like(x)
+        ws = torch.empty(mk.mlp_backward_workspace_size(w.dims, w.M), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(WARM_LAUNCHES):
+            mk.mlp_forward(x, Ws, out=out)
+        for _ in range(WARM_LAUNCHES):
+            mk.mlp_forward_train(x, Ws, out=out, acts=acts)
+            mk.mlp_backward(x, Ws, acts, g, dW=dW, dx=dx, workspace=ws)
+        torch.cuda.synchronize()
+        del x, Ws, g, out, acts, dW, dx, ws
         torch.cuda.empty_cache()
     print(json.dumps({"fusion_traffic_plan": traffic_plan()}), flush=True)
 
@@ -820,7 +851,9 @@ def summarize_counters(fetch_csv, write_csv):
     C = "mlp_megakernel_amd/csrc/"
     srcs = {"gemm16_kernel": [C + "gemm16.hip", C + "common.hpp"], "gemm32_kernel": [C + "gemm32.hip", C + "common.hpp"],
             "mlp_kernel": [C + "mlp.hip", C + "mlp_kernel.hpp", C + "mlp_common.hpp", C + "common.hpp"],
-            "backward": [C + "mlp_bwd.hip", C + "mlp_common.hpp", C + "common.hpp"]}
+            "backward": [C + "mlp_bwd.hip", C + "mlp_common.hpp", C + "common.hpp"],
+            "mlp_stream_kernel": [C + "mlp_stream.hip", C + "mlp_common.hpp", C + "common.hpp"],
+            "stream_backward": [C + "mlp_bwd_stream.hip", C + "mlp_common.hpp", C + "common.hpp"]}
 
     def sha(files):
         h = hashlib.sha256()
@@ -890,6 +923,18 @@ def summarize_counters(fetch_csv, write_csv):
             out["%s/%s" % (key, wl)] = {"kernels": [kern], "sources": srcs[kern], "fetch_bytes": f_,
                                         "write_bytes": w_, "source_sha256": sha(srcs[kern])}
             print("| %s/%s | %.1f MB | %.1f MB | %.1f MB |" % (key, wl, f_ / 1e6, w_ / 1e6, by / 1e6))
+    for wl in TRAFFIC_CHAINS:
+        w = datagen.WORKLOADS[wl]
+        hidden = sum(w.dims[1:-1])
+        for role, key, kern, by in (("stream_forward_warm", "stream_forward", "mlp_stream_kernel", w.bytes()),
+                                    ("stream_forward_train_warm", "stream_forward_train", "mlp_stream_kernel",
+                                     w.bytes() + 4.0 * w.M * hidden),
+                                    ("stream_backward_warm", "stream_backward", "stream_backward",
+                                     w.M * (4.0 * w.dims[0] + 2.0 * w.dims[-1] + 4.0 * hidden))):
+            f_, w_ = tot(fe, role, wl, f_fac), tot(wr, role, wl, w_fac)
+            out["%s/%s" % (key, wl)] = {"kernels": [kern], "sources": srcs[kern], "fetch_bytes": f_,
+                                        "write_bytes": w_, "source_sha256": sha(srcs[kern])}
+            print("| %s/%s | %.1f MB | %.1f MB | %.1f MB |" % (key, wl, f_ / 1e6, w_ / 1e6, by / 1e6))
     print()
     print("calibration: FETCH_SIZE x %.4f, WRITE_SIZE x %.4f" % (f_fac, w_fac))
     with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
@@ -915,6 +960,11 @@ def summarize_trace(trace_csv, bench_json):
               "mlp_kernel" if res["unit"] == "rows/s" else ("gemm32_kernel" if res["dtype"] == "f32" else "gemm16_kernel"))]
     for wl, ent in (res.get("mlp") or {}).items():
         timed.append((wl, ent["roofline"], max(20, res["steps"]), "mlp_kernel"))
+    # the general chains' forward (the last launches of its instantiation in
+    # a run without the tuning section)
+    for wl, ent in (res.get("variants") or {}).items():
+        if isinstance(ent, dict) and "forward_roofline" in ent:
+            timed.append((wl + " forward", ent["forward_roofline"], max(20, res["steps"]), ent["forward_kernel"]))
     print("| timed kernel | dispatches | mean of all | mean of the last K (K) | HIP-event mean of the run | "
           "roofline frac from the trace | from the events |")
     print("|---|---|---|---|---|---|---|")
@@ -933,7 +983,9 @@ def summarize_trace(trace_csv, bench_json):
         if best is None:
             continue
         name, m, allm, n = best
-        if roof["unit"] == "TFLOP/s":
+        if "unit" not in roof:  # a general chain: the fraction of its largest bound scales with 1 / time
+            frac = roof["frac"] * want / m
+        elif roof["unit"] == "TFLOP/s":
             frac = roof["algorithmic_flop_per_launch"] / (m * 1e-3) / 1e12 / roof["peak"]
         else:
             frac = roof["algorithmic_bytes_per_launch"] / (m * 1e-3) / 1e9 / roof["peak"]
