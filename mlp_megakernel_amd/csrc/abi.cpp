@@ -868,8 +868,12 @@ coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, cons
   std::vector<TuneCfg> cands;
   cands.push_back(dflt);
   if (in_dtype == COALESCE_F32) {
+    // the tile shapes that split K into as many groups as the default's
+    // (the others add the partial sums in another order: other bits)
+    const int kg = gemm32_kgroups(gemm32_variant(M, N, cus));
     for (int variant : {1, 2, 3, 4})
-      for (int gm : {4, 8, 16}) add_unique(cands, TuneCfg{0, gm, variant});
+      if (gemm32_kgroups(variant) == kg)
+        for (int gm : {4, 8, 16}) add_unique(cands, TuneCfg{0, gm, variant});
   } else {
     // every tile shape (1 = 256 x 256, one workgroup per CU; 2 = 128 x 128,
     // two; 3 = 64 x 64, four), each with persistent grids of all, half and

@@ -10,18 +10,29 @@
 //     per 16 rows (4 consecutive k, one per MFMA) and its B^T operand as 32-bit
 //     reads; fp32 MFMA takes one k per lane, so no transpose is needed;
 //   * 2 LDS stages filled by 16-byte direct-to-LDS copies one K step ahead;
-//     2 workgroups per CU (64 KB of LDS each at 128 x 128).
+//     2 workgroups per CU (64 KB of LDS each at 128 x 128);
+//   * the smaller tiles split K inside the workgroup: KG groups of 4 waves
+//     (2 at 64 x 64 and 64 x 32, 4 at 32 x 32) each take a contiguous run of
+//     K steps with LDS stages of their own, and the groups' accumulators are
+//     added through LDS in a fixed order (group 0 + 1 + ...) before the
+//     epilogue.  A small problem has one such tile per CU or fewer, whose
+//     K loop is a chain of dependent steps (copy, barrier, 8 MFMAs on one
+//     accumulator); the groups run their chains side by side.
 // The fp32 MFMA accumulates in fp32 with the hardware's own summation order,
 // which is the same for the fused kernel and for the same kernel run with
 // act = NONE and no bias (the unfused baseline's GEMM step), so the fused and
-// unfused results agree bit for bit.
+// unfused results agree bit for bit.  Tile shapes with the same number of K
+// groups accumulate in the same order (the autotuner only exchanges those).
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace coalesce {
 namespace {
 
-constexpr int BK = 32, THREADS = 256;
+constexpr int BK = 32;
+
+// K groups of a tile shape (4 waves each).
+constexpr int kgroups(int BM, int BN) { return BM == 128 ? 1 : BM == 32 ? 4 : 2; }
 
 __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -47,6 +58,9 @@ __device__ __forceinline__ int swzB(int k) {
 
 template <int BM, int BN>
 struct Cfg {
+  static constexpr int KG = kgroups(BM, BN);
+  static constexpr int THREADS = 256 * KG;
+  static constexpr int STAGE = BM * BK + BK * BN;  // floats of one LDS stage (A then B)
   static constexpr int A_BLOCKS = BM * BK * 4 / 1024;  // 1 KB copies per stage for A
   static constexpr int B_BLOCKS = BK * BN * 4 / 1024;
   static constexpr int B_ROWS_PER_BLOCK = 1024 / (BN * 4);
@@ -150,20 +164,25 @@ __device__ __forceinline__ void compute_stage(const float* sa, const float* sb, 
 }
 
 template <int BM, int BN, int ACT, bool HAS_BIAS>
-__global__ __launch_bounds__(THREADS, 2) void gemm32_kernel(GemmParams p) {
+__global__ __launch_bounds__((Cfg<BM, BN>::THREADS), 2) void gemm32_kernel(GemmParams p) {
   typedef Cfg<BM, BN> C;
-  __shared__ __attribute__((aligned(1024))) float sA0[BM * BK];
-  __shared__ __attribute__((aligned(1024))) float sB0[BK * BN];
-  __shared__ __attribute__((aligned(1024))) float sA1[BM * BK];
-  __shared__ __attribute__((aligned(1024))) float sB1[BK * BN];
+  constexpr int KG = C::KG;
+  // per K group two stages of A (BM x BK) and B (BK x BN)
+  __shared__ __attribute__((aligned(1024))) float lds[KG * 2 * C::STAGE];
 
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const int wm = w & 1, wn = w >> 1;
+  const int kg = __builtin_amdgcn_readfirstlane(w >> 2);  // K group
+  const int wl = w & 3;                                   // wave within the group
+  const int wu = __builtin_amdgcn_readfirstlane(wl);
+  const int wm = wl & 1, wn = wl >> 1;
   const int nlast = ((p.N - 1) >> 2) << 2;
+  float* sA0 = lds + (2 * kg) * C::STAGE;
+  float* sB0 = sA0 + BM * BK;
+  float* sA1 = sA0 + C::STAGE;
+  float* sB1 = sA1 + BM * BK;
 
   f32x4 acc[C::NT][C::MT];
 #pragma unroll
@@ -173,32 +192,59 @@ __global__ __launch_bounds__(THREADS, 2) void gemm32_kernel(GemmParams p) {
 
   const int kfull = p.K / BK;
   const int ktiles = (p.K + BK - 1) / BK;
-  if (ktiles > 0) {
-    if (kfull > 0)
-      fill_dma<BM, BN>(p, m0, n0, 0, nlast, sA0, sB0, wu, lane);
+  // the group's K steps [kbeg, kend); every group passes the same `per`
+  // barriers
+  const int per = (ktiles + KG - 1) / KG;
+  const int kbeg = kg * per;
+  const int kend = min(ktiles, kbeg + per);
+  if (kbeg < kend) {
+    if (kbeg < kfull)
+      fill_dma<BM, BN>(p, m0, n0, kbeg * BK, nlast, sA0, sB0, wu, lane);
     else
-      fill_tail<BM, BN>(p, m0, n0, 0, nlast, sA0, sB0, wu, lane);
+      fill_tail<BM, BN>(p, m0, n0, kbeg * BK, nlast, sA0, sB0, wu, lane);
   }
-  for (int kt = 0; kt < ktiles; kt += 2) {
+  for (int j0 = 0; j0 < per; j0 += 2) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
-      const int k = kt + half;
-      if (k < ktiles) {
+      const int j = j0 + half;
+      if (j < per) {
+        const int k = kbeg + j;
         float* ca = half ? sA1 : sA0;
         float* cb = half ? sB1 : sB0;
         float* na = half ? sA0 : sA1;
         float* nb = half ? sB0 : sB1;
         wait_vmcnt0();
         __syncthreads();
-        if (k + 1 < ktiles) {
+        if (k + 1 < kend) {
           if (k + 1 < kfull)
             fill_dma<BM, BN>(p, m0, n0, (k + 1) * BK, nlast, na, nb, wu, lane);
           else
             fill_tail<BM, BN>(p, m0, n0, (k + 1) * BK, nlast, na, nb, wu, lane);
         }
-        compute_stage<BM, BN>(ca, cb, acc, wm, wn, lane);
+        if (k < kend) compute_stage<BM, BN>(ca, cb, acc, wm, wn, lane);
       }
     }
+  }
+
+  if constexpr (KG > 1) {
+    // groups 1 .. KG-1 hand their sums to group 0 through the (now free)
+    // stages; group 0 adds them in group order
+    f32x4* red = (f32x4*)lds;
+    __syncthreads();
+    if (kg > 0) {
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int s = 0; s < C::MT; ++s)
+          red[((((kg - 1) * 4 + wl) * C::NT + t) * C::MT + s) * 64 + lane] = acc[t][s];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+    for (int g2 = 1; g2 < KG; ++g2)
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+        for (int s = 0; s < C::MT; ++s) acc[t][s] += red[((((g2 - 1) * 4 + wl) * C::NT + t) * C::MT + s) * 64 + lane];
   }
 
   const int q = lane & 15, g = lane >> 4;
@@ -237,7 +283,7 @@ hipError_t launch_cfg(GemmParams p, hipStream_t stream) {
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   if (p.group_m <= 0) p.group_m = 8;
-  dim3 grid(p.tiles_m * p.tiles_n), block(THREADS);
+  dim3 grid(p.tiles_m * p.tiles_n), block(Cfg<BM, BN>::THREADS);
   if (p.bias)
     hipLaunchKernelGGL((gemm32_kernel<BM, BN, ACT, true>), grid, block, 0, stream, p);
   else
@@ -257,17 +303,24 @@ hipError_t launch_act(GemmParams p, int act, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_gemm32(GemmParams p, int act, hipStream_t stream, int num_cus) {
+int gemm32_variant(int64_t M, int64_t N, int num_cus) {
   // 128 x 128 tiles when they give at least one workgroup per CU; else 64 x 64
   // when those give two; else 64 x 32 when those give one; else 32 x 32
   // (measured: 1024^3 runs 5 % faster on 64 x 32 than on 64 x 64, 512^3 best
-  // on 32 x 32).  Variant 1 / 2 / 3 / 4 forces 128 x 128 / 64 x 64 / 32 x 32
-  // / 64 x 32: an autotuning knob.
-  const long tiles128 = (long)((p.M + 127) / 128) * ((p.N + 127) / 128);
-  const long tiles64 = (long)((p.M + 63) / 64) * ((p.N + 63) / 64);
-  const long tiles6432 = (long)((p.M + 63) / 64) * ((p.N + 31) / 32);
+  // on 32 x 32).
+  const long tiles128 = (long)((M + 127) / 128) * ((N + 127) / 128);
+  const long tiles64 = (long)((M + 63) / 64) * ((N + 63) / 64);
+  const long tiles6432 = (long)((M + 63) / 64) * ((N + 31) / 32);
+  return tiles128 >= num_cus ? 1 : tiles64 >= 2L * num_cus ? 2 : tiles6432 >= num_cus ? 4 : 3;
+}
+
+int gemm32_kgroups(int variant) { return variant == 1 ? 1 : variant == 3 ? 4 : 2; }
+
+hipError_t launch_gemm32(GemmParams p, int act, hipStream_t stream, int num_cus) {
+  // Variant 1 / 2 / 3 / 4 forces 128 x 128 / 64 x 64 / 32 x 32 / 64 x 32: an
+  // autotuning knob; 0 takes gemm32_variant's choice.
   int v = p.variant;
-  if (v == 0) v = tiles128 >= num_cus ? 1 : tiles64 >= 2L * num_cus ? 2 : tiles6432 >= num_cus ? 4 : 3;
+  if (v == 0) v = gemm32_variant(p.M, p.N, num_cus);
   if (v == 1) return launch_act<128, 128>(p, act, stream);
   if (v == 2) return launch_act<64, 64>(p, act, stream);
   if (v == 4) return launch_act<64, 32>(p, act, stream);

@@ -26,6 +26,11 @@ struct GemmParams {
 // `stream`; it returns the hipError_t of the launch.
 hipError_t launch_gemm16(GemmParams p, DType in, DType out, int act, hipStream_t stream, int num_cus);
 hipError_t launch_gemm32(GemmParams p, int act, hipStream_t stream, int num_cus);
+// The FP32 GEMM's tile shape for an M x N problem (the variant numbers of
+// GemmParams::variant), and the number of K groups a variant splits K into
+// (variants with the same count give the same bits).
+int gemm32_variant(int64_t M, int64_t N, int num_cus);
+int gemm32_kgroups(int variant);
 
 struct MlpParams {
   const void* x;
