@@ -8,11 +8,12 @@ output).
 
   * the fused GEMM + bias + GELU at 512^3 .. 4096^3 (fp32) and the bf16 FFN
     up-projection (8192 x 4096 x 16384, 134M outputs);
-  * the softplus MLP megakernel: 3 x 128 on 2^20 rows, 5 x 64 on 2^22 rows
-    and the two non-square chains on 2^20 rows;
-  * the training pair at the two MLP workloads: the training forward's out and
-    every stored fp32 activation, the backward's dx and every weight gradient
-    (summed over all rows).
+  * the softplus MLP megakernel: 3 x 128 on 2^20 rows, 5 x 64 on 2^22 rows,
+    the two non-square chains and the two chains whose weights exceed the
+    LDS (6 x 128, 3 x 256; the layer-streaming kernel) on 2^20 rows;
+  * the training pair at the two MLP workloads and the two streamed chains:
+    the training forward's out and every stored fp32 activation, the
+    backward's dx and every weight gradient (summed over all rows).
 
 The inputs are the workloads' own seeded inputs (no periodic or reduced
 stand-in).  The oracle runs on all host threads; the largest case (the FFN,
@@ -57,7 +58,7 @@ def test_gemm_every_output(name):
 
 
 @pytest.mark.parametrize("name", ["fp16_mlp3_d128", "fp16_mlp5_d64", "fp16_mlp_32_128_128_16",
-                                  "fp16_mlp_64_128_96_128_32"])
+                                  "fp16_mlp_64_128_96_128_32", "fp16_mlp6_d128", "fp16_mlp3_d256"])
 def test_mlp_forward_every_output(name):
     w = datagen.WORKLOADS[name]
     progress("full output %s (M=%d dims=%s)" % (name, w.M, w.dims))
@@ -70,7 +71,7 @@ def test_mlp_forward_every_output(name):
     _report(name, y, ref, 2e-2)
 
 
-@pytest.mark.parametrize("name", ["fp16_mlp3_d128", "fp16_mlp5_d64"])
+@pytest.mark.parametrize("name", ["fp16_mlp3_d128", "fp16_mlp5_d64", "fp16_mlp6_d128", "fp16_mlp3_d256"])
 def test_training_pair_every_output(name):
     w = datagen.WORKLOADS[name]
     L = w.L
