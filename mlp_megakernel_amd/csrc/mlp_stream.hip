@@ -53,7 +53,10 @@ struct SGeo {
   static constexpr int MT = 2;            // 16-row sub-tiles per wave tile: one weight read feeds two MFMAs
   static constexpr int TR = 16 * MT;      // rows per wave tile
   static constexpr int KSM = P / 32;      // k steps of the widest layer
-  static constexpr int WAVES = 8;         // two per SIMD
+  // waves per workgroup (one batch of wave tiles) and per SIMD: at width
+  // 256 two (the registers of two 256-unit activation buffers), else three
+  static constexpr int MINW = P == 256 ? 2 : 3;
+  static constexpr int WAVES = 4 * MINW;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWS = P;          // k rows of a slot
   static constexpr int SLOT = ROWS * 128;  // fp16 elements of a slot (128 units per row)
@@ -113,20 +116,21 @@ __device__ __forceinline__ ChunkPos next_chunk(const MlpStreamParams& p, ChunkPo
   return ChunkPos{c.l + 1 < p.L ? c.l + 1 : 0, 0};
 }
 
-// Copy chunk c into the slot at LDS byte address slot: wave w issues copies
-// i = 0 .. KS_l - 1, each filling 4 rows (64 chunks of 16 bytes) from row
-// 4 (w + 8 i) on.  Rows past the layer's k steps are not copied (never read).
+// Copy chunk c into the slot at LDS byte address slot: copy j (0 .. 8 KS_l
+// - 1) fills the 4 rows 4 j .. 4 j + 3 (64 chunks of 16 bytes); wave w
+// issues the copies j = w, w + WAVES, ...  Rows past the layer's k steps
+// are not copied (never read).
 template <int P>
 __device__ __forceinline__ void copy_chunk(const MlpStreamParams& p, ChunkPos c, uint32_t slot, int wu, int lane) {
   const int K = p.dims[c.l], N = p.dims[c.l + 1];
   const int ks = ceil_div(K, 32);
   const u32x4 rs = rsrc_words(p.W[c.l], (uint32_t)K * (uint32_t)N * 2u);
   const int sl = lane & 15;
-  for (int i = 0; i < ks; ++i) {
-    const int row = 4 * (wu + 8 * i) + (lane >> 4);
+  for (int j = wu; j < 8 * ks; j += SGeo<P>::WAVES) {
+    const int row = 4 * j + (lane >> 4);
     const int n = 128 * c.cc + 8 * (sl ^ sswz(row));
     const uint32_t off = row < K && n < N ? ((uint32_t)row * (uint32_t)N + (uint32_t)n) * 2u : S_OFF_NONE;
-    dma16_rsrc(rs, off, slot + (uint32_t)(wu + 8 * i) * 1024u);
+    dma16_rsrc(rs, off, slot + (uint32_t)j * 1024u);
   }
 }
 
@@ -469,7 +473,7 @@ __device__ __forceinline__ int run_chunk(const MlpStreamParams& p, int l, uint32
 }
 
 template <int P, int ACT, bool ST>
-__global__ __launch_bounds__(SGeo<P>::THREADS, 2) void mlp_stream_kernel(MlpStreamParams p) {
+__global__ __launch_bounds__(SGeo<P>::THREADS, SGeo<P>::MINW) void mlp_stream_kernel(MlpStreamParams p) {
   using G = SGeo<P>;
   __shared__ __attribute__((aligned(1024))) _Float16 sW[2 * G::SLOT];
   const int lane = threadIdx.x & 63;
