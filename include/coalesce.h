@@ -181,10 +181,12 @@ size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L, int6
  * each sums its rows' weight-gradient terms in registers) and a reduction
  * that adds the per-workgroup sums in a fixed order.  The other chains that
  * coalesce_mlp_forward supports (up to 16 layers, widths up to 256) run
- * layer by layer, l = L-1 .. 0: one fused kernel per layer computes dz_l (or
- * dx) and the per-workgroup sums of dW[l] from the same row tiles, with dz_l
- * kept as fp16 in the workspace (the precision in which the next layer uses
- * it either way), then the reduction of dW[l].  Either way repeated calls
+ * layer by layer, l = L-1 .. 0: one fused kernel per layer (per pair of
+ * layers at widths up to 128, the pair's inner gradient staying on chip)
+ * computes dz_l (or dx) and the per-workgroup sums of dW[l] from the same
+ * row tiles, with the dz_l passed between launches kept as fp16 in the
+ * workspace (the precision in which the next layer uses it either way),
+ * then the reductions of the dW.  Either way repeated calls
  * give identical bits.  M == 0 gives dW = 0.  Non-square chains write only
  * the true dims[l] x dims[l+1] of each dW and the true columns of dx.
  * Outputs must not overlap the inputs, each other or the workspace.  Calls

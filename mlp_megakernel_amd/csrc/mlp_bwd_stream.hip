@@ -290,6 +290,232 @@ __global__ __launch_bounds__(LGeo<P>::THREADS, 1) void mlp_layer_bwd_kernel(Laye
   }
 }
 
+// Two consecutive layers per launch at width <= 128: the top layer t = l and
+// the bottom layer b = l - 1.  The top layer's dz_l never leaves the
+// workgroup: its epilogue writes it (fp16, the precision the next MFMAs take
+// it in either way) into an LDS tile that the bottom layer's data product and
+// weight gradient read, so a pair of layers reads dz_{l+1}, h_l and h_{l-1}
+// and writes dz_{l-1} (or dx) once -- the HBM round trip of dz_l is gone.
+// Same arithmetic per element as two single-layer launches, so the same bits.
+struct Layer2Args {
+  const void* dz;    // M x Jt fp16 (ldz): dLoss/dz_{l+1}
+  const float* ht;   // M x It fp32 (ldht): h_l
+  const void* hb;    // M x Ib: h_{l-1} in fp32 (l - 1 > 0) or x in fp16, pitch ldhb
+  const void* Wt;    // It x Jt fp16, dense (W_l)
+  const void* Wb;    // Ib x It fp16, dense (W_{l-1})
+  void* out;         // M x Ib fp16 (ldo): dz_{l-1}, dx, or nullptr
+  float* pt;         // grid x It x Jt fp32: partial dW_l
+  float* pb;         // grid x Ib x It fp32: partial dW_{l-1}
+  int64_t ldz, ldht, ldhb, ldo;
+  int It, Jt, Ib, M, num_tiles;
+};
+
+template <int MODE>
+struct Tile2Regs {
+  u32x4 z;                                                   // dz_{l+1}: piece threadIdx.x of the tile
+  f32x4 ht[2];                                               // h_l: rows 16 nt + q, units 16 w + 4 g .. + 3
+  typename std::conditional<MODE == 1, f32x4, u32x2>::type hb[2];  // h_{l-1} (or x), same places
+};
+
+template <int MODE>
+__device__ __forceinline__ void load_tile2(const Layer2Args& a, int tile, int w, int q, int g, Tile2Regs<MODE>& r) {
+  using G = LGeo<128>;
+  const int64_t row0 = (int64_t)tile * G::R;
+  {
+    const __amdgpu_buffer_rsrc_t rz = rows_rsrc(a.dz, a.M, row0, G::R, a.ldz, 2);
+    const int row = threadIdx.x / G::PIECES, c = threadIdx.x % G::PIECES;
+    r.z = __builtin_amdgcn_raw_buffer_load_b128(
+        rz, lmask(8 * c < a.Jt, (uint32_t)row * (uint32_t)(a.ldz * 2) + 16u * (uint32_t)c), 0, 0);
+  }
+  const int u = 16 * w + 4 * g;  // the lane's first unit
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    const __amdgpu_buffer_rsrc_t rt = rows_rsrc(a.ht, a.M, row0 + 16 * nt, 16, a.ldht, 4);
+    r.ht[nt] = __builtin_bit_cast(
+        f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                   rt, lmask(u < a.It, (uint32_t)q * (uint32_t)(a.ldht * 4) + 4u * (uint32_t)u), 0, 0));
+    const __amdgpu_buffer_rsrc_t rb = rows_rsrc(a.hb, a.M, row0 + 16 * nt, 16, a.ldhb, MODE == 1 ? 4 : 2);
+    if constexpr (MODE == 1)
+      r.hb[nt] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rb, lmask(u < a.Ib, (uint32_t)q * (uint32_t)(a.ldhb * 4) + 4u * (uint32_t)u), 0, 0));
+    else
+      r.hb[nt] = __builtin_amdgcn_raw_buffer_load_b64(
+          rb, lmask(u < a.Ib, (uint32_t)q * (uint32_t)(a.ldhb * 2) + 2u * (uint32_t)u), 0, 0);
+  }
+}
+
+// One wave's share of a layer's data product over a 32-row tile: the 16
+// units 16 w .. of the output side (A = rows of W from LDS, B = the staged
+// input-gradient tile), k steps < ksn.  acc[nt] = C[16 w + 4 g + e][16 nt + q].
+__device__ __forceinline__ void data_product128(uint32_t sWr, uint32_t sIn, uint32_t bz, int w, int q, int g,
+                                                int ksn, f32x4 (&acc)[2]) {
+  using G = LGeo<128>;
+  acc[0] = acc[1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const uint32_t arow = sWr + (uint32_t)((16 * w + q) * G::ROWB);
+#pragma unroll
+  for (int ks = 0; ks < G::KS; ++ks) {
+    if (ks < ksn) {
+      const i16x8 b0 = lds_read128(sIn + (bz ^ (uint32_t)(ks << 6)));
+      const i16x8 b1 = lds_read128(sIn + (bz ^ (uint32_t)(ks << 6)) + 16 * G::ROWB);
+      const i16x8 av = lds_read128(arow + ((uint32_t)((g ^ q) << 4) ^ (uint32_t)(ks << 6)));
+      acc[0] = mfma16x16x32(av, b0, acc[0], _Float16{});
+      acc[1] = mfma16x16x32(av, b1, acc[1], _Float16{});
+    }
+  }
+}
+
+// One wave's weight-gradient terms of a 32-row tile: dW^T (rows j of the
+// input-gradient side, columns the wave's 16 units) += sIn^T sH over the
+// rows, j tiles < njn.
+__device__ __forceinline__ void weight_grad128(uint32_t sIn, uint32_t sH, uint32_t trk, int w, int njn,
+                                               f32x4 (&dw)[LGeo<128>::NJ]) {
+  using G = LGeo<128>;
+  const uint32_t ah = sH + (trk ^ (uint32_t)(w << 5));
+  const i16x4 hl = lds_tr(ah), hh = lds_tr(ah + 16 * G::ROWB);
+  const i16x8 hb = (i16x8){hl[0], hl[1], hl[2], hl[3], hh[0], hh[1], hh[2], hh[3]};
+#pragma unroll
+  for (int jt = 0; jt < G::NJ; ++jt) {
+    if (jt < njn) {
+      const uint32_t ad = sIn + (trk ^ (uint32_t)(jt << 5));
+      const i16x4 lo = lds_tr(ad), hi = lds_tr(ad + 16 * G::ROWB);
+      const i16x8 za = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      dw[jt] = mfma16x16x32(za, hb, dw[jt], _Float16{});
+    }
+  }
+}
+
+// Stage W (rows x cols fp16, dense) as LDS rows of 256 bytes, zero past the
+// matrix up to the next 16 rows and 128 columns.
+__device__ __forceinline__ void stage_w128(uint32_t sWr, const void* W, int rows, int cols) {
+  using G = LGeo<128>;
+  const int rr = (rows + 15) & ~15;
+  for (int idx = threadIdx.x; idx < rr * G::PIECES; idx += G::THREADS) {
+    const int i = idx / G::PIECES, c = idx % G::PIECES;
+    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+    if (i < rows && 8 * c < cols) v = *(const u32x4*)((const _Float16*)W + (int64_t)i * cols + 8 * c);
+    lds_write128(sWr + (uint32_t)(i * G::ROWB + ((c ^ (i & 15)) << 4)), v);
+  }
+}
+
+// ACT: the hidden activation (the top layer's derivative, and the bottom
+// layer's in MODE 1).  MODE of the bottom layer: 1 hidden (dz_{l-1} with the
+// derivative), 2 the first layer with dx, 0 the first layer without dx.
+template <int ACT, int MODE>
+__global__ __launch_bounds__(LGeo<128>::THREADS, 1) void mlp_layer2_bwd_kernel(Layer2Args a) {
+  using G = LGeo<128>;
+  constexpr int R = G::R, ROWB = G::ROWB, NJ = G::NJ;
+  // W_l, W_{l-1} (128 rows each), then dz_{l+1}, h_l, dz_l, h_{l-1} tiles (32 rows each)
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[(2 * 128 + 4 * R) * ROWB];
+  const uint32_t sWt = lds_addr(lds), sWb = sWt + 128 * ROWB, sZ = sWb + 128 * ROWB, sH = sZ + R * ROWB,
+                 sZ2 = sH + R * ROWB, sH2 = sZ2 + R * ROWB;
+  const int It = a.It, Jt = a.Jt, Ib = a.Ib;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, q = lane & 15, g = lane >> 4;
+
+  stage_w128(sWt, a.Wt, It, Jt);
+  if constexpr (MODE != 0) stage_w128(sWb, a.Wb, Ib, It);
+
+  const bool on_t = 16 * w < It, on_b = 16 * w < Ib;
+  const int ksn_t = (Jt + 31) >> 5, njn_t = (Jt + 15) >> 4;
+  const int ksn_b = (It + 31) >> 5, njn_b = (It + 15) >> 4;
+  const uint32_t zrow = (uint32_t)(q * ROWB);
+  const uint32_t bz = zrow + (uint32_t)((g ^ zsw(q)) << 4);
+  const int rt = 4 * g + (q >> 2);
+  const uint32_t trk = (uint32_t)(rt * ROWB + ((((q & 3) >> 1) ^ zsw(rt)) << 4) + ((q & 1) << 3));
+  // the lane's 8-byte staging place (rows q and 16 + q, units 16 w + 4 g .. + 3)
+  const uint32_t hst = (zrow + (uint32_t)((((g >> 1) ^ zsw(q)) << 4) + ((g & 1) << 3))) ^ (uint32_t)(w << 5);
+
+  f32x4 dwt[NJ], dwb[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) dwt[j] = dwb[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  Tile2Regs<MODE> nx;
+  int tile = blockIdx.x;
+  if (tile < a.num_tiles) load_tile2<MODE>(a, tile, w, q, g, nx);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  for (; tile < a.num_tiles; tile += gridDim.x) {
+    const int next = tile + gridDim.x;
+    __syncthreads();  // the previous tile's reads of the tiles are done (and the weights are staged)
+    {
+      const int row = threadIdx.x / G::PIECES, c = threadIdx.x % G::PIECES;
+      lds_write128(sZ + (uint32_t)(row * ROWB + ((c ^ zsw(row)) << 4)), nx.z);
+    }
+    f32x4 hct[2];
+    typename std::conditional<MODE == 1, f32x4, u32x2>::type hcb[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      hct[nt] = nx.ht[nt];
+      hcb[nt] = nx.hb[nt];
+      lds_write64(sH + hst + (uint32_t)(16 * nt * ROWB),
+                  (u32x2){pack_f16(hct[nt][0], hct[nt][1]), pack_f16(hct[nt][2], hct[nt][3])});
+      u32x2 vb;
+      if constexpr (MODE == 1)
+        vb = (u32x2){pack_f16(hcb[nt][0], hcb[nt][1]), pack_f16(hcb[nt][2], hcb[nt][3])};
+      else
+        vb = hcb[nt];
+      lds_write64(sH2 + hst + (uint32_t)(16 * nt * ROWB), vb);
+    }
+    if (next < a.num_tiles) load_tile2<MODE>(a, next, w, q, g, nx);
+    __syncthreads();  // sZ holds dz_{l+1}
+
+    // top layer: dz_l = (dz_{l+1} W_l^T) * act'(h_l) into sZ2 (zeros where
+    // the wave's units lie past It, so the bottom product reads finite values)
+    {
+      f32x4 acc[2];
+      if (on_t) {
+        data_product128(sWt, sZ, bz, w, q, g, ksn_t, acc);
+      } else {
+        acc[0] = acc[1] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 v = acc[nt];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = apply_grad<ACT>(v[e], hct[nt][e]);
+        lds_write64(sZ2 + hst + (uint32_t)(16 * nt * ROWB), (u32x2){pack_f16(v[0], v[1]), pack_f16(v[2], v[3])});
+      }
+    }
+    if (on_t) weight_grad128(sZ, sH, trk, w, njn_t, dwt);
+    __syncthreads();  // sZ2 holds dz_l
+
+    // bottom layer: dz_{l-1} (MODE 1) or dx (MODE 2) from dz_l, and dW_{l-1}
+    if constexpr (MODE != 0) {
+      if (on_b) {
+        f32x4 acc[2];
+        data_product128(sWb, sZ2, bz, w, q, g, ksn_b, acc);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          f32x4 v = acc[nt];
+          if constexpr (MODE == 1) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = apply_grad<ACT>(v[e], hcb[nt][e]);
+          }
+          const __amdgpu_buffer_rsrc_t ro = rows_rsrc(a.out, a.M, (int64_t)tile * R + 16 * nt, 16, a.ldo, 2);
+          const int u = 16 * w + 4 * g;
+          __builtin_amdgcn_raw_buffer_store_b64((u32x2){pack_f16(v[0], v[1]), pack_f16(v[2], v[3])}, ro,
+                                                lmask(u < Ib, (uint32_t)q * (uint32_t)(a.ldo * 2) + 2u * (uint32_t)u),
+                                                0, 0);
+        }
+      }
+    }
+    if (on_b) weight_grad128(sZ2, sH2, trk, w, njn_b, dwb);
+  }
+
+  // partial sums: rows i = 16 w + q, columns 16 jt + 4 g .. + 3
+  {
+    const int i = 16 * w + q;
+    float* pt = a.pt + (size_t)blockIdx.x * (size_t)It * (size_t)Jt;
+    float* pb = a.pb + (size_t)blockIdx.x * (size_t)Ib * (size_t)It;
+#pragma unroll
+    for (int jt = 0; jt < NJ; ++jt) {
+      const int j = 16 * jt + 4 * g;
+      if (i < It && j < Jt) *(f32x4*)(pt + (size_t)i * Jt + j) = dwt[jt];
+      if (i < Ib && j < It) *(f32x4*)(pb + (size_t)i * It + j) = dwb[jt];
+    }
+  }
+}
+
 // dW = sum of nparts partials of E float4 groups each (row-major, as dW).  A
 // workgroup owns 32 groups and splits the partial index over 8 slices (slice
 // s adds partials s, s + 8, ... in order), then adds the slice sums in slice
@@ -338,9 +564,13 @@ constexpr int kRowsPerTile = 32;
 size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 struct StreamBwdLayout {
-  size_t partial_bytes, dz_bytes;
+  size_t partial_bytes;  // per-workgroup partial sums (a pair's two layers share it: it holds
+                         // 2 x #CUs partials of the largest layer)
+  size_t dz_bytes;       // one M-row fp16 buffer of hidden gradients
   int ldz;
-  int max_groups;  // workgroups of a layer launch at most
+  int max_groups;        // workgroups of a launch at most
+  bool pairs;            // width <= 128: two layers per launch
+  int nbuf;              // dz buffers needed
 };
 
 StreamBwdLayout stream_bwd_layout(const int* dims, int L, int64_t M, int num_cus) {
@@ -350,13 +580,24 @@ StreamBwdLayout stream_bwd_layout(const int* dims, int L, int64_t M, int num_cus
   for (int l = 0; l < L; ++l) maxij = std::max(maxij, (size_t)dims[l] * (size_t)dims[l + 1]);
   for (int l = 1; l < L; ++l) ldz = std::max(ldz, dims[l]);
   for (int l = 0; l <= L; ++l) mx = std::max(mx, dims[l]);
-  // Width 128 takes 48 KB of LDS and under 128 VGPRs a lane, so two
-  // workgroups share a CU (twice the row tiles in flight); width 256 fills
-  // the LDS with its weights.
+  // Width <= 128: a single-layer launch takes 48 KB of LDS and under 128
+  // VGPRs a lane, so two of its workgroups share a CU (twice the row tiles
+  // in flight); the two-layer launch (96 KB) one.  Width 256 fills the LDS
+  // with one layer's weights.
+  s.pairs = mx <= 128;
   s.max_groups = std::max(num_cus, 1) * (mx > 128 ? 1 : 2);
   s.partial_bytes = align256((size_t)s.max_groups * maxij * sizeof(float));
   s.dz_bytes = align256((size_t)std::max<int64_t>(M, 0) * (size_t)ldz * 2);
   s.ldz = ldz;
+  // hidden gradients that leave a launch: every dz_l (l = L-1 .. 1) one layer
+  // at a time; with pairs only the dz_{l-1} at the bottom of each pair
+  int writes = 0;
+  for (int l = L - 1; l >= 0;) {
+    const int step = s.pairs && l >= 1 ? 2 : 1;
+    if (l - step + 1 > 0) ++writes;
+    l -= step;
+  }
+  s.nbuf = std::min(writes, 2);
   return s;
 }
 
@@ -364,8 +605,7 @@ StreamBwdLayout stream_bwd_layout(const int* dims, int L, int64_t M, int num_cus
 
 size_t mlp_backward_stream_workspace(const int* dims, int L, int64_t M, int num_cus) {
   const StreamBwdLayout s = stream_bwd_layout(dims, L, M, num_cus);
-  const int nbuf = L >= 3 ? 2 : L - 1;  // dz_l for l = L-1 .. 1, alternating between two buffers
-  return s.partial_bytes + (size_t)nbuf * s.dz_bytes;
+  return s.partial_bytes + (size_t)s.nbuf * s.dz_bytes;
 }
 
 hipError_t launch_mlp_backward_stream(const MlpStreamBwdParams& p, int P, int hidden_act, int num_cus,
@@ -373,12 +613,90 @@ hipError_t launch_mlp_backward_stream(const MlpStreamBwdParams& p, int P, int hi
   const StreamBwdLayout s = stream_bwd_layout(p.dims, p.L, p.M, num_cus);
   const int tiles = (int)(((int64_t)p.M + kRowsPerTile - 1) / kRowsPerTile);
   const int nwg = std::max(1, std::min(tiles, s.max_groups));
+  const int nwg2 = std::max(1, std::min(tiles, std::max(num_cus, 1)));
   char* ws = (char*)workspace;
   float* partial = (float*)ws;
-  // dz_l lives in buffer (L - 1 - l) % 2: layer l reads dz_{l+1} from one and
-  // writes dz_l to the other
-  void* zbuf[2] = {ws + s.partial_bytes, ws + s.partial_bytes + s.dz_bytes};
-  for (int l = p.L - 1; l >= 0; --l) {
+  char* zbase = ws + s.partial_bytes;
+  // The hidden gradients that leave a launch alternate between two buffers:
+  // a launch reads the previous one's and writes the other.
+  void* zbuf[2] = {zbase, zbase + s.dz_bytes};
+  const void* zin = p.dout;
+  int64_t ldzin = p.ldd;
+  int zsel = 0;
+  auto reduce = [&](const float* part, int nparts, int I, int J, float* dW) -> hipError_t {
+    const int groups = I * J / 4;
+    hipLaunchKernelGGL(layer_bwd_reduce, dim3((groups + LRED_GROUPS - 1) / LRED_GROUPS),
+                       dim3(LRED_GROUPS * LRED_SLICES), 0, stream, part, nparts, groups, dW);
+    return hipGetLastError();
+  };
+  hipError_t e = hipSuccess;
+  for (int l = p.L - 1; l >= 0;) {
+    if (s.pairs && l >= 1) {
+      // layers l (top) and l - 1 (bottom) in one launch
+      const int b = l - 1;
+      Layer2Args a{};
+      a.dz = zin;
+      a.ldz = ldzin;
+      a.ht = p.acts[l - 1];
+      a.ldht = p.lda;
+      a.Wt = p.W[l];
+      a.Wb = p.W[b];
+      a.It = p.dims[l];
+      a.Jt = p.dims[l + 1];
+      a.Ib = p.dims[b];
+      a.M = p.M;
+      a.num_tiles = tiles;
+      // the top layer's partials, then the bottom layer's: nwg2 x (It Jt + Ib
+      // It) floats, within 2 #CUs x the largest layer
+      a.pt = partial;
+      a.pb = partial + (size_t)nwg2 * (size_t)a.It * (size_t)a.Jt;
+      int mode;
+      if (b > 0) {
+        mode = 1;
+        a.hb = p.acts[b - 1];
+        a.ldhb = p.lda;
+        a.out = zbuf[zsel];
+        a.ldo = s.ldz;
+      } else {
+        mode = p.dx ? 2 : 0;
+        a.hb = p.x;
+        a.ldhb = p.ldx;
+        a.out = p.dx;
+        a.ldo = p.ldq;
+      }
+      // (ACT is the top layer's activation, whose derivative every pair applies)
+      if (mode == 0 && hidden_act == ACT_SOFTPLUS)
+        hipLaunchKernelGGL((mlp_layer2_bwd_kernel<ACT_SOFTPLUS, 0>), dim3(nwg2), dim3(LGeo<128>::THREADS), 0, stream,
+                           a);
+      else if (mode == 0 && hidden_act == ACT_RELU)
+        hipLaunchKernelGGL((mlp_layer2_bwd_kernel<ACT_RELU, 0>), dim3(nwg2), dim3(LGeo<128>::THREADS), 0, stream, a);
+      else if (mode == 0)
+        hipLaunchKernelGGL((mlp_layer2_bwd_kernel<ACT_NONE, 0>), dim3(nwg2), dim3(LGeo<128>::THREADS), 0, stream, a);
+      else if (mode == 2 && hidden_act == ACT_SOFTPLUS)
+        hipLaunchKernelGGL((mlp_layer2_bwd_kernel<ACT_SOFTPLUS, 2>), dim3(nwg2), dim3(LGeo<128>::THREADS), 0, stream,
+                           a);
+      else if (mode == 2 && hidden_act == ACT_RELU)
+        hipLaunchKernelGGL((mlp_layer2_bwd_kernel<ACT_RELU, 2>), dim3(nwg2), dim3(LGeo<128>::THREADS), 0, stream, a);
+      else if (mode == 2)
+        hipLaunchKernelGGL((mlp_layer2_bwd_kernel<ACT_NONE, 2>), dim3(nwg2), dim3(LGeo<128>::THREADS), 0, stream, a);
+      else if (hidden_act == ACT_SOFTPLUS)
+        hipLaunchKernelGGL((mlp_layer2_bwd_kernel<ACT_SOFTPLUS, 1>), dim3(nwg2), dim3(LGeo<128>::THREADS), 0, stream,
+                           a);
+      else if (hidden_act == ACT_RELU)
+        hipLaunchKernelGGL((mlp_layer2_bwd_kernel<ACT_RELU, 1>), dim3(nwg2), dim3(LGeo<128>::THREADS), 0, stream, a);
+      else
+        hipLaunchKernelGGL((mlp_layer2_bwd_kernel<ACT_NONE, 1>), dim3(nwg2), dim3(LGeo<128>::THREADS), 0, stream, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      if ((e = reduce(partial, nwg2, a.It, a.Jt, p.dW[l])) != hipSuccess) return e;
+      if ((e = reduce(a.pb, nwg2, a.Ib, a.It, p.dW[b])) != hipSuccess) return e;
+      if (b > 0) {
+        zin = zbuf[zsel];
+        ldzin = s.ldz;
+        zsel ^= 1;
+      }
+      l -= 2;
+      continue;
+    }
     LayerArgs a{};
     a.I = p.dims[l];
     a.J = p.dims[l + 1];
@@ -386,19 +704,14 @@ hipError_t launch_mlp_backward_stream(const MlpStreamBwdParams& p, int P, int hi
     a.num_tiles = tiles;
     a.W = p.W[l];
     a.partial = partial;
-    if (l == p.L - 1) {
-      a.dz = p.dout;
-      a.ldz = p.ldd;
-    } else {
-      a.dz = zbuf[(p.L - 2 - l) & 1];
-      a.ldz = s.ldz;
-    }
+    a.dz = zin;
+    a.ldz = ldzin;
     int mode;
     if (l > 0) {
       mode = 1;
       a.h = p.acts[l - 1];
       a.ldh = p.lda;
-      a.out = zbuf[(p.L - 1 - l) & 1];
+      a.out = zbuf[zsel];
       a.ldo = s.ldz;
     } else {
       mode = p.dx ? 2 : 0;
@@ -407,13 +720,16 @@ hipError_t launch_mlp_backward_stream(const MlpStreamBwdParams& p, int P, int hi
       a.out = p.dx;
       a.ldo = p.ldq;
     }
-    hipError_t e = P == 256 ? launch_layer_p<256>(a, mode, hidden_act, nwg, stream)
-                            : launch_layer_p<128>(a, mode, hidden_act, nwg, stream);
+    e = P == 256 ? launch_layer_p<256>(a, mode, hidden_act, nwg, stream)
+                 : launch_layer_p<128>(a, mode, hidden_act, nwg, stream);
     if (e != hipSuccess) return e;
-    const int groups = a.I * a.J / 4;
-    hipLaunchKernelGGL(layer_bwd_reduce, dim3((groups + LRED_GROUPS - 1) / LRED_GROUPS),
-                       dim3(LRED_GROUPS * LRED_SLICES), 0, stream, (const float*)partial, nwg, groups, p.dW[l]);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = reduce(partial, nwg, a.I, a.J, p.dW[l])) != hipSuccess) return e;
+    if (l > 0) {
+      zin = zbuf[zsel];
+      ldzin = s.ldz;
+      zsel ^= 1;
+    }
+    l -= 1;
   }
   return hipSuccess;
 }
