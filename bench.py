@@ -78,6 +78,8 @@ def parse():
                     help="skip the non-square chains and the other epilogues / hidden activations")
     ap.add_argument("--prewarm-ms", type=float, default=500.0,
                     help="untimed back-to-back running before the warmup steps of each timed case")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the measured ceilings (matrix-core rate probe, plain HBM copy)")
     ap.add_argument("--harness-iters", type=int, default=100)
     ap.add_argument("--harness-warmup-ms", type=float, default=1000.0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
@@ -288,6 +290,47 @@ def main():
                          "peak": round(PEAK_TRANS_PER_S / 1e12, 3), "unit": "T transcendentals/s",
                          "frac": round(trans / (mean_ms * 1e-3) / PEAK_TRANS_PER_S, 4)}}
 
+    def matrix_ceiling():
+        """What the matrix cores sustain on this board with nothing else
+        sharing the time: the library's rate probe (one 8-wave workgroup per
+        CU, the 256 x 256 GEMM wave's 4 x 8 block of bf16 16x16x32 MFMAs on
+        register operands) with the FFN's operand distribution (A ~ N(0, 1),
+        B ~ N(0, 1/64), 64 distinct sets) and with all-zero operands, each
+        timed like the workloads (pre-warm, 20 back-to-back launches), with
+        the engine clock from the kernel's own counters."""
+        nsets, iters = 64, 1024
+        gen = torch.Generator().manual_seed(20)
+        ops = torch.randn((nsets, 24, 64, 8), generator=gen)
+        ops[:, list(range(4, 12)) + list(range(16, 24))] *= 0.125
+        ops = ops.to(torch.bfloat16).to(dev)
+        waves = mk.matrix_rate_waves()
+        sink = torch.empty(waves * 64, dtype=torch.float32, device=dev)
+        clocks = torch.zeros(waves * 2, dtype=torch.int64, device=dev)
+        out = {"probe": "one 8-wave workgroup per CU, %d rounds of 64 bf16 16x16x32 MFMAs per wave on register "
+                        "operands (2^20 FLOP per round and wave)" % iters}
+        for name, o in (("ffn_operands", ops), ("zero_operands", torch.zeros_like(ops))):
+            khz = [0]
+
+            def run():
+                khz[0] = mk.matrix_rate(o, iters, sink, clocks)[1]
+
+            _, ev = timed_steps(run, 20, 5)
+            c = clocks.view(-1, 2).double().sum(0).cpu()
+            flop = float(waves) * iters * 2 ** 20
+            out[name] = {"tflops": round(flop / (ev * 1e-3) / 1e12, 1), "launch_ms": round(ev, 5),
+                         "engine_clock_ghz": round(float(c[0] / c[1]) * khz[0] / 1e6, 3),
+                         "frac_of_peak": round(flop / (ev * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"], 4)}
+        return out
+
+    def copy_ceiling(w):
+        """A plain device-to-device copy (torch's) of the MLP's input bytes:
+        the same read and write volume as the megakernel, with no compute."""
+        src = torch.empty(w.M * w.dims[0], dtype=torch.float16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        _, ev = timed_steps(lambda: dst.copy_(src), 20, 5)
+        by = 2.0 * src.numel() * 2
+        return {"bytes": by, "launch_ms": round(ev, 5), "achieved": round(by / (ev * 1e-3) / 1e9, 1), "unit": "GB/s"}
+
     def bounds(ms, by, flop, trans):
         """Lower-bound times of one launch (HBM bytes, MFMA flops at the fp16
         dense peak, transcendentals at PEAK_TRANS_PER_S) against the measured
@@ -341,7 +384,7 @@ def main():
         res = {"dims": list(w.dims), "rows": w.M, "kernel_width": P,
                "forward_kernel": "mlp_kernel" if resident else "mlp_stream_kernel",
                "backward_kernels": ("mlp_bwd_kernel + mlp_bwd_reduce" if resident else
-                                    "per layer: mlp_layer_bwd_kernel + layer_bwd_reduce")}
+                                    " + ".join(stream_backward_kernels(w.dims)))}
         if resident:
             res["padded_flop_factor"] = round(2.0 * w.M * w.L * P * P / w.flops(), 3)
         f_ms, f_ev = timed_steps(fwd, max(20, args.steps), 10)
@@ -398,6 +441,15 @@ def main():
     if not is_mlp:
         result["pct_mfma_peak"] = round(100.0 * value / PEAK_TFLOPS[prim.in_dtype], 2)
     result["roofline"] = roof
+    if not is_mlp and prim.in_dtype == "bf16" and not args.no_ceiling:
+        print("bench: matrix-core ceiling", file=sys.stderr, flush=True)
+        ceil = matrix_ceiling()
+        ceil["frac_of_sustained"] = round(roof["achieved"] / ceil["ffn_operands"]["tflops"], 4)
+        roof["measured_ceiling"] = ceil
+    if is_mlp and prim.dims[0] == prim.dims[-1] and not args.no_ceiling:
+        cc = copy_ceiling(prim)
+        cc["frac_of_copy"] = round(roof["achieved"] / cc["achieved"], 4)
+        roof["measured_ceiling"] = cc
     harness = {}
     if not args.no_harness:
         print("bench: pages harness %s" % prim.name, file=sys.stderr, flush=True)
@@ -419,6 +471,10 @@ def main():
             ms, mk_ms = timed_steps(f, max(20, args.steps), 10)
             mlp_res[w.name] = {"rows_per_s": round(w.M / (ms * 1e-3), 1), "ms_per_call": round(ms, 5),
                                "roofline": roofline_mlp(w, mk_ms)}
+            if not args.no_ceiling and w.dims[0] == w.dims[-1]:
+                cc = copy_ceiling(w)
+                cc["frac_of_copy"] = round(mlp_res[w.name]["roofline"]["achieved"] / cc["achieved"], 4)
+                mlp_res[w.name]["roofline"]["measured_ceiling"] = cc
             if not args.no_harness:
                 hf, hu = pages_harness(f), pages_harness(u)
                 harness[w.name] = {"fused": hf, "unfused": hu, "rows_per_s": round(w.M / (hf["median_ms"] * 1e-3), 1),
@@ -731,9 +787,25 @@ def traffic_plan():
         w = datagen.WORKLOADS[name]
         plan += [("warm", name, "stream_forward_warm", ["mlp_stream_kernel"])] * WARM_LAUNCHES
         plan += [("warm", name, "stream_forward_train_warm", ["mlp_stream_kernel"]),
-                 ("warm", name, "stream_backward_warm", ["mlp_layer_bwd_kernel", "layer_bwd_reduce"] * w.L)] \
-            * WARM_LAUNCHES
+                 ("warm", name, "stream_backward_warm", stream_backward_kernels(w.dims))] * WARM_LAUNCHES
     return plan
+
+
+def stream_backward_kernels(dims):
+    """Dispatch sequence of the layer-by-layer backward: from the top, two
+    layers per launch while every width is at most 128 (then one reduction
+    per layer), else one layer per launch and its reduction."""
+    L, seq, l = len(dims) - 1, [], len(dims) - 2
+    pairs = max(dims) <= 128
+    while l >= 0:
+        if pairs and l >= 1:
+            seq += ["mlp_layer2_bwd_kernel", "layer_bwd_reduce", "layer_bwd_reduce"]
+            l -= 2
+        else:
+            seq += ["mlp_layer_bwd_kernel", "layer_bwd_reduce"]
+            l -= 1
+    assert seq.count("layer_bwd_reduce") == L
+    return seq
 
 
 def fusion_traffic(gemm_case, mlp_case, train_case, flush):

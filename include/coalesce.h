@@ -288,6 +288,35 @@ coalesce_status coalesce_activation(const void* X, int64_t ldx, void* Y, int64_t
 coalesce_status coalesce_flush_caches(const void* buf, size_t bytes, void* sink, void* stream);
 
 /*
+ * Benchmark helper: the matrix-core rate and engine clock this board sustains
+ * with nothing else sharing the time ("Coalesce" README, Results: figures are
+ * taken after the boost clock has settled; Triton port and the notes for
+ * future sessions: thermal throttling moves repeated runs by ~10 %).  One
+ * 8-wave workgroup per CU (two waves per SIMD, as the 256 x 256 bf16 GEMM
+ * tile); each wave runs `iters` rounds of the GEMM wave's 4 x 8 block of
+ * v_mfma_f32_16x16x32_bf16 twice, on two sets of operand fragments held in
+ * registers: 64 MFMAs = 2^20 FLOP per wave and round, no memory traffic.
+ *   ops    device, 16-byte aligned: nsets x 24 x 64 fragments of 8 bf16
+ *          (16 bytes); wave w takes set w mod nsets, fragment f of lane l at
+ *          index (set * 24 + f) * 64 + l; fragments 0-3 and 12-15 are the A
+ *          operands, 4-11 and 16-23 the B operands of the two sets.
+ *   sink   device float[waves * 64]: each lane's sum of its accumulators
+ *          (keeps the work alive).
+ *   clocks device uint64[2 * waves]: per wave, the shader-clock counter
+ *          (s_memtime) and the constant-rate counter (s_memrealtime) elapsed
+ *          over its loop; engine clock = first / second x wallclock_khz.
+ *   max_waves  capacity of sink and clocks in waves.
+ *   *waves, *wallclock_khz (host): the launch's wave count (8 per CU) and the
+ *          constant-rate counter's frequency; written before any other check,
+ *          so a call with NULL buffers queries them and returns
+ *          COALESCE_ERR_INVALID_ARGUMENT without a launch.
+ * Errors: NULL or misaligned pointers, nsets or iters <= 0, max_waves below the
+ * launch's wave count -> an error before any launch.
+ */
+coalesce_status coalesce_matrix_rate(const void* ops, int32_t nsets, int32_t iters, void* sink, void* clocks,
+                                     int64_t max_waves, int32_t* waves, int64_t* wallclock_khz, void* stream);
+
+/*
  * Per-shape autotuning ("Coalesce" README, plan's phase 4 and its finding that
  * tile shape was worth more than anything else measured; "MLP Megakernel"
  * README, "Autotuning": an exhaustive search per shape, a cached fast path,

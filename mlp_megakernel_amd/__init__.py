@@ -48,6 +48,7 @@ SIGNATURES = {
     "coalesce_bias_add": (_i32, [_p, _i64, _p, _p, _i64, _i64, _i64, _i32, _i32, _i32, _p]),
     "coalesce_activation": (_i32, [_p, _i64, _p, _i64, _i64, _i64, _i32, _i32, _p]),
     "coalesce_flush_caches": (_i32, [_p, _sz, _p, _p]),
+    "coalesce_matrix_rate": (_i32, [_p, _i32, _i32, _p, _p, _i64, _p, _p, _p]),
     "coalesce_device_cu_count": (_i32, []),
     "coalesce_status_string": (ctypes.c_char_p, [_i32]),
     "coalesce_last_error": (ctypes.c_char_p, []),
@@ -474,6 +475,31 @@ def flush_caches(buf: torch.Tensor, sink: torch.Tensor, stream=None):
     """Stream ``buf`` through L2 / MALL (timing harness helper)."""
     lib = load_library()
     _check(lib.coalesce_flush_caches(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
+
+
+def matrix_rate(ops: torch.Tensor, iters: int, sink: torch.Tensor, clocks: torch.Tensor, stream=None):
+    """Run the matrix-core rate probe once (benchmark helper).  ``ops`` holds
+    nsets x 24 x 64 x 8 bf16 operand fragments, ``sink`` float32 and ``clocks``
+    int64 of at least 64 and 2 entries per wave.  Returns (waves,
+    wallclock_khz); FLOP of the launch = waves x iters x 2^20."""
+    lib = load_library()
+    if ops.dtype != torch.bfloat16 or ops.numel() % (24 * 64 * 8):
+        raise ValueError("ops must be bf16 with a multiple of 24 x 64 x 8 elements")
+    if sink.dtype != torch.float32 or clocks.dtype != torch.int64:
+        raise ValueError("sink must be float32 and clocks int64")
+    cap = min(sink.numel() // 64, clocks.numel() // 2)
+    waves, khz = ctypes.c_int32(0), ctypes.c_int64(0)
+    _check(lib.coalesce_matrix_rate(_ptr(ops), ops.numel() // (24 * 64 * 8), int(iters), _ptr(sink), _ptr(clocks),
+                                    cap, ctypes.byref(waves), ctypes.byref(khz), _stream(stream)))
+    return waves.value, khz.value
+
+
+def matrix_rate_waves() -> int:
+    """Wave count of the matrix-core rate probe's launch on the current device."""
+    lib = load_library()
+    waves, khz = ctypes.c_int32(0), ctypes.c_int64(0)
+    lib.coalesce_matrix_rate(None, 0, 0, None, None, 0, ctypes.byref(waves), ctypes.byref(khz), None)
+    return waves.value
 
 
 def device_cu_count() -> int:

@@ -635,6 +635,31 @@ coalesce_status coalesce_flush_caches(const void* buf, size_t bytes, void* sink,
   return ok();
 }
 
+coalesce_status coalesce_matrix_rate(const void* ops, int32_t nsets, int32_t iters, void* sink, void* clocks,
+                                     int64_t max_waves, int32_t* waves, int64_t* wallclock_khz, void* stream) {
+  if (!waves || !wallclock_khz) return fail(COALESCE_ERR_INVALID_ARGUMENT, "waves or wallclock_khz is NULL");
+  int cus = 0;
+  coalesce_status s = current_cus(&cus);
+  if (s != COALESCE_OK) return s;
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_fail(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return device_fail(e, "hipDeviceGetAttribute");
+  *waves = matrix_rate_waves(cus);
+  *wallclock_khz = khz;
+  if (!ops || !sink || !clocks) return fail(COALESCE_ERR_INVALID_ARGUMENT, "ops, sink or clocks is NULL");
+  if (!aligned16(ops)) return fail(COALESCE_ERR_UNSUPPORTED, "ops must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(sink) & 3u || reinterpret_cast<uintptr_t>(clocks) & 7u)
+    return fail(COALESCE_ERR_UNSUPPORTED, "sink must be 4-byte and clocks 8-byte aligned");
+  if (nsets <= 0 || iters <= 0) return fail(COALESCE_ERR_INVALID_ARGUMENT, "nsets and iters must be positive");
+  if (max_waves < *waves) return fail(COALESCE_ERR_INVALID_ARGUMENT, "sink and clocks hold %lld waves, the launch has %d",
+                                      (long long)max_waves, *waves);
+  e = launch_matrix_rate(ops, nsets, iters, sink, clocks, (hipStream_t)stream, cus);
+  if (e != hipSuccess) return device_fail(e, "matrix_rate launch");
+  return ok();
+}
+
 coalesce_status coalesce_weight_norm(const void* const* v, const void* const* g, void* const* W, const int64_t* dims,
                                      int32_t L, coalesce_dtype dtype, void* stream) {
   WnParams p{};

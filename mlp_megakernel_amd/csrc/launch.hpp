@@ -139,6 +139,12 @@ hipError_t launch_bias_add(const void* X, int64_t ldx, const void* bias, void* Y
 hipError_t launch_activation(const void* X, int64_t ldx, void* Y, int64_t ldy, int M, int N, DType dt, int act,
                              hipStream_t stream, int num_cus);
 hipError_t launch_flush(const void* buf, size_t bytes, void* sink, hipStream_t stream, int num_cus);
+// Matrix-core rate probe: one 8-wave workgroup per CU, each wave `iters`
+// rounds of 64 bf16 16x16x32 MFMAs on register operands; per wave two
+// counter deltas (shader clock, constant-rate clock) into `clocks`.
+int matrix_rate_waves(int num_cus);
+hipError_t launch_matrix_rate(const void* ops, int nsets, int iters, void* sink, void* clocks, hipStream_t stream,
+                              int num_cus);
 // counter += number of 16-bit words that differ between two rows x row_bytes
 // matrices (pitches in bytes; row_bytes even).
 hipError_t launch_compare(const void* a, int64_t pitch_a, const void* b, int64_t pitch_b, int64_t rows,
