@@ -47,15 +47,20 @@ namespace coalesce {
 namespace {
 
 // Geometry per width class P (the widest layer, rounded up to 64, 128 or
-// 256): MT 16-row sub-tiles per wave tile, KSM 32-deep k steps at most.
-template <int P>
+// 256) and form (ST: the training forward): MT 16-row sub-tiles per wave
+// tile, KSM 32-deep k steps at most.
+template <int P, bool ST = false>
 struct SGeo {
   static constexpr int MT = 2;            // 16-row sub-tiles per wave tile: one weight read feeds two MFMAs
   static constexpr int TR = 16 * MT;      // rows per wave tile
   static constexpr int KSM = P / 32;      // k steps of the widest layer
   // waves per workgroup (one batch of wave tiles) and per SIMD: at width
-  // 256 two (the registers of two 256-unit activation buffers), else three
-  static constexpr int MINW = P == 256 ? 2 : 3;
+  // 256 two (the registers of two 256-unit activation buffers); at 128 three
+  // for the inference forward and two for the training forward, whose fp32
+  // activation stores dominate (6 x 128 on 2^20 rows, alternating runs:
+  // forward 0.342 / 0.361 ms with three / two, training forward 0.705 /
+  // 0.651 ms); at 64 three
+  static constexpr int MINW = P == 256 || (P == 128 && ST) ? 2 : 3;
   static constexpr int WAVES = 4 * MINW;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int ROWS = P;          // k rows of a slot
@@ -120,13 +125,13 @@ __device__ __forceinline__ ChunkPos next_chunk(const MlpStreamParams& p, ChunkPo
 // - 1) fills the 4 rows 4 j .. 4 j + 3 (64 chunks of 16 bytes); wave w
 // issues the copies j = w, w + WAVES, ...  Rows past the layer's k steps
 // are not copied (never read).
-template <int P>
+template <int P, bool ST>
 __device__ __forceinline__ void copy_chunk(const MlpStreamParams& p, ChunkPos c, uint32_t slot, int wu, int lane) {
   const int K = p.dims[c.l], N = p.dims[c.l + 1];
   const int ks = ceil_div(K, 32);
   const u32x4 rs = rsrc_words(p.W[c.l], (uint32_t)K * (uint32_t)N * 2u);
   const int sl = lane & 15;
-  for (int j = wu; j < 8 * ks; j += SGeo<P>::WAVES) {
+  for (int j = wu; j < 8 * ks; j += SGeo<P, ST>::WAVES) {
     const int row = 4 * j + (lane >> 4);
     const int n = 128 * c.cc + 8 * (sl ^ sswz(row));
     const uint32_t off = row < K && n < N ? ((uint32_t)row * (uint32_t)N + (uint32_t)n) * 2u : S_OFF_NONE;
@@ -473,8 +478,8 @@ __device__ __forceinline__ int run_chunk(const MlpStreamParams& p, int l, uint32
 }
 
 template <int P, int ACT, bool ST>
-__global__ __launch_bounds__(SGeo<P>::THREADS, SGeo<P>::MINW) void mlp_stream_kernel(MlpStreamParams p) {
-  using G = SGeo<P>;
+__global__ __launch_bounds__((SGeo<P, ST>::THREADS), (SGeo<P, ST>::MINW)) void mlp_stream_kernel(MlpStreamParams p) {
+  using G = SGeo<P, ST>;
   __shared__ __attribute__((aligned(1024))) _Float16 sW[2 * G::SLOT];
   const int lane = threadIdx.x & 63;
   const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -490,7 +495,7 @@ __global__ __launch_bounds__(SGeo<P>::THREADS, SGeo<P>::MINW) void mlp_stream_ke
   // x prefetch and the output stores stay in flight across the barrier.
   ChunkPos cur{0, 0};
   int js = 0;  // slot of cur
-  copy_chunk<P>(p, cur, slot0, wu, lane);
+  copy_chunk<P, ST>(p, cur, slot0, wu, lane);
   // Two activation buffers: every layer reads ha and writes hb, which is
   // then copied into ha (a few register moves per layer, where alternating
   // the roles at run time would make the compiler address the buffers
@@ -511,7 +516,7 @@ __global__ __launch_bounds__(SGeo<P>::THREADS, SGeo<P>::MINW) void mlp_stream_ke
       wait_vm_rt(after);
       __syncthreads();
       const ChunkPos nxt = next_chunk(p, cur);
-      if (!(nxt.l == 0 && nxt.cc == 0 && nextb >= nbatch)) copy_chunk<P>(p, nxt, js ? slot0 : slot1, wu, lane);
+      if (!(nxt.l == 0 && nxt.cc == 0 && nextb >= nbatch)) copy_chunk<P, ST>(p, nxt, js ? slot0 : slot1, wu, lane);
       after = 0;
       if (l == p.L - 1 && CC == 0) {
         // the next batch's x (a zero-row tile past the last batch reads nothing)
@@ -536,7 +541,7 @@ __global__ __launch_bounds__(SGeo<P>::THREADS, SGeo<P>::MINW) void mlp_stream_ke
 // (occupancy from the runtime, cached), or the caller's count.
 template <int P, int ACT, bool ST>
 hipError_t launch_pa(MlpStreamParams p, int num_workgroups, int num_cus, hipStream_t stream) {
-  using G = SGeo<P>;
+  using G = SGeo<P, ST>;
   const int64_t tiles = ((int64_t)p.M + G::TR - 1) / G::TR;
   p.num_tiles = (int)((tiles + G::WAVES - 1) / G::WAVES);  // batches
   static std::atomic<int> per_cu_cache{0};
