@@ -29,7 +29,11 @@ WIDE = (256, 256, 256, 256)               # 3 layers of 256
 DEEP64 = (64,) * 13                       # 12 layers of 64
 MIXED = (200, 256, 40, 136, 256, 8, 64)   # ragged widths, 256-wide layers
 DEEP16 = (32, 96, 64, 128, 64, 96, 128, 32, 64, 128, 96, 64, 32, 128, 64, 96, 48)  # 16 layers
-CHAINS = [DEEP128, WIDE, DEEP64, MIXED, DEEP16]
+# an odd layer count at widths <= 128: two-layer launches, then the first
+# layer on its own
+ODD128 = (128,) * 6                       # 5 layers of 128
+ODDRAG = (72, 128, 120, 8, 128, 104, 40, 128)  # 7 ragged layers
+CHAINS = [DEEP128, WIDE, DEEP64, MIXED, DEEP16, ODD128, ODDRAG]
 IDS = ["x".join(map(str, d)) for d in CHAINS]
 
 
@@ -118,7 +122,8 @@ def test_identity_weights_sigmoid_chain(dims):
     assert np.all(np.abs(f64(dx) - o_dx) <= bound), np.max(np.abs(f64(dx) - o_dx) / bound)
 
 
-@pytest.mark.parametrize("dims", [WIDE, MIXED], ids=["x".join(map(str, d)) for d in (WIDE, MIXED)])
+@pytest.mark.parametrize("dims", [WIDE, MIXED, DEEP128, ODDRAG],
+                         ids=["x".join(map(str, d)) for d in (WIDE, MIXED, DEEP128, ODDRAG)])
 def test_without_dx_deterministic_and_empty(dims):
     w = datagen.MLP3
     L = len(dims) - 1
