@@ -307,14 +307,19 @@ hipError_t launch_act(GemmParams p, int act, hipStream_t stream) {
 }  // namespace
 
 int gemm32_variant(int64_t M, int64_t N, int num_cus) {
-  // 128 x 128 tiles when they give at least one workgroup per CU; else 64 x 64
-  // when those give two; else 64 x 32 when those give one; else 32 x 32
-  // (measured: 1024^3 runs 5 % faster on 64 x 32 than on 64 x 64, 512^3 best
-  // on 32 x 32).
+  // 128 x 128 tiles when they give at least one workgroup per CU; below,
+  // 32 x 32 (four K groups) while 64 x 32 tiles would leave CUs idle, else
+  // the two-group tiles: 64 x 64 while they number at most one per CU,
+  // 64 x 32 beyond.  Measured with the K groups (the per-shape tuner, which
+  // exchanges only same-group tiles): 64 x 64 faster on 768^3 (7 %), 1024^3
+  // (7 %), 1024^2 x 4096 (9 %); 64 x 32 faster on 1536^2 x 1024 (13 %) and
+  // 1280 x 1024^2 (2 %); 512^3 best on 32 x 32.
   const long tiles128 = (long)((M + 127) / 128) * ((N + 127) / 128);
   const long tiles64 = (long)((M + 63) / 64) * ((N + 63) / 64);
   const long tiles6432 = (long)((M + 63) / 64) * ((N + 31) / 32);
-  return tiles128 >= num_cus ? 1 : tiles64 >= 2L * num_cus ? 2 : tiles6432 >= num_cus ? 4 : 3;
+  if (tiles128 >= num_cus) return 1;
+  if (tiles6432 < num_cus) return 3;
+  return tiles64 > num_cus ? 4 : 2;
 }
 
 int gemm32_kgroups(int variant) { return variant == 1 ? 1 : variant == 3 ? 4 : 2; }
