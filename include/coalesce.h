@@ -96,13 +96,23 @@ coalesce_status coalesce_gemm_bias_act(const void* A, int64_t lda, const void* B
  *   dims  HOST array of L + 1 widths
  *   out   device, M x dims[L] fp16, leading dimension ldo >= dims[L] (written)
  * Supported: dtype F16; hidden_act SOFTPLUS, RELU or NONE (a linear chain);
- * widths multiples of 8 and at most 128, in any mix (the quick start's D, H,
- * out_features), L = 1..8 when every width is at most 64, L = 1..4 otherwise.
- * Chains whose widths are not all 64 or all 128 run at kernel width 64 or 128
- * with the weights zero-padded in LDS and x loads / out stores limited to the
- * true columns: the padded units add exact zeros, so the result is the one
- * the narrower chain gives.  x is M x dims[0], out M x dims[L], W[l] dense
- * dims[l] x dims[l+1].  M == 0 is a no-op.
+ * widths multiples of 8 and at most 256, in any mix (the quick start's D, H,
+ * out_features), L = 1..16 ("MLP Megakernel" README, Reports: the megakernel
+ * generalised to N layers).  Chains whose weights fit in LDS (every width at
+ * most 64 and L <= 8, or at most 128 and L <= 4) run the resident kernel
+ * above: all W_l staged in LDS once per workgroup, each layer at the padded
+ * kernel width 64 or 128 (the weights zero-padded in LDS, x loads and out
+ * stores limited to the true columns, the k steps past dims[0] and the output
+ * sub-tiles past dims[L] skipped: the padded units add exact zeros, so the
+ * result is the one the narrower chain gives).  The other chains run the
+ * layer-streaming kernel: the same layer arithmetic, each layer at its own
+ * width, with the weights passed through LDS one 128-unit chunk at a time
+ * (direct copies from the caller's unpadded W[l], double-buffered); softplus
+ * there is evaluated in the exact form max(z, 0) + ln(1 + e^-|z|), equal
+ * in real arithmetic to the resident kernel's guarded form up to the guard's
+ * ln(1 + e^-20) ~ 2e-9 (the two round differently in fp32, so a chain run by
+ * both kernels need not give the same bits).  x is M x dims[0], out
+ * M x dims[L], W[l] dense dims[l] x dims[l+1].  M == 0 is a no-op.
  */
 coalesce_status coalesce_mlp_forward(const void* x, int64_t ldx, const void* const* W, const int64_t* dims, int32_t L,
                                      void* out, int64_t ldo, int64_t M, coalesce_dtype dtype, coalesce_act hidden_act,
@@ -331,7 +341,8 @@ coalesce_status coalesce_matrix_rate(const void* ops, int32_t nsets, int32_t ite
  * output equals the default
  * configuration's bit for bit (every candidate performs the same arithmetic
  * per output element, so equality is the exact test; the default is kept
- * unless a candidate is more than 1 % faster), and records it: later
+ * unless a candidate is more than 1 % faster than the default's faster pass
+ * in both of its own passes), and records it: later
  * calls of coalesce_gemm_bias_act / coalesce_mlp_forward with the same
  * device, shape, dtypes and activation use it.  Each candidate is timed in
  * two passes (the second in reverse order) and keeps its faster time, so

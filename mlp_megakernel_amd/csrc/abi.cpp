@@ -806,7 +806,7 @@ coalesce_status tune(const std::vector<TuneCfg>& cands, Run run, int iters, void
   // single pass would favour whichever candidates come late.  A candidate
   // is valid only if both of its runs reproduced the reference.
   const size_t n = cands.size();
-  std::vector<float> us(n, 0.f);
+  std::vector<float> us(n, 0.f), worst(n, 0.f);
   std::vector<char> ok_run(n, 1);
   for (int pass = 0; pass < 2; ++pass)
     for (size_t j = 0; j < n; ++j) {
@@ -815,27 +815,30 @@ coalesce_status tune(const std::vector<TuneCfg>& cands, Run run, int iters, void
       Trial t = trial([&]() { return run(c); }, iters, st, out, out_pitch_bytes, ref, rows, row_bytes, counter, cus);
       if (t.status != COALESCE_OK) return t.status;
       us[i] = pass == 0 ? t.us : std::min(us[i], t.us);
+      worst[i] = pass == 0 ? t.us : std::max(worst[i], t.us);
       ok_run[i] = ok_run[i] && t.valid;
     }
-  TuneCfg best = dflt;
-  float best_us = 0.f;
   const float default_us = us[0];
   const bool default_valid = ok_run[0] != 0;
   int valid = 0;
-  for (size_t i = 0; i < n; ++i) {
+  for (size_t i = 0; i < n; ++i) valid += ok_run[i] ? 1 : 0;
+  if (valid == 0) return fail(COALESCE_ERR_DEVICE, "no configuration reproduced the default's output");
+  // A candidate replaces the default only if both of its passes beat the
+  // default's faster pass by more than 1 %: on launches of a few
+  // microseconds a single fast pass is often noise (measured: a 5 x 64
+  // chain on 16384 rows once tuned to a configuration 7 % slower).  Among
+  // those, the fastest.  Without a valid default, the fastest valid one.
+  TuneCfg best = dflt;
+  float best_us = default_us;
+  bool have = default_valid;
+  for (size_t i = 1; i < n; ++i) {
     if (!ok_run[i]) continue;
-    ++valid;
-    if (valid == 1 || us[i] < best_us) {
+    const bool beats = default_valid ? worst[i] < 0.99f * default_us : true;
+    if (beats && (!have || us[i] < best_us)) {
       best = cands[i];
       best_us = us[i];
+      have = true;
     }
-  }
-  if (valid == 0) return fail(COALESCE_ERR_DEVICE, "no configuration reproduced the default's output");
-  // a candidate has to beat the default by more than timing noise (1 %) to
-  // replace it
-  if (valid > 0 && default_valid && best_us > 0.99f * default_us) {
-    best = dflt;
-    best_us = default_us;
   }
   {
     std::lock_guard<std::mutex> lock(g_tune_mutex);
