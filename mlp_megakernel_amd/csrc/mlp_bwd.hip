@@ -63,23 +63,32 @@ struct BGeo {
 
 // Staging buffers sH (h_l) and sZ (dz_{l+1}): R rows x D fp16, rows of 2D
 // bytes, 16-byte piece c (units 8 c .. 8 c + 7) of row r at piece position
-// c ^ sfz(r), where sfz depends on r mod 16 only.  The LDS serves 256 bytes
-// (64 four-byte banks) per pass, half a wave for 8-byte accesses and a
-// quarter for 16-byte ones; every pass below then touches each bank once:
-//   * 8-byte writes (4 units of one row per lane): a half-wave covers 16
-//     consecutive rows at one piece index;
-//   * 16-byte writes: a quarter-wave covers 16 consecutive rows at one piece;
-//   * transposing reads: a half-wave covers 8 consecutive rows, two pieces
-//     each.  The 32 rows of a weight-gradient contraction step are paired as
-//     kk = 8 g + 4 h + rho <-> row 16 h + 4 g + rho, so that the rows of one
-//     read are 8 consecutive ones and the second read is 16 rows further
-//     (sfz unchanged: the offset stays an immediate).
+// c ^ sfz(r), where sfz depends on r mod 16 only.  The LDS serves 128 bytes
+// per pass (measured on this GPU with a probe of these access patterns and
+// SQ_LDS_BANK_CONFLICT): 8 lanes of a 16-byte access, 16 lanes of an 8-byte
+// access or of a transposing read.  Then:
+//   * 16-byte writes: 8 lanes cover 8 consecutive rows (from a multiple of
+//     8) at one piece index; sfz mod 8 (D = 128: the 128-byte position of a
+//     piece in a 256-byte row) or sfz (D = 64: 128-byte rows) takes 8
+//     distinct values over those rows: one pass;
+//   * transposing reads: 16 lanes cover 4 consecutive rows (from a multiple
+//     of 4), two neighbouring pieces each; (sfz >> 1) mod 4 takes 4 distinct
+//     values over them: one pass.  The 32 rows of a weight-gradient
+//     contraction step are paired as kk = 8 g + 4 h + rho <-> row 16 h + 4 g
+//     + rho, so that the second read is 16 rows further (sfz unchanged: the
+//     offset stays an immediate);
+//   * 8-byte writes (4 units of one row per lane): 16 lanes cover 16 rows
+//     at the same half of one piece index, which a piece layout can spread
+//     over 8 positions of a pass only: two passes.
+// (The earlier sfz, ((r & 7) << 1) | ((r >> 3) & 1) and (((r >> 1) & 3) << 1)
+// | ((r >> 3) & 1), was laid out for 256-byte passes and took two passes for
+// every 16-byte write.)
 template <int D>
 __device__ __forceinline__ int sfz(int r) {
   if constexpr (D == 128)
-    return ((r & 7) << 1) | ((r >> 3) & 1);
+    return ((r & 7) << 1) ^ ((r >> 2) & 1) ^ ((r >> 3) & 1);
   else
-    return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+    return ((r & 3) << 1) | ((r >> 2) & 1);
 }
 
 // Weights in LDS: W_l as D rows k of D fp16, 16-byte chunks swizzled by

@@ -71,13 +71,29 @@ struct LayerArgs {
   int I, J, M, num_tiles;
 };
 
-// Staged dz_{l+1} / h_l rows: 16-byte piece c of row r sits at c ^ zsw(r).
-// zsw depends on r mod 16 only; it takes 16 distinct values over any 16
-// consecutive rows (the 16-byte reads of the data product: 16 rows, one
-// piece), and zsw >> 1 takes 8 distinct values over any 8 consecutive rows
-// (a transposing read covers 8 consecutive rows, two neighbouring pieces
-// each).  Weight rows use c ^ (i mod 16): 16 consecutive rows, one piece.
-__device__ __forceinline__ int zsw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+// LDS bank model (measured on this GPU with a probe of each access pattern
+// below and SQ_LDS_BANK_CONFLICT): a pass serves 128 bytes, i.e. 8 lanes of
+// a 16-byte access, 16 lanes of an 8-byte access or of a transposing read.
+//
+// Staged dz rows: 16-byte piece c of row r sits at c ^ zsw(r).  zsw depends
+// on r mod 16 only; zsw mod 8 takes 8 distinct values over each 8
+// consecutive rows starting at a multiple of 8 (the 16-byte reads of the
+// data product: 8 lanes = 8 rows, one piece each), and (zsw >> 1) mod 4
+// takes 4 distinct values over each 4 consecutive rows starting at a
+// multiple of 4 (a transposing read: 16 lanes = 4 rows, 32 bytes each).
+// The row-major 16-byte staging writes cover 8 pieces of one row per pass.
+// (The earlier ((r & 7) << 1) | ((r >> 3) & 1) repeats mod 8 within 8 rows:
+// every data-product read took two passes.)  Weight rows use c ^ (i mod
+// 16): 8 consecutive rows, one piece.
+__device__ __forceinline__ int zsw(int r) { return ((r & 7) << 1) ^ ((r >> 2) & 1) ^ ((r >> 3) & 1); }
+
+// Staged h rows (written 8 bytes per lane, read only by transposing reads):
+// 8-byte chunk k of row r sits at k ^ hsw(r).  hsw mod 16 takes 16 distinct
+// values over 16 consecutive rows (a write pass: 16 rows, the same chunk),
+// and (hsw >> 2) mod 4 4 distinct values over each aligned 4 rows (a
+// transposing read: 4 rows, 4 chunks each).  With the piece layout of zsw
+// the 16 rows of a write pass fall on 8 chunk positions (two passes).
+__device__ __forceinline__ int hsw(int r) { return ((r & 3) << 2) ^ (((r >> 2) & 1) * 17) ^ (((r >> 3) & 1) << 1); }
 
 constexpr uint32_t L_OFF_NONE = 0x80000000u;  // past every resource (all span less than 2^31 bytes)
 __device__ __forceinline__ uint32_t lmask(bool ok, uint32_t off) { return ok ? off : L_OFF_NONE; }
@@ -167,7 +183,8 @@ __global__ __launch_bounds__(LGeo<P>::THREADS, 1) void mlp_layer_bwd_kernel(Laye
   const uint32_t bz = zrow + (uint32_t)((g ^ zsw(q)) << 4);           // data-product B piece, k step 0
   const int rt = 4 * g + (q >> 2);                                    // transposing read: row of a 32-row chunk
   const uint32_t trk = (uint32_t)(rt * ROWB + ((((q & 3) >> 1) ^ zsw(rt)) << 4) + ((q & 1) << 3));
-  const uint32_t hst = zrow + (uint32_t)((((g >> 1) ^ zsw(q)) << 4) + ((g & 1) << 3));  // h staging, i tile 0
+  const uint32_t trkh = (uint32_t)(rt * ROWB + (((q & 3) ^ hsw(rt)) << 3));  // the same read in the h layout
+  const uint32_t hst = zrow + (uint32_t)((g ^ hsw(q)) << 3);                 // h staging, i tile 0
 
   f32x4 dw[TI][NJ];
 #pragma unroll
@@ -259,7 +276,7 @@ __global__ __launch_bounds__(LGeo<P>::THREADS, 1) void mlp_layer_bwd_kernel(Laye
     i16x8 hb[TI];
 #pragma unroll
     for (int t = 0; t < TI; ++t) {
-      const uint32_t ad = sH + (trk ^ (uint32_t)((TI * w + t) << 5));
+      const uint32_t ad = sH + (trkh ^ (uint32_t)((TI * w + t) << 5));
       const i16x4 lo = lds_tr(ad), hi = lds_tr(ad + 16 * ROWB);
       hb[t] = (i16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
@@ -367,11 +384,12 @@ __device__ __forceinline__ void data_product128(uint32_t sWr, uint32_t sIn, uint
 
 // One wave's weight-gradient terms of a 32-row tile: dW^T (rows j of the
 // input-gradient side, columns the wave's 16 units) += sIn^T sH over the
-// rows, j tiles < njn.
-__device__ __forceinline__ void weight_grad128(uint32_t sIn, uint32_t sH, uint32_t trk, int w, int njn,
-                                               f32x4 (&dw)[LGeo<128>::NJ]) {
+// rows, j tiles < njn (sIn in the zsw layout, read at trk; sH in the hsw
+// layout, read at trkh).
+__device__ __forceinline__ void weight_grad128(uint32_t sIn, uint32_t sH, uint32_t trk, uint32_t trkh, int w,
+                                               int njn, f32x4 (&dw)[LGeo<128>::NJ]) {
   using G = LGeo<128>;
-  const uint32_t ah = sH + (trk ^ (uint32_t)(w << 5));
+  const uint32_t ah = sH + (trkh ^ (uint32_t)(w << 5));
   const i16x4 hl = lds_tr(ah), hh = lds_tr(ah + 16 * G::ROWB);
   const i16x8 hb = (i16x8){hl[0], hl[1], hl[2], hl[3], hh[0], hh[1], hh[2], hh[3]};
 #pragma unroll
@@ -422,8 +440,12 @@ __global__ __launch_bounds__(LGeo<128>::THREADS, 1) void mlp_layer2_bwd_kernel(L
   const uint32_t bz = zrow + (uint32_t)((g ^ zsw(q)) << 4);
   const int rt = 4 * g + (q >> 2);
   const uint32_t trk = (uint32_t)(rt * ROWB + ((((q & 3) >> 1) ^ zsw(rt)) << 4) + ((q & 1) << 3));
-  // the lane's 8-byte staging place (rows q and 16 + q, units 16 w + 4 g .. + 3)
+  const uint32_t trkh = (uint32_t)(rt * ROWB + (((q & 3) ^ hsw(rt)) << 3));
+  // the lane's 8-byte staging place (rows q and 16 + q, units 16 w + 4 g .. + 3):
+  // dz_l (read by the bottom data product's 16-byte reads too) in the zsw
+  // layout, h_l and h_{l-1} in the hsw layout
   const uint32_t hst = (zrow + (uint32_t)((((g >> 1) ^ zsw(q)) << 4) + ((g & 1) << 3))) ^ (uint32_t)(w << 5);
+  const uint32_t hsth = (zrow + (uint32_t)((g ^ hsw(q)) << 3)) ^ (uint32_t)(w << 5);
 
   f32x4 dwt[NJ], dwb[NJ];
 #pragma unroll
@@ -447,14 +469,14 @@ __global__ __launch_bounds__(LGeo<128>::THREADS, 1) void mlp_layer2_bwd_kernel(L
     for (int nt = 0; nt < 2; ++nt) {
       hct[nt] = nx.ht[nt];
       hcb[nt] = nx.hb[nt];
-      lds_write64(sH + hst + (uint32_t)(16 * nt * ROWB),
+      lds_write64(sH + hsth + (uint32_t)(16 * nt * ROWB),
                   (u32x2){pack_f16(hct[nt][0], hct[nt][1]), pack_f16(hct[nt][2], hct[nt][3])});
       u32x2 vb;
       if constexpr (MODE == 1)
         vb = (u32x2){pack_f16(hcb[nt][0], hcb[nt][1]), pack_f16(hcb[nt][2], hcb[nt][3])};
       else
         vb = hcb[nt];
-      lds_write64(sH2 + hst + (uint32_t)(16 * nt * ROWB), vb);
+      lds_write64(sH2 + hsth + (uint32_t)(16 * nt * ROWB), vb);
     }
     if (next < a.num_tiles) load_tile2<MODE>(a, next, w, q, g, nx);
     __syncthreads();  // sZ holds dz_{l+1}
@@ -476,7 +498,7 @@ __global__ __launch_bounds__(LGeo<128>::THREADS, 1) void mlp_layer2_bwd_kernel(L
         lds_write64(sZ2 + hst + (uint32_t)(16 * nt * ROWB), (u32x2){pack_f16(v[0], v[1]), pack_f16(v[2], v[3])});
       }
     }
-    if (on_t) weight_grad128(sZ, sH, trk, w, njn_t, dwt);
+    if (on_t) weight_grad128(sZ, sH, trk, trkh, w, njn_t, dwt);
     __syncthreads();  // sZ2 holds dz_l
 
     // bottom layer: dz_{l-1} (MODE 1) or dx (MODE 2) from dz_l, and dW_{l-1}
@@ -499,7 +521,7 @@ __global__ __launch_bounds__(LGeo<128>::THREADS, 1) void mlp_layer2_bwd_kernel(L
         }
       }
     }
-    if (on_b) weight_grad128(sZ2, sH2, trk, w, njn_b, dwb);
+    if (on_b) weight_grad128(sZ2, sH2, trk, trkh, w, njn_b, dwb);
   }
 
   // partial sums: rows i = 16 w + q, columns 16 jt + 4 g .. + 3
