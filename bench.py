@@ -648,9 +648,34 @@ def main():
     # ------------------------------------------------- per-shape autotuning
     if not args.no_tune:
         # The ordinary entry point timed before tuning (the launchers' default
-        # configuration) and after it (the recorded winner), both as
-        # sustained back-to-back launches; the record is cleared afterwards so
-        # that nothing else in this run depends on it.
+        # configuration) and after it (the recorded winner), both as the
+        # device time per call of 20 calls replayed from a HIP graph (eager
+        # calls of a few microseconds are bound by the host, which would hide
+        # the configurations' difference); the record is cleared afterwards
+        # so that nothing else in this run depends on it.
+        def graph_call_ms(fn, calls=20, reps=10):
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                for _ in range(calls):
+                    fn()
+            for _ in range(3):
+                graph.replay()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(reps):
+                graph.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            del graph
+            return a.elapsed_time(b) / (reps * calls)
+
         tune_res = {"search_space": {
             "gemm_bf16_fp16": "compiled tiles 256x256 (8 waves), 128x128, 64x64 x persistent grid (occupancy, 1/2 "
                               "and 3/4 of the tile's workgroup slots, one per tile) x tile-group height 4/8/16",
@@ -658,7 +683,8 @@ def main():
             "mlp_resident": "both compiled launch configurations (width 128: 12 waves / 3 per SIMD or 8 / 2; "
                             "width 64: 16 / 4 or 12 / 3) x grid (default, CUs/4, /2, x1, x2, x3)",
             "mlp_streamed": "grid (default, CUs/4, /2, x1, x2, x3)",
-            "validation": "bitwise equality with the default configuration's output"}}
+            "validation": "bitwise equality with the default configuration's output",
+            "timing": "device time per call: 20 calls in a HIP graph, 10 replays, before and after tuning"}}
         cases = [("gemm", datagen.BF16_FFN, None), ("gemm", datagen.FP32_1024, None),
                  ("gemm", datagen.FP32_2048, None)]
         cases += [("mlp", datagen.MLP3, m) for m in (1 << 12, 1 << 14, 1 << 16, 1 << 20)]
@@ -689,11 +715,10 @@ def main():
 
                 def tune():
                     return mk.autotune_mlp_forward(x, Ws, out=Y, iters=5)[1]
-            steps = max(20, args.steps)
-            d_ms, d_ev = timed_steps(run, steps, 5)
+            d_ev = graph_call_ms(run)
             ref = Y.clone()
             rep = tune()
-            t_ms, t_ev = timed_steps(run, steps, 5)
+            t_ev = graph_call_ms(run)
             same = bool(torch.equal(Y, ref))
             tune_res[label] = {"default_us": round(d_ev * 1e3, 2), "tuned_us": round(t_ev * 1e3, 2),
                                "speedup": round(d_ev / t_ev, 4), "bitwise_equal_to_default": same,
