@@ -31,8 +31,6 @@ namespace {
 
 constexpr int BK = 32;
 
-// K groups of a tile shape (4 waves each).
-constexpr int kgroups(int BM, int BN) { return BM == 128 ? 1 : BM == 32 ? 4 : 2; }
 
 __device__ __forceinline__ f32x4 mfma16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -56,9 +54,9 @@ __device__ __forceinline__ int swzB(int k) {
     return ((k >> 2) & 1) << 2;
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int KG_>
 struct Cfg {
-  static constexpr int KG = kgroups(BM, BN);
+  static constexpr int KG = KG_;  // K groups of 4 waves
   static constexpr int THREADS = 256 * KG;
   static constexpr int STAGE = BM * BK + BK * BN;  // floats of one LDS stage (A then B)
   static constexpr int A_BLOCKS = BM * BK * 4 / 1024;  // 1 KB copies per stage for A
@@ -72,7 +70,7 @@ struct Cfg {
 template <int BM, int BN>
 __device__ __forceinline__ void fill_dma(const GemmParams& p, int m0, int n0, int k0, int nlast, float* sa, float* sb,
                                          int wu, int lane) {
-  typedef Cfg<BM, BN> C;
+  typedef Cfg<BM, BN, 1> C;
   const float* A = (const float*)p.A;
   const float* B = (const float*)p.B;
 #pragma unroll
@@ -96,7 +94,7 @@ __device__ __forceinline__ void fill_dma(const GemmParams& p, int m0, int n0, in
 template <int BM, int BN>
 __device__ __forceinline__ void fill_tail(const GemmParams& p, int m0, int n0, int k0, int nlast, float* sa, float* sb,
                                           int w, int lane) {
-  typedef Cfg<BM, BN> C;
+  typedef Cfg<BM, BN, 1> C;
   const float* A = (const float*)p.A;
   const float* B = (const float*)p.B;
   f32x4 ra[C::A_BLOCKS / 4], rb[C::B_BLOCKS / 4];
@@ -133,9 +131,10 @@ __device__ __forceinline__ void fill_tail(const GemmParams& p, int m0, int n0, i
 }
 
 template <int BM, int BN>
-__device__ __forceinline__ void compute_stage(const float* sa, const float* sb, f32x4 (&acc)[Cfg<BM, BN>::NT][Cfg<BM, BN>::MT],
-                                              int wm, int wn, int lane) {
-  typedef Cfg<BM, BN> C;
+__device__ __forceinline__ void compute_stage(const float* sa, const float* sb,
+                                              f32x4 (&acc)[Cfg<BM, BN, 1>::NT][Cfg<BM, BN, 1>::MT], int wm, int wn,
+                                              int lane) {
+  typedef Cfg<BM, BN, 1> C;
   const int q = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int kg = 0; kg < BK / 16; ++kg) {
@@ -163,9 +162,9 @@ __device__ __forceinline__ void compute_stage(const float* sa, const float* sb, 
   }
 }
 
-template <int BM, int BN, int ACT, bool HAS_BIAS>
-__global__ __launch_bounds__((Cfg<BM, BN>::THREADS), 2) void gemm32_kernel(GemmParams p) {
-  typedef Cfg<BM, BN> C;
+template <int BM, int BN, int KG_, int ACT, bool HAS_BIAS>
+__global__ __launch_bounds__((Cfg<BM, BN, KG_>::THREADS), 2) void gemm32_kernel(GemmParams p) {
+  typedef Cfg<BM, BN, KG_> C;
   constexpr int KG = C::KG;
   // per K group two stages of A (BM x BK) and B (BK x BN)
   __shared__ __attribute__((aligned(1024))) float lds[KG * 2 * C::STAGE];
@@ -281,26 +280,26 @@ __global__ __launch_bounds__((Cfg<BM, BN>::THREADS), 2) void gemm32_kernel(GemmP
   }
 }
 
-template <int BM, int BN, int ACT>
+template <int BM, int BN, int KG, int ACT>
 hipError_t launch_cfg(GemmParams p, hipStream_t stream) {
   p.tiles_m = (p.M + BM - 1) / BM;
   p.tiles_n = (p.N + BN - 1) / BN;
   if (p.group_m <= 0) p.group_m = 8;
-  dim3 grid(p.tiles_m * p.tiles_n), block(Cfg<BM, BN>::THREADS);
+  dim3 grid(p.tiles_m * p.tiles_n), block(Cfg<BM, BN, KG>::THREADS);
   if (p.bias)
-    hipLaunchKernelGGL((gemm32_kernel<BM, BN, ACT, true>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((gemm32_kernel<BM, BN, KG, ACT, true>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm32_kernel<BM, BN, ACT, false>), grid, block, 0, stream, p);
+    hipLaunchKernelGGL((gemm32_kernel<BM, BN, KG, ACT, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int KG>
 hipError_t launch_act(GemmParams p, int act, hipStream_t stream) {
   switch (act) {
-    case ACT_GELU: return launch_cfg<BM, BN, ACT_GELU>(p, stream);
-    case ACT_SOFTPLUS: return launch_cfg<BM, BN, ACT_SOFTPLUS>(p, stream);
-    case ACT_RELU: return launch_cfg<BM, BN, ACT_RELU>(p, stream);
-    default: return launch_cfg<BM, BN, ACT_NONE>(p, stream);
+    case ACT_GELU: return launch_cfg<BM, BN, KG, ACT_GELU>(p, stream);
+    case ACT_SOFTPLUS: return launch_cfg<BM, BN, KG, ACT_SOFTPLUS>(p, stream);
+    case ACT_RELU: return launch_cfg<BM, BN, KG, ACT_RELU>(p, stream);
+    default: return launch_cfg<BM, BN, KG, ACT_NONE>(p, stream);
   }
 }
 
@@ -314,9 +313,30 @@ int gemm32_variant(int64_t M, int64_t N, int num_cus) {
   // exchanges only same-group tiles): 64 x 64 faster on 768^3 (7 %), 1024^3
   // (7 %), 1024^2 x 4096 (9 %); 64 x 32 faster on 1536^2 x 1024 (13 %) and
   // 1280 x 1024^2 (2 %); 512^3 best on 32 x 32.
+  //
+  // Past one round of 128 x 128 tiles (two workgroups per CU) the last round
+  // may be mostly empty; 64 x 64 tiles (two K groups, also two workgroups per
+  // CU, a quarter of the work each) then sometimes finish sooner.  Cost model,
+  // fitted to back-to-back times of both shapes on seven problems from 2560^3
+  // to 6144^2 x 1024: a full round of 128 x 128 tiles takes ~0.125 us per
+  // element of K (0.51 ms at K = 4096), one of 64 x 64 tiles ~0.037 (18 % more
+  // per flop); a last round of at most one workgroup per CU costs ~0.55 of a
+  // full one (each workgroup has its CU to itself).  Measured: 3072^3 590 ->
+  // 511 us, 3584^3 908 -> 851 us, 3200^2 x 4096 784 -> 753 us; 4096^3,
+  // 4608^3, 5120^3, 3328^3, 3456^2 x 2048, 3072 x 4096 x 2048 and 6144^2 x
+  // 1024 stay on 128 x 128, 1-14 % faster there (the last four checked
+  // after the fit, as predicted).
   const long tiles128 = (long)((M + 127) / 128) * ((N + 127) / 128);
   const long tiles64 = (long)((M + 63) / 64) * ((N + 63) / 64);
   const long tiles6432 = (long)((M + 63) / 64) * ((N + 31) / 32);
+  const long slots = 2L * num_cus;
+  if (tiles128 > slots) {
+    auto rounds = [&](long n) {  // in hundredths of a full round
+      const long rest = n % slots;
+      return 100 * (n / slots) + (rest == 0 ? 0 : rest <= num_cus ? 55 : 100);
+    };
+    return 37 * rounds(tiles64) < 125 * rounds(tiles128) ? 2 : 1;
+  }
   if (tiles128 >= num_cus) return 1;
   if (tiles6432 < num_cus) return 3;
   return tiles64 > num_cus ? 4 : 2;
@@ -329,10 +349,10 @@ hipError_t launch_gemm32(GemmParams p, int act, hipStream_t stream, int num_cus)
   // autotuning knob; 0 takes gemm32_variant's choice.
   int v = p.variant;
   if (v == 0) v = gemm32_variant(p.M, p.N, num_cus);
-  if (v == 1) return launch_act<128, 128>(p, act, stream);
-  if (v == 2) return launch_act<64, 64>(p, act, stream);
-  if (v == 4) return launch_act<64, 32>(p, act, stream);
-  return launch_act<32, 32>(p, act, stream);
+  if (v == 1) return launch_act<128, 128, 1>(p, act, stream);
+  if (v == 2) return launch_act<64, 64, 2>(p, act, stream);
+  if (v == 4) return launch_act<64, 32, 2>(p, act, stream);
+  return launch_act<32, 32, 4>(p, act, stream);
 }
 
 }  // namespace coalesce

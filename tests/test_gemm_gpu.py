@@ -135,6 +135,26 @@ def test_fused_equals_unfused_fp32_bitwise():
     assert torch.equal(Yf.cpu().view(torch.int32), Yu.cpu().view(torch.int32))
 
 
+def test_fp32_large_problem_on_small_tiles():
+    # Past one full round of 128 x 128 tiles the FP32 launcher may take 64 x 64
+    # tiles (two K groups) when the last 128 x 128 round would be mostly
+    # empty: 3000 x 3100 (600 tiles of 128 x 128 for 512 slots, 2303 of
+    # 64 x 64) does, with ragged edges in M, N and K.  Sampled rows against
+    # the oracle; fused and unfused bit for bit (the same tiles for both).
+    w = datagen.FP32_1024
+    M, N, K = 3000, 3100, 3000
+    A, B, bias = datagen.gemm_inputs(w, M=M, N=N, K=K)
+    progress("fp32 large on 64x64 tiles M=%d N=%d K=%d" % (M, N, K))
+    Ag, Bg, bg = to_gpu(A), to_gpu(B), bias.to("cuda")
+    Yf = mk.gemm_bias_act(Ag, Bg, bg, act="gelu")
+    Yu = mk.activation(mk.bias_add(mk.gemm_bias_act(Ag, Bg, None, act="none"), bg), "gelu")
+    torch.cuda.synchronize()
+    assert torch.equal(Yf.cpu().view(torch.int32), Yu.cpu().view(torch.int32))
+    rows = [0, 1, 63, 64, 1500, M - 1]
+    ref = oracle.gemm_bias_act(f64(A), f64(B), f64(bias), act="gelu", rows=rows)
+    assert_close(f64(Yf)[rows], ref, 1e-4, "fp32 3000x3100x3000 rows")
+
+
 def test_unfused_bf16_baseline_within_tolerance():
     w = datagen.BF16_FFN
     A, B, bias = datagen.gemm_inputs(w, M=300, N=520, K=256)
