@@ -689,8 +689,9 @@ def main():
             "gemm_bf16_fp16": "compiled tiles 256x256 (8 waves), 128x128, 64x64 x persistent grid (occupancy, 1/2 "
                               "and 3/4 of the tile's workgroup slots, one per tile) x tile-group height 4/8/16",
             "gemm_fp32": "compiled tiles 128x128, 64x64, 32x32, 64x32 x tile-group height 4/8/16",
-            "mlp_resident": "both compiled launch configurations (width 128: 12 waves / 3 per SIMD or 8 / 2; "
-                            "width 64: 16 / 4 or 12 / 3) x grid (default, CUs/4, /2, x1, x2, x3)",
+            "mlp_resident": "the launcher's choice and the three compiled launch configurations (32-row "
+                            "wave tiles with width 128: 12 waves / 3 per SIMD or 8 / 2, width 64: 16 / 4 or "
+                            "12 / 3; 16-row tiles with 12 / 16 waves) x grid (default, CUs/4, /2, x1, x2, x3)",
             "mlp_streamed": "grid (default, CUs/4, /2, x1, x2, x3)",
             "validation": "bitwise equality with the default configuration's output",
             "timing": "device time per call: 20 calls in a HIP graph, replayed for 200 ms, then 10 timed "

@@ -366,8 +366,10 @@ typedef struct {
   int32_t variant;     /* GEMM tile shape, 0 = the launcher's heuristic.  FP32: 1 = 128 x 128,
                           2 = 64 x 64, 3 = 32 x 32, 4 = 64 x 32; bf16 / fp16: 1 = 256 x 256,
                           2 = 128 x 128, 3 = 64 x 64.  MLP (chains whose
-                          weights fit in LDS): 0 = the default launch configuration (12 waves per
-                          workgroup at width 128, 16 at 64), 1 = the other (8 / 12 waves) */
+                          weights fit in LDS): 0 = the launcher's choice (16-row wave tiles for
+                          batches of at most ~96 rows per wave of the grid, else 32-row tiles),
+                          1 = 32-row tiles with 8 / 12 waves per workgroup (width 128 / 64),
+                          2 = 16-row tiles, 3 = 32-row tiles (12 / 16 waves) */
 } coalesce_tune_report;
 
 coalesce_status coalesce_autotune_gemm_bias_act(const void* A, int64_t lda, const void* B, int64_t ldb,

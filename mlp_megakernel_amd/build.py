@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcoalesce.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["mlp.hip", "mlp_alt.hip", "mlp_stream.hip", "mlp_bwd.hip", "mlp_bwd_stream.hip", "gemm16.hip", "gemm32.hip", "elementwise.hip", "matrix_rate.hip", "weightnorm.hip", "abi.cpp"]
+SOURCES = ["mlp.hip", "mlp_alt.hip", "mlp_small.hip", "mlp_stream.hip", "mlp_bwd.hip", "mlp_bwd_stream.hip", "gemm16.hip", "gemm32.hip", "elementwise.hip", "matrix_rate.hip", "weightnorm.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 

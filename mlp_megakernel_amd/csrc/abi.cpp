@@ -273,9 +273,10 @@ coalesce_status check_rows(const void* t, int64_t ld, int64_t D, int64_t es, con
   return COALESCE_OK;
 }
 
-// variant: the resident kernel's launch configuration (0 default, 1 the
-// alternative; inference forward only).  num_workgroups == 0 and variant ==
-// 0 let a tuned record of this shape, if any, choose both.
+// variant: the resident kernel's launch configuration (0 the launcher's
+// choice, 1 32-row wave tiles with fewer waves (inference forward only), 2
+// 16-row wave tiles, 3 32-row wave tiles; the same bits).  num_workgroups ==
+// 0 and variant == 0 let a tuned record of this shape, if any, choose both.
 coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* W, const int64_t* dims, int32_t L,
                                  void* out, int64_t ldo, float* const* acts, int64_t lda, int64_t M,
                                  coalesce_dtype dtype, coalesce_act hidden_act, int64_t num_workgroups, int variant,
@@ -363,11 +364,8 @@ coalesce_status mlp_forward_impl(const void* x, int64_t ldx, const void* const* 
       variant = tc.variant;
     }
   }
-  hipError_t e = variant == 1 && !train
-                     ? launch_mlp_alt(p, (int)P, (int)L, act_code(hidden_act), !square, (int)num_workgroups, cus,
-                                      (hipStream_t)stream)
-                     : launch_mlp(p, (int)P, (int)L, act_code(hidden_act), train && L > 1, !square,
-                                  (int)num_workgroups, cus, (hipStream_t)stream);
+  hipError_t e = launch_mlp(p, (int)P, (int)L, act_code(hidden_act), train && L > 1, !square, variant,
+                            (int)num_workgroups, cus, (hipStream_t)stream);
   if (e != hipSuccess) return device_fail(e, "MLP launch");
   return ok();
 }
@@ -943,13 +941,14 @@ coalesce_status coalesce_autotune_mlp_forward(const void* x, int64_t ldx, const 
   if (M == 0) return ok();
   int cus = 0;
   if ((s = current_cus(&cus)) != COALESCE_OK) return s;
-  // both compiled launch configurations of the resident kernel (variant 0:
-  // the default wave count, 1: fewer waves with more registers each), each
-  // with its occupancy-derived grid and fixed grids around one workgroup per
-  // CU; the layer-streaming kernel has one configuration (grids only)
+  // the compiled launch configurations of the resident kernel (variant 0:
+  // the launcher's choice, 1: 32-row wave tiles with fewer waves and more
+  // registers each, 2: 16-row wave tiles, 3: 32-row wave tiles), each with
+  // its occupancy-derived grid and fixed grids around one workgroup per CU;
+  // the layer-streaming kernel has one configuration (grids only)
   std::vector<TuneCfg> cands;
   cands.push_back(TuneCfg{});
-  for (int v : resident ? std::vector<int>{0, 1} : std::vector<int>{0})
+  for (int v : resident ? std::vector<int>{0, 1, 2, 3} : std::vector<int>{0})
     for (int g : {0, cus / 4, cus / 2, cus, 2 * cus, 3 * cus}) add_unique(cands, TuneCfg{g, 0, v});
   const std::string key = mlp_key(current_device(), dims, L, M, hidden_act);
   return tune(

@@ -49,12 +49,19 @@ struct MlpParams {
 // masked to the true columns.  num_workgroups <= 0: a workgroup per #WAVES
 // tiles, at least min(#tiles, #CUs), at most #CUs x occupancy.  store_acts: also write the hidden activations to
 // p.acts (training forward).
-hipError_t launch_mlp(const MlpParams& p, int D, int L, int hidden_act, bool store_acts, bool pad, int num_workgroups,
-                      int num_cus, hipStream_t stream);
-// The same kernels in the second launch configuration (inference forward
-// only; an autotuning candidate, identical results).
+// variant: the launch configuration (all give the same bits): 0 = the
+// launcher's choice (mlp_default_variant), 1 = 32-row wave tiles with fewer
+// waves per workgroup (inference only), 2 = 16-row wave tiles, 3 = 32-row
+// wave tiles.
+hipError_t launch_mlp(const MlpParams& p, int D, int L, int hidden_act, bool store_acts, bool pad, int variant,
+                      int num_workgroups, int num_cus, hipStream_t stream);
+// The launcher's choice of variant for a batch of M rows at kernel width D.
+int mlp_default_variant(int D, int64_t M, bool store_acts, int num_cus);
+// Variants 1 and 2 (mlp_alt.hip, mlp_small.hip).
 hipError_t launch_mlp_alt(const MlpParams& p, int D, int L, int hidden_act, bool pad, int num_workgroups, int num_cus,
                           hipStream_t stream);
+hipError_t launch_mlp_small(const MlpParams& p, int D, int L, int hidden_act, bool store_acts, bool pad,
+                            int num_workgroups, int num_cus, hipStream_t stream);
 
 // Chains for the layer-streaming megakernel (mlp_stream.hip): up to 16
 // layers of widths up to 256, weights streamed through LDS chunk by chunk.

@@ -8,7 +8,8 @@
 // Design for gfx950, widths D of 64 or 128:
 //   * a workgroup copies every W_l into LDS once (L * D * D fp16: 96 KB for
 //     3 x 128, 40 KB for 5 x 64) and reuses it for all of its row tiles;
-//   * a wave works on a tile of 32 rows at a time; workgroup b owns the
+//   * a wave works on a tile of 32 rows at a time (16 for small batches,
+//     see MlpCfg); workgroup b owns the
 //     tiles b, b + G, b + 2G, ... (G workgroups) and its waves claim them one
 //     at a time from a counter in LDS.  The SIMD issues from its oldest
 //     ready wave first, so waves sharing a SIMD progress at very different
@@ -52,38 +53,49 @@ namespace {
 
 // Per-width geometry.  A wave owns a tile of 16 * MT rows; a workgroup has
 // WAVES waves, and the kernel is held to the VGPR budget of MINW waves per
-// SIMD (the second launch-bounds argument).  Both widths use 32-row tiles:
+// SIMD (the second launch-bounds argument).  Large batches use 32-row tiles:
 // one 128-bit weight read from LDS then feeds two MFMAs, which keeps the LDS
 // port below its limit, and the activations of a tile take 2 x 16 (D = 128)
-// or 2 x 8 (D = 64) VGPRs.  Two launch configurations per width, V, both
-// compiled (the autotuner may pick either; the results are the same bits):
-//   V = 0 (default)  D = 128: 12 waves, one workgroup per CU (its 96 KB of
+// or 2 x 8 (D = 64) VGPRs.  Three launch configurations per width, V, all
+// compiled (the launcher picks 0 or 2 by batch size, the autotuner may pick
+// any; every row gets the same bits):
+//   V = 0            D = 128: 12 waves, one workgroup per CU (its 96 KB of
 //                    weights fill the LDS), 3 waves per SIMD within 168
 //                    VGPRs;  D = 64: 16 waves, 4 per SIMD within 128 VGPRs;
 //   V = 1            D = 128: 8 waves, 2 per SIMD within 256 VGPRs;
-//                    D = 64: 12 waves, 3 per SIMD within 168 VGPRs.
+//                    D = 64: 12 waves, 3 per SIMD within 168 VGPRs;
+//   V = 2            as V = 0 with 16-row tiles: a batch of few tiles per
+//                    wave runs each tile's layer chain in half the time.
 template <int D, int V>
 struct MlpCfg;
 template <>
 struct MlpCfg<128, 0> {
-  static constexpr int WAVES = 12, MINW = 3;
+  static constexpr int WAVES = 12, MINW = 3, MT = 2;
 };
 template <>
 struct MlpCfg<64, 0> {
-  static constexpr int WAVES = 16, MINW = 4;
+  static constexpr int WAVES = 16, MINW = 4, MT = 2;
 };
 template <>
 struct MlpCfg<128, 1> {
-  static constexpr int WAVES = 8, MINW = 2;
+  static constexpr int WAVES = 8, MINW = 2, MT = 2;
 };
 template <>
 struct MlpCfg<64, 1> {
-  static constexpr int WAVES = 12, MINW = 3;
+  static constexpr int WAVES = 12, MINW = 3, MT = 2;
+};
+template <>
+struct MlpCfg<128, 2> {
+  static constexpr int WAVES = 12, MINW = 3, MT = 1;
+};
+template <>
+struct MlpCfg<64, 2> {
+  static constexpr int WAVES = 16, MINW = 4, MT = 1;
 };
 
 template <int D, int V = 0>
 struct Geo {
-  static constexpr int MT = 2;                       // 16-row sub-tiles per wave tile
+  static constexpr int MT = MlpCfg<D, V>::MT;        // 16-row sub-tiles per wave tile
   static constexpr int WAVES = MlpCfg<D, V>::WAVES;  // waves per workgroup
   static constexpr int MINW = MlpCfg<D, V>::MINW;    // waves per SIMD the VGPR budget allows
   static constexpr int THREADS = 64 * WAVES;
@@ -95,9 +107,9 @@ struct Geo {
 // Activations of one row tile in MFMA B-operand form: v[s][ks] holds, for
 // rows 16 s .. 16 s + 15, the 8 fp16 inputs of k step ks that this lane feeds
 // (two per dword).
-template <int D>
+template <int D, int V>
 struct HTile {
-  u32x4 v[Geo<D>::MT][Geo<D>::KS];
+  u32x4 v[Geo<D, V>::MT][Geo<D, V>::KS];
 };
 
 template <int D>
@@ -168,9 +180,9 @@ __device__ __forceinline__ Lane<D> lane_setup(const MlpParams& p, const _Float16
 // (stores) or read as zero (loads), so the ragged last tile needs no branch.
 // The host bounds the pitch by 2^24 elements, so 16 rows span less than 2^32
 // bytes.
-template <int D>
+template <int D, int V>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t sub_rsrc(const void* base, int M, int tile, int s, int64_t ld) {
-  const int64_t first = (int64_t)tile * Geo<D>::TR + 16 * s;
+  const int64_t first = (int64_t)tile * Geo<D, V>::TR + 16 * s;
   const int64_t rows = min((int64_t)16, max((int64_t)0, (int64_t)M - first));
   char* p = (char*)base + first * ld * 2;
   return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)((uint32_t)rows * (uint32_t)(ld * 2)), 0x00020000);
@@ -178,9 +190,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sub_rsrc(const void* base, int
 
 // As sub_rsrc, over the fp32 activation matrix acts[l] (pitch ld elements;
 // the host bounds it by 2^24).
-template <int D>
+template <int D, int V>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t act_rsrc(float* base, int M, int tile, int s, int64_t ld) {
-  const int64_t first = (int64_t)tile * Geo<D>::TR + 16 * s;
+  const int64_t first = (int64_t)tile * Geo<D, V>::TR + 16 * s;
   const int64_t rows = min((int64_t)16, max((int64_t)0, (int64_t)M - first));
   char* p = (char*)base + first * ld * 4;
   return __builtin_amdgcn_make_buffer_rsrc(p, (short)0, (int)((uint32_t)rows * (uint32_t)(ld * 4)), 0x00020000);
@@ -202,12 +214,12 @@ constexpr uint32_t OFF_NONE = 0x80000000u;
 __device__ __forceinline__ uint32_t masked(bool ok, uint32_t off) { return ok ? off : OFF_NONE; }
 __device__ __forceinline__ int lane_group() { return (int)(threadIdx.x & 63) >> 4; }
 
-template <int D, bool PAD>
-__device__ __forceinline__ void load_x(const MlpParams& p, const Lane<D>& c, int tile, HTile<D>& h) {
+template <int D, int V, bool PAD>
+__device__ __forceinline__ void load_x(const MlpParams& p, const Lane<D>& c, int tile, HTile<D, V>& h) {
   const uint32_t xoff = opaque(c.xoff);  // keeps the k-step offsets in the instructions' immediate field
 #pragma unroll
-  for (int s = 0; s < Geo<D>::MT; ++s) {
-    const __amdgpu_buffer_rsrc_t rs = sub_rsrc<D>(p.x, p.M, tile, s, p.ldx);
+  for (int s = 0; s < Geo<D, V>::MT; ++s) {
+    const __amdgpu_buffer_rsrc_t rs = sub_rsrc<D, V>(p.x, p.M, tile, s, p.ldx);
 #pragma unroll
     for (int ks = 0; ks < Geo<D>::KS; ++ks) {
       // units 32 ks + 8 g .. + 7 of the row
@@ -294,16 +306,16 @@ __device__ __forceinline__ void interleave() {
 // Hidden layer l for one row tile: hout = act(hin W_l), in the step pipeline
 // described at the top, with the unguarded softplus; the largest output is
 // folded into mx.
-template <int D, int l, int ACT, bool ST, bool PAD>
-__device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& c, const HTile<D>& hin,
-                                             HTile<D>& hout, f16x2& mx, int tile) {
-  using G = Geo<D>;
+template <int D, int V, int l, int ACT, bool ST, bool PAD>
+__device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& c, const HTile<D, V>& hin,
+                                             HTile<D, V>& hout, f16x2& mx, int tile) {
+  using G = Geo<D, V>;
   constexpr bool SP = ACT == ACT_SOFTPLUS;
   __amdgpu_buffer_rsrc_t ra[G::MT];
   uint32_t aoff = 0;
   if constexpr (ST) {
 #pragma unroll
-    for (int s = 0; s < G::MT; ++s) ra[s] = act_rsrc<D>(p.acts[l], p.M, tile, s, p.lda);
+    for (int s = 0; s < G::MT; ++s) ra[s] = act_rsrc<D, V>(p.acts[l], p.M, tile, s, p.lda);
     aoff = opaque(c.aoff);
   }
   constexpr bool IN_B2 = SP && l > 0;  // does the accumulator arrive in base-2 units?
@@ -399,16 +411,16 @@ __device__ __forceinline__ void hidden_layer(const MlpParams& p, const Lane<D>& 
 // Last layer l = L - 1 for one row tile: out = hin W_L (times ln 2 when hin
 // is in base-2 units), fp16, stored through a buffer resource that drops the
 // rows beyond M.
-template <int D, int l, int ACT, bool PAD>
-__device__ __forceinline__ void last_layer(const MlpParams& p, const Lane<D>& c, const HTile<D>& hin,
+template <int D, int V, int l, int ACT, bool PAD>
+__device__ __forceinline__ void last_layer(const MlpParams& p, const Lane<D>& c, const HTile<D, V>& hin,
                                            int tile) {
-  using G = Geo<D>;
+  using G = Geo<D, V>;
   constexpr bool IN_B2 = ACT == ACT_SOFTPLUS && l > 0;
   constexpr int VPM = (G::MT * 4 * (IN_B2 ? 3 : 1) / 2 + G::KS * G::MT - 1) / (G::KS * G::MT);
   constexpr int ST_EVERY = G::KS;  // MT stores per step (every other step) over KS * MT MFMAs
   __amdgpu_buffer_rsrc_t rs[G::MT];
 #pragma unroll
-  for (int s = 0; s < G::MT; ++s) rs[s] = sub_rsrc<D>(p.out, p.M, tile, s, p.ldo);
+  for (int s = 0; s < G::MT; ++s) rs[s] = sub_rsrc<D, V>(p.out, p.M, tile, s, p.ldo);
   const uint32_t ooff = opaque(c.ooff);  // keeps the sub-tile offsets in the instructions' immediate field
   uint32_t wk[G::KS];
 #pragma unroll
@@ -464,17 +476,23 @@ __device__ __forceinline__ void last_layer(const MlpParams& p, const Lane<D>& c,
 // Per element it executes the same MFMA accumulation order and the same
 // exp2/add/log2/pack instructions as the pipelined path, so it reproduces
 // that path's bits wherever the guard does not apply.
-template <int D, int L, int ACT, bool ST, bool PAD>
+template <int D, int V, int L, int ACT, bool ST, bool PAD>
 __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& c, int tile) {
-  using G = Geo<D>;
+  using G = Geo<D, V>;
   constexpr bool SP = ACT == ACT_SOFTPLUS;
 #pragma unroll 1
   for (int s = 0; s < G::MT; ++s) {
-    const __amdgpu_buffer_rsrc_t rx = sub_rsrc<D>(p.x, p.M, tile, s, p.ldx);
-    const __amdgpu_buffer_rsrc_t ro = sub_rsrc<D>(p.out, p.M, tile, s, p.ldo);
+    const __amdgpu_buffer_rsrc_t rx = sub_rsrc<D, V>(p.x, p.M, tile, s, p.ldx);
+    const __amdgpu_buffer_rsrc_t ro = sub_rsrc<D, V>(p.out, p.M, tile, s, p.ldo);
     const uint32_t xoff = opaque(c.xoff), ooff = opaque(c.ooff);
+    // hn and ev fully defined on every path (the last layer writes neither,
+    // and h is not copied from hn after it): with undefined lanes in that
+    // loop-carried copy, the 16-row-tile build of this path reused the
+    // registers of the loaded x before the first layer read them
     u32x4 h[G::KS], hn[G::KS];
-    u32x2 ev;
+    u32x2 ev = (u32x2){0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) hn[ks] = (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks)
       h[ks] = __builtin_amdgcn_raw_buffer_load_b128(
@@ -513,7 +531,7 @@ __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& 
           if constexpr (ST) {
             const float sc = SP ? 0.693147180559945309f : 1.0f;
             const uint32_t off = opaque(c.aoff) + 64u * (uint32_t)t;
-            store_act(act_rsrc<D>(p.acts[l], p.M, tile, s, p.lda),
+            store_act(act_rsrc<D, V>(p.acts[l], p.M, tile, s, p.lda),
                       PAD ? masked(16 * t + 4 * lane_group() < p.dims[l + 1], off) : off, v[0] * sc, v[1] * sc,
                       v[2] * sc, v[3] * sc);
           }
@@ -531,22 +549,24 @@ __device__ __forceinline__ void tile_guarded(const MlpParams& p, const Lane<D>& 
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (l + 1 < L) {
 #pragma unroll
-      for (int ks = 0; ks < G::KS; ++ks) h[ks] = hn[ks];
+        for (int ks = 0; ks < G::KS; ++ks) h[ks] = hn[ks];
+      }
     }
   }
 }
 
 // One row tile, layers l .. L-1.  hin holds the layer-l input; hfree is free.
 // mx collects the largest unguarded softplus output.
-template <int D, int L, int l, int ACT, bool ST, bool PAD>
-__device__ __forceinline__ void tile_chain(const MlpParams& p, const Lane<D>& c, int tile, HTile<D>& hin,
-                                           HTile<D>& hfree, f16x2& mx) {
+template <int D, int V, int L, int l, int ACT, bool ST, bool PAD>
+__device__ __forceinline__ void tile_chain(const MlpParams& p, const Lane<D>& c, int tile, HTile<D, V>& hin,
+                                           HTile<D, V>& hfree, f16x2& mx) {
   if constexpr (l < L - 1) {
-    hidden_layer<D, l, ACT, ST, PAD>(p, c, hin, hfree, mx, tile);
-    tile_chain<D, L, l + 1, ACT, ST, PAD>(p, c, tile, hfree, hin, mx);
+    hidden_layer<D, V, l, ACT, ST, PAD>(p, c, hin, hfree, mx, tile);
+    tile_chain<D, V, L, l + 1, ACT, ST, PAD>(p, c, tile, hfree, hin, mx);
   } else {
-    last_layer<D, l, ACT, PAD>(p, c, hin, tile);
+    last_layer<D, V, l, ACT, PAD>(p, c, hin, tile);
   }
 }
 
@@ -585,8 +605,8 @@ __global__ __launch_bounds__((Geo<D, V>::THREADS), (Geo<D, V>::MINW)) void mlp_k
   // zero rows, so it reads zeros without touching memory): a conditional
   // load would make the compiler wait for every outstanding memory operation
   // where the paths join, stores included.
-  HTile<D> ha, hb, hc;
-  if (tile < p.num_tiles) load_x<D, PAD>(p, c, tile, ha);
+  HTile<D, V> ha, hb, hc;
+  if (tile < p.num_tiles) load_x<D, V, PAD>(p, c, tile, ha);
   // The compiler's memory-counter waits at the loop head are those of the
   // loop entry and of the back edge merged.  Entered with this load still in
   // flight, the first use of ha waited as if it had just been issued -- on
@@ -598,18 +618,18 @@ __global__ __launch_bounds__((Geo<D, V>::THREADS), (Geo<D, V>::MINW)) void mlp_k
   __builtin_amdgcn_s_waitcnt(0x0F70);
   while (tile < p.num_tiles) {
     int next = claim_tile(&s_next);
-    load_x<D, PAD>(p, c, next, hc);
-    tile_chain<D, L, 0, ACT, ST, PAD>(p, c, tile, ha, hb, mx);
+    load_x<D, V, PAD>(p, c, next, hc);
+    tile_chain<D, V, L, 0, ACT, ST, PAD>(p, c, tile, ha, hb, mx);
     tile = next;
     if (tile >= p.num_tiles) break;
     next = claim_tile(&s_next);
-    load_x<D, PAD>(p, c, next, hb);
-    tile_chain<D, L, 0, ACT, ST, PAD>(p, c, tile, hc, ha, mx);
+    load_x<D, V, PAD>(p, c, next, hb);
+    tile_chain<D, V, L, 0, ACT, ST, PAD>(p, c, tile, hc, ha, mx);
     tile = next;
     if (tile >= p.num_tiles) break;
     next = claim_tile(&s_next);
-    load_x<D, PAD>(p, c, next, ha);
-    tile_chain<D, L, 0, ACT, ST, PAD>(p, c, tile, hb, hc, mx);
+    load_x<D, V, PAD>(p, c, next, ha);
+    tile_chain<D, V, L, 0, ACT, ST, PAD>(p, c, tile, hb, hc, mx);
     tile = next;
   }
   if constexpr (ACT == ACT_SOFTPLUS && L > 1) {
@@ -626,7 +646,7 @@ __global__ __launch_bounds__((Geo<D, V>::THREADS), (Geo<D, V>::MINW)) void mlp_k
       wait_vmcnt0();
       __syncthreads();
       for (int t = (int)blockIdx.x + wv * (int)gridDim.x; t < p.num_tiles; t += G::WAVES * (int)gridDim.x)
-        tile_guarded<D, L, ACT, ST, PAD>(p, c, t);
+        tile_guarded<D, V, L, ACT, ST, PAD>(p, c, t);
     }
   }
 }
