@@ -57,6 +57,7 @@ __device__ __forceinline__ int swzB(int k) {
 template <int BM, int BN, int KG_>
 struct Cfg {
   static constexpr int KG = KG_;  // K groups of 4 waves
+  static constexpr int NS = 2;    // LDS stages per K group (copies one K step ahead)
   static constexpr int THREADS = 256 * KG;
   static constexpr int STAGE = BM * BK + BK * BN;  // floats of one LDS stage (A then B)
   static constexpr int A_BLOCKS = BM * BK * 4 / 1024;  // 1 KB copies per stage for A
@@ -162,12 +163,26 @@ __device__ __forceinline__ void compute_stage(const float* sa, const float* sb,
   }
 }
 
+// Wait for every copy this wave has in flight (the builtin, not inline asm,
+// so that the compiler's own counter bookkeeping sees it).  Encoding: vmcnt
+// 0, expcnt 7 and lgkmcnt 15 (those two untouched).
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Workgroup barrier of the K loop: the wave's own LDS accesses complete
+// (lgkmcnt 0), then s_barrier; the loop writes no global memory, so it needs
+// none of __syncthreads' fences.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+#pragma clang diagnostic pop
+
 template <int BM, int BN, int KG_, int ACT, bool HAS_BIAS>
 __global__ __launch_bounds__((Cfg<BM, BN, KG_>::THREADS), 2) void gemm32_kernel(GemmParams p) {
   typedef Cfg<BM, BN, KG_> C;
   constexpr int KG = C::KG;
-  // per K group two stages of A (BM x BK) and B (BK x BN)
-  __shared__ __attribute__((aligned(1024))) float lds[KG * 2 * C::STAGE];
+  constexpr int NS = C::NS;
+  // per K group NS stages of A (BM x BK) and B (BK x BN)
+  __shared__ __attribute__((aligned(1024))) float lds[KG * NS * C::STAGE];
 
   int tm, tn;
   tile_coords(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
@@ -181,10 +196,7 @@ __global__ __launch_bounds__((Cfg<BM, BN, KG_>::THREADS), 2) void gemm32_kernel(
   const int wu = __builtin_amdgcn_readfirstlane(wl);
   const int wm = wl & 1, wn = wl >> 1;
   const int nlast = ((p.N - 1) >> 2) << 2;
-  float* sA0 = lds + (2 * kg) * C::STAGE;
-  float* sB0 = sA0 + BM * BK;
-  float* sA1 = sA0 + C::STAGE;
-  float* sB1 = sA1 + BM * BK;
+  float* const stages = lds + (NS * kg) * C::STAGE;  // stage i: A at i STAGE, B after it
 
   f32x4 acc[C::NT][C::MT];
 #pragma unroll
@@ -199,31 +211,35 @@ __global__ __launch_bounds__((Cfg<BM, BN, KG_>::THREADS), 2) void gemm32_kernel(
   const int per = (ktiles + KG - 1) / KG;
   const int kbeg = kg * per;
   const int kend = min(ktiles, kbeg + per);
-  if (kbeg < kend) {
-    if (kbeg < kfull)
-      fill_dma<BM, BN>(p, m0, n0, kbeg * BK, nlast, sA0, sB0, wu, lane);
+  auto fill = [&](int i, int k) {  // K step k into stage i
+    float* sa = stages + i * C::STAGE;
+    if (k < kfull)
+      fill_dma<BM, BN>(p, m0, n0, k * BK, nlast, sa, sa + BM * BK, wu, lane);
     else
-      fill_tail<BM, BN>(p, m0, n0, kbeg * BK, nlast, sA0, sB0, wu, lane);
-  }
-  for (int j0 = 0; j0 < per; j0 += 2) {
+      fill_tail<BM, BN>(p, m0, n0, k * BK, nlast, sa, sa + BM * BK, wu, lane);
+  };
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int j = j0 + half;
+  for (int i = 0; i + 1 < NS; ++i)
+    if (kbeg + i < kend) fill(i, kbeg + i);
+  // Step j: wait for this wave's copies, barrier (every wave's copies of step
+  // j have landed, and every wave is done with step j - 1, whose stage is
+  // refilled next), copy step j + 1, compute step j.  (Written this way, with
+  // the stage an immediate of the unrolled loop and the wait visible to the
+  // compiler, the 128 x 128 tile runs 4096^3 in 1024 instead of 1058 us, the
+  // other tiles unchanged.)
+  for (int j0 = 0; j0 < per; j0 += NS) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int j = j0 + i;
       if (j < per) {
         const int k = kbeg + j;
-        float* ca = half ? sA1 : sA0;
-        float* cb = half ? sB1 : sB0;
-        float* na = half ? sA0 : sA1;
-        float* nb = half ? sB0 : sB1;
-        wait_vmcnt0();
-        __syncthreads();
-        if (k + 1 < kend) {
-          if (k + 1 < kfull)
-            fill_dma<BM, BN>(p, m0, n0, (k + 1) * BK, nlast, na, nb, wu, lane);
-          else
-            fill_tail<BM, BN>(p, m0, n0, (k + 1) * BK, nlast, na, nb, wu, lane);
+        wait_copies();
+        lds_barrier();
+        if (k + NS - 1 < kend) fill((i + NS - 1) % NS, k + NS - 1);
+        if (k < kend) {
+          const float* sa = stages + i * C::STAGE;
+          compute_stage<BM, BN>(sa, sa + BM * BK, acc, wm, wn, lane);
         }
-        if (k < kend) compute_stage<BM, BN>(ca, cb, acc, wm, wn, lane);
       }
     }
   }
