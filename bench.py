@@ -958,7 +958,8 @@ def summarize_counters(fetch_csv, write_csv):
     w_fac = (8192 * 16384 * 2) / (wr[1][4][0] * KiB)
     C = "mlp_megakernel_amd/csrc/"
     srcs = {"gemm16_kernel": [C + "gemm16.hip", C + "common.hpp"], "gemm32_kernel": [C + "gemm32.hip", C + "common.hpp"],
-            "mlp_kernel": [C + "mlp.hip", C + "mlp_kernel.hpp", C + "mlp_common.hpp", C + "common.hpp"],
+            "mlp_kernel": [C + "mlp.hip", C + "mlp_small.hip", C + "mlp_alt.hip", C + "mlp_kernel.hpp",
+                           C + "mlp_common.hpp", C + "common.hpp"],
             "backward": [C + "mlp_bwd.hip", C + "mlp_common.hpp", C + "common.hpp"],
             "mlp_stream_kernel": [C + "mlp_stream.hip", C + "mlp_common.hpp", C + "common.hpp"],
             "stream_backward": [C + "mlp_bwd_stream.hip", C + "mlp_common.hpp", C + "common.hpp"]}
