@@ -13,12 +13,14 @@
 //     the chain (layer 0 chunk 0, ..., layer L-1 last chunk) are copied in
 //     order into two LDS slots by direct buffer-to-LDS copies, the next chunk
 //     while the current one is used, so the copies overlap the MFMAs;
-//   * a workgroup of 8 waves works on a batch of 8 row tiles (one per wave,
-//     16 rows at width 256, 32 rows below) and takes the whole batch through
-//     the chain in lockstep: a barrier per chunk publishes the slot its
-//     copies filled; the activations stay in registers between layers, as in
-//     the resident kernel; the next batch's x is loaded during the current
-//     batch;
+//   * a workgroup of W waves works on up to W row tiles of 32 rows at a time
+//     (one per wave; in round r workgroup b takes tiles r G W + b + w G, so a
+//     small batch spreads over the workgroups) and takes them through the
+//     chain in lockstep: a barrier per chunk publishes the slot its copies
+//     filled; the activations stay in registers between layers, as in the
+//     resident kernel; the next round's x is loaded during the current one;
+//     a wave without a tile copies its share of the chunks but skips their
+//     arithmetic;
 //   * W_l stays in its natural layout (rows k, n contiguous).  The MFMA's A
 //     operand is W^T, read with gfx950's transposing LDS read
 //     (ds_read_b64_tr_b16), which gives each 16-lane group any 4 rows: so the
@@ -54,7 +56,7 @@ struct SGeo {
   static constexpr int MT = 2;            // 16-row sub-tiles per wave tile: one weight read feeds two MFMAs
   static constexpr int TR = 16 * MT;      // rows per wave tile
   static constexpr int KSM = P / 32;      // k steps of the widest layer
-  // waves per workgroup (one batch of wave tiles) and per SIMD: at width
+  // waves per workgroup (up to one wave tile each) and per SIMD: at width
   // 256 two (the registers of two 256-unit activation buffers); at 128 three
   // for the inference forward and two for the training forward, whose fp32
   // activation stores dominate (6 x 128 on 2^20 rows, alternating runs:
@@ -484,11 +486,18 @@ __global__ __launch_bounds__((SGeo<P, ST>::THREADS), (SGeo<P, ST>::MINW)) void m
   const int lane = threadIdx.x & 63;
   const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t slot0 = lds_addr(sW), slot1 = slot0 + 2u * G::SLOT;
-  const int nbatch = p.num_tiles;  // batches of WAVES wave tiles
-  int batch = blockIdx.x;
-  if (batch >= nbatch) return;
+  // Rounds: in round r workgroup b takes the wave tiles r G W + b + w G
+  // (G workgroups, W waves, w the wave), so a batch of fewer tiles than
+  // G W spreads over the workgroups (one tile each while there are at most
+  // G) instead of filling the waves of a few; the round goes on while the
+  // workgroup's first wave has a tile.
+  const int ntiles = p.num_tiles;
+  const int G_ = (int)gridDim.x;
+  const int64_t per_round = (int64_t)G_ * G::WAVES;
+  int64_t first = blockIdx.x;  // tile of wave 0 in this round
+  if (first >= ntiles) return;
 
-  // The chunk sequence repeats per batch; copies run one chunk ahead.  The
+  // The chunk sequence repeats per round; copies run one chunk ahead.  The
   // memory counter completes in order, so waiting for a chunk's copies means
   // waiting until no more than the wave's later operations are in flight:
   // `after` counts them (the x loads and stores issued since), and the
@@ -500,13 +509,21 @@ __global__ __launch_bounds__((SGeo<P, ST>::THREADS), (SGeo<P, ST>::MINW)) void m
   // then copied into ha (a few register moves per layer, where alternating
   // the roles at run time would make the compiler address the buffers
   // indirectly).  The last layer writes to memory, so hb is free while it
-  // runs: the next batch's x is loaded into it there.
+  // runs: the next round's x is loaded into it there.
   STile<P> ha, hb;
-  load_x<P>(p, batch * G::WAVES + wu, lane, ha);
+  // (tile indices past the last are clamped to it: a zero-row tile whose
+  // buffer resources start right after the rows)
+  load_x<P>(p, (int)min(first + (int64_t)wu * G_, (int64_t)ntiles), lane, ha);
   int after = G::MT * G::KSM;
-  while (batch < nbatch) {
-    const int tile = batch * G::WAVES + wu;
-    const int nextb = batch + (int)gridDim.x;
+  while (first < ntiles) {
+    const int64_t tile64 = first + (int64_t)wu * G_;
+    const int tile = (int)min(tile64, (int64_t)ntiles);
+    const int64_t next_first = first + per_round;
+    const int next_tile = (int)min(next_first + (int64_t)wu * G_, (int64_t)ntiles);
+    // A wave whose tile lies past the last row (a small batch, or the last
+    // round) still copies its share of every chunk and passes the barriers,
+    // but skips the chunk's arithmetic: zero rows would have come out of it.
+    const bool has_rows = tile64 < ntiles;
     // one chunk: wait for its copies (the wave's own; the barrier makes every
     // wave's visible and retires the other slot's last reader), start the
     // next chunk's copies, compute.  CC (the column chunk) is a template
@@ -516,14 +533,14 @@ __global__ __launch_bounds__((SGeo<P, ST>::THREADS), (SGeo<P, ST>::MINW)) void m
       wait_vm_rt(after);
       __syncthreads();
       const ChunkPos nxt = next_chunk(p, cur);
-      if (!(nxt.l == 0 && nxt.cc == 0 && nextb >= nbatch)) copy_chunk<P, ST>(p, nxt, js ? slot0 : slot1, wu, lane);
+      if (!(nxt.l == 0 && nxt.cc == 0 && next_first >= ntiles)) copy_chunk<P, ST>(p, nxt, js ? slot0 : slot1, wu, lane);
       after = 0;
       if (l == p.L - 1 && CC == 0) {
-        // the next batch's x (a zero-row tile past the last batch reads nothing)
-        load_x<P>(p, nextb * G::WAVES + wu, lane, hb);
+        // the next round's x (a zero-row tile past the last tile reads nothing)
+        load_x<P>(p, next_tile, lane, hb);
         after = G::MT * G::KSM;
       }
-      after += run_chunk<P, ACT, ST, CC>(p, l, js ? slot1 : slot0, ha, hb, tile, lane);
+      if (has_rows) after += run_chunk<P, ACT, ST, CC>(p, l, js ? slot1 : slot0, ha, hb, tile, lane);
       cur = nxt;
       js ^= 1;
     };
@@ -533,17 +550,16 @@ __global__ __launch_bounds__((SGeo<P, ST>::THREADS), (SGeo<P, ST>::MINW)) void m
         if (p.dims[l + 1] > 128) step(std::integral_constant<int, 1>{}, l);
       ha = hb;
     }
-    batch = nextb;
+    first = next_first;
   }
 }
 
-// Grid: min(#CUs x workgroups per CU, #batches) persistent workgroups
+// Grid: min(#CUs x workgroups per CU, #wave tiles) persistent workgroups
 // (occupancy from the runtime, cached), or the caller's count.
 template <int P, int ACT, bool ST>
 hipError_t launch_pa(MlpStreamParams p, int num_workgroups, int num_cus, hipStream_t stream) {
   using G = SGeo<P, ST>;
-  const int64_t tiles = ((int64_t)p.M + G::TR - 1) / G::TR;
-  p.num_tiles = (int)((tiles + G::WAVES - 1) / G::WAVES);  // batches
+  p.num_tiles = (int)(((int64_t)p.M + G::TR - 1) / G::TR);
   static std::atomic<int> per_cu_cache{0};
   int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu == 0) {
