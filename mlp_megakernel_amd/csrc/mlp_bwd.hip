@@ -91,38 +91,6 @@ __device__ __forceinline__ int sfz(int r) {
     return ((r & 3) << 1) | ((r >> 2) & 1);
 }
 
-// Weights in LDS: W_l as D rows k of D fp16, 16-byte chunks swizzled by
-// wswz.  Layer L-1 is fed by dout (natural unit order); the others by the
-// registers of the layer above, whose unit order is that of layer_k_slot.
-template <int D, int L>
-__device__ __forceinline__ void stage_weights_bwd(const MlpBwdParams& p, _Float16* sW) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  for (int idx = threadIdx.x; idx < L * D * CPR; idx += BGeo<D>::THREADS) {
-    const int l = idx / (D * CPR);
-    const int rem = idx - l * D * CPR;
-    const int k = rem / CPR;
-    const int cb = rem - k * CPR;
-    // the true layer is dims[l] x dims[l+1] (pitch dims[l+1]); units outside
-    // it are staged as zero (a narrower chain run at width D)
-    const int K = p.dims[l], N = p.dims[l + 1];
-    const _Float16* row = (const _Float16*)p.W[l] + (int64_t)k * N;
-    const f16x4 z4 = (f16x4){0, 0, 0, 0};
-    f16x8 v;
-    if (l == L - 1) {
-      v = (k < K && 8 * cb < N) ? *(const f16x8*)(row + 8 * cb) : (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
-    } else {
-      // slots 8 cb .. 8 cb + 7 (cb = 4 a + b) hold units 32 a + 4 b + 0..3
-      // and 32 a + 16 + 4 b + 0..3 (each group of 4 is inside or outside N
-      // as a whole, N being a multiple of 8)
-      const int a = cb >> 2, b = cb & 3;
-      const f16x4 lo = (k < K && 32 * a + 4 * b < N) ? *(const f16x4*)(row + 32 * a + 4 * b) : z4;
-      const f16x4 hi = (k < K && 32 * a + 16 + 4 * b < N) ? *(const f16x4*)(row + 32 * a + 16 + 4 * b) : z4;
-      v = (f16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
-    *(f16x8*)(sW + (l * D + k) * D + ((cb ^ wswz<D>(k)) << 3)) = v;
-  }
-}
-
 // Per-lane constants.
 template <int D>
 struct BLane {
@@ -187,6 +155,51 @@ struct RowsF32 {  // fp32 result layout: v[s][t] = units 16 t + 4 g .. + 3 of th
 constexpr uint32_t OFF_NONE = 0x80000000u;
 __device__ __forceinline__ uint32_t masked(bool ok, uint32_t off) { return ok ? off : OFF_NONE; }
 __device__ __forceinline__ int lane_group() { return (int)(threadIdx.x & 63) >> 4; }
+
+// Weights in LDS: W_l as D rows k of D fp16, 16-byte chunks swizzled by
+// wswz.  Layer L-1 is fed by dout (natural unit order); the others by the
+// registers of the layer above, whose unit order is that of layer_k_slot.
+// The true layer is dims[l] x dims[l+1] (pitch dims[l+1]); units outside it
+// are staged as zero (a narrower chain run at width D): their loads go to
+// OFF_NONE.  Each thread issues all its loads of a layer before its first
+// LDS write, and the layer index is a constant, so a layer costs one memory
+// round trip instead of one per 16-byte chunk.
+template <int D, int L>
+__device__ __forceinline__ void stage_weights_bwd(const MlpBwdParams& p, _Float16* sW) {
+  constexpr int CPR = D / 8;                             // 16-byte chunks per row
+  constexpr int PER = D * CPR / BGeo<D>::THREADS;        // chunks of one layer per thread
+  static_assert(D * CPR % BGeo<D>::THREADS == 0, "whole chunks per thread");
+#pragma unroll
+  for (int l = 0; l < L; ++l) {
+    const int K = p.dims[l], N = p.dims[l + 1];
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.W[l], (short)0, K * N * 2, 0x00020000);
+    u32x4 v[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = (int)threadIdx.x + i * BGeo<D>::THREADS;
+      const int k = idx / CPR, cb = idx % CPR;
+      const uint32_t row = (uint32_t)(k * N) * 2u;
+      if (l == L - 1) {
+        v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, masked(k < K && 8 * cb < N, row + 16u * cb), 0, 0);
+      } else {
+        // slots 8 cb .. 8 cb + 7 (cb = 4 a + b) hold units 32 a + 4 b + 0..3
+        // and 32 a + 16 + 4 b + 0..3 (each group of 4 is inside or outside N
+        // as a whole, N being a multiple of 8)
+        const int u = 32 * (cb >> 2) + 4 * (cb & 3);
+        const u32x2 lo = __builtin_amdgcn_raw_buffer_load_b64(rs, masked(k < K && u < N, row + 2u * u), 0, 0);
+        const u32x2 hi = __builtin_amdgcn_raw_buffer_load_b64(rs, masked(k < K && u + 16 < N, row + 2u * (u + 16)), 0, 0);
+        v[i] = (u32x4){lo[0], lo[1], hi[0], hi[1]};
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int idx = (int)threadIdx.x + i * BGeo<D>::THREADS;
+      const int k = idx / CPR, cb = idx % CPR;
+      *(u32x4*)(sW + (l * D + k) * D + ((cb ^ wswz<D>(k)) << 3)) = v[i];
+    }
+  }
+}
 
 // B-form fp16 rows (x, dout) of `width` true columns: units 32 ks + 8 g .. + 7.
 template <int D>
@@ -503,8 +516,6 @@ __global__ __launch_bounds__(BGeo<D>::THREADS, 1) void mlp_bwd_kernel(MlpBwdPara
   using P = BPolicy<D, L>;
   __shared__ __attribute__((aligned(16))) _Float16 sW[L * D * D];
   __shared__ __attribute__((aligned(256))) _Float16 sStage[P::SETS * 2 * G::R * D];
-  stage_weights_bwd<D, L>(p, sW);
-
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const BLane<D> c = blane_setup<D>(p, sW, w, lane);
@@ -531,6 +542,8 @@ __global__ __launch_bounds__(BGeo<D>::THREADS, 1) void mlp_bwd_kernel(MlpBwdPara
       load_h<D, L>(p, c, L - 1, tile, w, st);
     }
   }
+  // the weights' loads go out behind the first tile's
+  stage_weights_bwd<D, L>(p, sW);
   __syncthreads();  // weights staged
   while (tile < p.num_tiles) {
     const int next = tile + (int)gridDim.x;

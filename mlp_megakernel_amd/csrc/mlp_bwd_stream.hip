@@ -98,6 +98,35 @@ __device__ __forceinline__ int hsw(int r) { return ((r & 3) << 2) ^ (((r >> 2) &
 constexpr uint32_t L_OFF_NONE = 0x80000000u;  // past every resource (all span less than 2^31 bytes)
 __device__ __forceinline__ uint32_t lmask(bool ok, uint32_t off) { return ok ? off : L_OFF_NONE; }
 
+// Stage W (rows x cols fp16, dense, rows <= MAXR, cols <= 8 PIECES) as LDS
+// rows of 16 PIECES bytes, 16-byte piece c of row i at c ^ (i mod 16), zero
+// past the matrix up to the next 16 rows and 8 PIECES columns.  A thread
+// issues up to 16 loads before its first LDS write (pieces outside the
+// matrix read zero through the buffer's range check), so the copy costs one
+// or two memory round trips, not one per piece.
+template <int THREADS, int PIECES, int MAXR>
+__device__ __forceinline__ void stage_w_rows(uint32_t sWr, const void* W, int rows, int cols) {
+  constexpr int TOTAL = MAXR * PIECES / THREADS;  // pieces per thread at most
+  constexpr int B = TOTAL < 16 ? TOTAL : 16;
+  static_assert(MAXR * PIECES % THREADS == 0, "whole pieces per thread");
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, rows * cols * 2, 0x00020000);
+  const int n = ((rows + 15) & ~15) * PIECES;
+  for (int base = threadIdx.x; base < n; base += B * THREADS) {
+    u32x4 v[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int idx = base + u * THREADS, i = idx / PIECES, c = idx % PIECES;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, lmask(i < rows && 8 * c < cols, (uint32_t)(i * cols + 8 * c) * 2u),
+                                                   0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const int idx = base + u * THREADS, i = idx / PIECES, c = idx % PIECES;
+      if (idx < n) lds_write128(sWr + (uint32_t)(i * 16 * PIECES + ((c ^ (i & 15)) << 4)), v[u]);
+    }
+  }
+}
+
 // Buffer resource over rows [first, first + n) of a matrix (pitch ld
 // elements of es bytes, M rows): rows past M read as zero, stores to them
 // are dropped.
@@ -161,17 +190,6 @@ __global__ __launch_bounds__(LGeo<P>::THREADS, 1) void mlp_layer_bwd_kernel(Laye
   const int I = a.I, J = a.J;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, q = lane & 15, g = lane >> 4;
 
-  if constexpr (DATA) {
-    // W_l rows (zero past I up to the next 16, and past J up to P)
-    const int rows = (I + 15) & ~15;
-    for (int idx = threadIdx.x; idx < rows * PIECES; idx += G::THREADS) {
-      const int i = idx / PIECES, c = idx % PIECES;
-      u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-      if (i < I && 8 * c < J) v = *(const u32x4*)((const _Float16*)a.W + (int64_t)i * J + 8 * c);
-      lds_write128(sW + (uint32_t)(i * ROWB + ((c ^ (i & 15)) << 4)), v);
-    }
-  }
-
   const int ksn = (J + 31) >> 5;  // data-product k steps
   const int njn = (J + 15) >> 4;  // j tiles
   bool on[TI];                    // the wave's i tiles that hold units below I
@@ -195,6 +213,9 @@ __global__ __launch_bounds__(LGeo<P>::THREADS, 1) void mlp_layer_bwd_kernel(Laye
   TileRegs<P, MODE> nx;
   int tile = blockIdx.x;
   if (tile < a.num_tiles) load_tile<P, MODE>(a, tile, w, q, g, nx);
+  // W_l rows (zero past I up to the next 16, and past J up to P), loaded
+  // behind the first tile
+  if constexpr (DATA) stage_w_rows<G::THREADS, PIECES, P>(sW, a.W, I, J);
   // nothing of the prologue stays in flight into the loop
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
@@ -403,17 +424,10 @@ __device__ __forceinline__ void weight_grad128(uint32_t sIn, uint32_t sH, uint32
   }
 }
 
-// Stage W (rows x cols fp16, dense) as LDS rows of 256 bytes, zero past the
-// matrix up to the next 16 rows and 128 columns.
+// Stage W (rows x cols fp16, dense, rows <= 128) as LDS rows of 256 bytes,
+// zero past the matrix up to the next 16 rows and 128 columns.
 __device__ __forceinline__ void stage_w128(uint32_t sWr, const void* W, int rows, int cols) {
-  using G = LGeo<128>;
-  const int rr = (rows + 15) & ~15;
-  for (int idx = threadIdx.x; idx < rr * G::PIECES; idx += G::THREADS) {
-    const int i = idx / G::PIECES, c = idx % G::PIECES;
-    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
-    if (i < rows && 8 * c < cols) v = *(const u32x4*)((const _Float16*)W + (int64_t)i * cols + 8 * c);
-    lds_write128(sWr + (uint32_t)(i * G::ROWB + ((c ^ (i & 15)) << 4)), v);
-  }
+  stage_w_rows<LGeo<128>::THREADS, LGeo<128>::PIECES, 128>(sWr, W, rows, cols);
 }
 
 // ACT: the hidden activation (the top layer's derivative, and the bottom
@@ -429,9 +443,6 @@ __global__ __launch_bounds__(LGeo<128>::THREADS, 1) void mlp_layer2_bwd_kernel(L
                  sZ2 = sH + R * ROWB, sH2 = sZ2 + R * ROWB;
   const int It = a.It, Jt = a.Jt, Ib = a.Ib;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, q = lane & 15, g = lane >> 4;
-
-  stage_w128(sWt, a.Wt, It, Jt);
-  if constexpr (MODE != 0) stage_w128(sWb, a.Wb, Ib, It);
 
   const bool on_t = 16 * w < It, on_b = 16 * w < Ib;
   const int ksn_t = (Jt + 31) >> 5, njn_t = (Jt + 15) >> 4;
@@ -454,6 +465,9 @@ __global__ __launch_bounds__(LGeo<128>::THREADS, 1) void mlp_layer2_bwd_kernel(L
   Tile2Regs<MODE> nx;
   int tile = blockIdx.x;
   if (tile < a.num_tiles) load_tile2<MODE>(a, tile, w, q, g, nx);
+  // the weights, loaded behind the first tile
+  stage_w128(sWt, a.Wt, It, Jt);
+  if constexpr (MODE != 0) stage_w128(sWb, a.Wb, Ib, It);
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   for (; tile < a.num_tiles; tile += gridDim.x) {
