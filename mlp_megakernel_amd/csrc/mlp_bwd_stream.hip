@@ -555,14 +555,26 @@ __global__ __launch_bounds__(LGeo<128>::THREADS, 1) void mlp_layer2_bwd_kernel(L
 // dW = sum of nparts partials of E float4 groups each (row-major, as dW).  A
 // workgroup owns 32 groups and splits the partial index over 8 slices (slice
 // s adds partials s, s + 8, ... in order), then adds the slice sums in slice
-// order: a fixed order for a given grid.
+// order: a fixed order for a given grid.  One launch sums up to two layers
+// (a two-layer launch's partials): the first blocks0 workgroups the first,
+// the rest the second.
 constexpr int LRED_GROUPS = 32, LRED_SLICES = 8;
 
-__global__ __launch_bounds__(LRED_GROUPS* LRED_SLICES) void layer_bwd_reduce(const float* __restrict__ partial,
-                                                                              int nparts, int E, float* __restrict__ dW) {
+struct ReduceSeg {
+  const float* partial;
+  float* dW;
+  int E;
+};
+
+__global__ __launch_bounds__(LRED_GROUPS* LRED_SLICES) void layer_bwd_reduce(ReduceSeg s0, ReduceSeg s1, int blocks0,
+                                                                              int nparts) {
   __shared__ f32x4 red[LRED_SLICES][LRED_GROUPS];
+  const bool second = (int)blockIdx.x >= blocks0;
+  const float* __restrict__ partial = second ? s1.partial : s0.partial;
+  float* __restrict__ dW = second ? s1.dW : s0.dW;
+  const int E = second ? s1.E : s0.E;
   const int gi = threadIdx.x % LRED_GROUPS, slice = threadIdx.x / LRED_GROUPS;
-  const int e = blockIdx.x * LRED_GROUPS + gi;
+  const int e = ((int)blockIdx.x - (second ? blocks0 : 0)) * LRED_GROUPS + gi;
   f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
   if (e < E) {
     const f32x4* src = (const f32x4*)partial + e;
@@ -659,10 +671,11 @@ hipError_t launch_mlp_backward_stream(const MlpStreamBwdParams& p, int P, int hi
   const void* zin = p.dout;
   int64_t ldzin = p.ldd;
   int zsel = 0;
-  auto reduce = [&](const float* part, int nparts, int I, int J, float* dW) -> hipError_t {
-    const int groups = I * J / 4;
-    hipLaunchKernelGGL(layer_bwd_reduce, dim3((groups + LRED_GROUPS - 1) / LRED_GROUPS),
-                       dim3(LRED_GROUPS * LRED_SLICES), 0, stream, part, nparts, groups, dW);
+  // the sums of one or two layers' partials (nparts each) in one launch
+  auto reduce = [&](int nparts, ReduceSeg s0, ReduceSeg s1) -> hipError_t {
+    const int b0 = (s0.E + LRED_GROUPS - 1) / LRED_GROUPS, b1 = (s1.E + LRED_GROUPS - 1) / LRED_GROUPS;
+    hipLaunchKernelGGL(layer_bwd_reduce, dim3(b0 + b1), dim3(LRED_GROUPS * LRED_SLICES), 0, stream, s0, s1, b0,
+                       nparts);
     return hipGetLastError();
   };
   hipError_t e = hipSuccess;
@@ -723,8 +736,9 @@ hipError_t launch_mlp_backward_stream(const MlpStreamBwdParams& p, int P, int hi
       else
         hipLaunchKernelGGL((mlp_layer2_bwd_kernel<ACT_NONE, 1>), dim3(nwg2), dim3(LGeo<128>::THREADS), 0, stream, a);
       if ((e = hipGetLastError()) != hipSuccess) return e;
-      if ((e = reduce(partial, nwg2, a.It, a.Jt, p.dW[l])) != hipSuccess) return e;
-      if ((e = reduce(a.pb, nwg2, a.Ib, a.It, p.dW[b])) != hipSuccess) return e;
+      if ((e = reduce(nwg2, ReduceSeg{partial, p.dW[l], a.It * a.Jt / 4}, ReduceSeg{a.pb, p.dW[b], a.Ib * a.It / 4})) !=
+          hipSuccess)
+        return e;
       if (b > 0) {
         zin = zbuf[zsel];
         ldzin = s.ldz;
@@ -759,7 +773,8 @@ hipError_t launch_mlp_backward_stream(const MlpStreamBwdParams& p, int P, int hi
     e = P == 256 ? launch_layer_p<256>(a, mode, hidden_act, nwg, stream)
                  : launch_layer_p<128>(a, mode, hidden_act, nwg, stream);
     if (e != hipSuccess) return e;
-    if ((e = reduce(partial, nwg, a.I, a.J, p.dW[l])) != hipSuccess) return e;
+    if ((e = reduce(nwg, ReduceSeg{partial, p.dW[l], a.I * a.J / 4}, ReduceSeg{partial, p.dW[l], 0})) != hipSuccess)
+      return e;
     if (l > 0) {
       zin = zbuf[zsel];
       ldzin = s.ldz;
