@@ -830,17 +830,16 @@ def traffic_plan():
 def stream_backward_kernels(dims):
     """Dispatch sequence of the layer-by-layer backward: from the top, two
     layers per launch while every width is at most 128 (then one reduction
-    per layer), else one layer per launch and its reduction."""
-    L, seq, l = len(dims) - 1, [], len(dims) - 2
+    launch for both), else one layer per launch and its reduction."""
+    seq, l = [], len(dims) - 2
     pairs = max(dims) <= 128
     while l >= 0:
         if pairs and l >= 1:
-            seq += ["mlp_layer2_bwd_kernel", "layer_bwd_reduce", "layer_bwd_reduce"]
+            seq += ["mlp_layer2_bwd_kernel", "layer_bwd_reduce"]
             l -= 2
         else:
             seq += ["mlp_layer_bwd_kernel", "layer_bwd_reduce"]
             l -= 1
-    assert seq.count("layer_bwd_reduce") == L
     return seq
 
 
