@@ -98,3 +98,37 @@ def test_grid_invariance_and_nan_free_padding():
     torch.cuda.synchronize()
     assert torch.equal(ob[:, :O].cpu().view(torch.int16), outs[0].view(torch.int16))
     assert bool(torch.isnan(ob[:, O:]).all())
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16 if t.element_size() == 2 else torch.int32)
+
+
+@pytest.mark.parametrize("dims", [DEEP128, WIDE], ids=lambda d: "x".join(map(str, d)))
+def test_small_batches_equal_rows_of_a_large_batch(dims):
+    # A round hands wave w of workgroup b the tile r G W + b + w G; small
+    # batches leave most waves of a round without a tile (they copy the
+    # chunks and pass the barriers, nothing else).  Each row's arithmetic does
+    # not depend on which wave runs it, so a small batch must equal the same
+    # rows of a large one bit for bit, forward and training forward (out and
+    # the stored activations), on the default grid and on a few others.
+    w = datagen.MLP3
+    big = 70_000
+    x, Ws = datagen.mlp_inputs(w, M=big, dims=dims)
+    xg, wg = to_gpu(x), [t.to("cuda") for t in Ws]
+    progress("stream small batches %s M=%d" % ("x".join(map(str, dims)), big))
+    full = mk.mlp_forward(xg, wg)
+    tout, tacts = mk.mlp_forward_train(xg, wg)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(tout), _bits(full))
+    for m in (1, 33, 1000, 9000):
+        for g in (0, 1, 7):
+            part = mk.mlp_forward(xg[:m], wg, num_workgroups=g)
+            assert torch.equal(_bits(part), _bits(full[:m])), (m, g)
+        o, a = mk.mlp_forward_train(xg[:m], wg)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(o), _bits(full[:m])), m
+        for l, (s, t) in enumerate(zip(a, tacts)):
+            assert torch.equal(_bits(s), _bits(t[:m])), (m, l)
+    ref = oracle.mlp_forward(f64(x[:1000]), [f64(t) for t in Ws])
+    assert_close(f64(full[:1000]), ref, 2e-2, "small batch %s" % ("x".join(map(str, dims)),))
