@@ -196,7 +196,7 @@ size_t coalesce_mlp_backward_workspace_size(const int64_t* dims, int32_t L, int6
  * computes dz_l (or dx) and the per-workgroup sums of dW[l] from the same
  * row tiles, with the dz_l passed between launches kept as fp16 in the
  * workspace (the precision in which the next layer uses it either way),
- * then the reductions of the dW.  Either way repeated calls
+ * then the reduction of that launch's dW sums.  Either way repeated calls
  * give identical bits.  M == 0 gives dW = 0.  Non-square chains write only
  * the true dims[l] x dims[l+1] of each dW and the true columns of dx.
  * Outputs must not overlap the inputs, each other or the workspace.  Calls

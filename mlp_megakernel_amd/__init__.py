@@ -277,7 +277,8 @@ def mlp_backward(x: torch.Tensor, weights: Sequence[torch.Tensor], acts: Sequenc
     """(dW list (fp32), dx or None): the backward of the chain from the
     stored activations (coalesce_mlp_backward): one fused kernel plus a
     fixed-order reduction, or for chains whose weights do not fit in LDS one
-    fused kernel and one reduction per layer."""
+    fused kernel and one reduction launch per layer (per pair of layers at
+    widths up to 128)."""
     lib = load_library()
     M, ldx, dims = _chain_dims(x, weights)
     L = len(weights)
