@@ -85,3 +85,17 @@ def test_timed_kernels_have_traffic_records():
                 "forward_train/fp16_mlp3_d128", "backward/fp16_mlp3_d128"]:
         e = TRAFFIC[key]
         assert e["fetch_bytes"] > 0 and e["write_bytes"] > 0 and len(e["source_sha256"]) == 64
+
+
+@pytest.mark.parametrize("dims,expect", [
+    ((128,) * 7, ["mlp_layer2_bwd_kernel", "layer_bwd_reduce"] * 3),
+    ((256,) * 4, ["mlp_layer_bwd_kernel", "layer_bwd_reduce"] * 3),
+    ((64,) * 6, ["mlp_layer2_bwd_kernel", "layer_bwd_reduce"] * 2 + ["mlp_layer_bwd_kernel", "layer_bwd_reduce"]),
+    ((200, 256, 40, 136), ["mlp_layer_bwd_kernel", "layer_bwd_reduce"] * 3),
+])
+def test_stream_backward_dispatch_plan(dims, expect):
+    # the counter runs match dispatches to this plan: from the top layer, two
+    # layers per launch while every width is at most 128, each launch followed
+    # by one reduction launch (both layers of a pair in one)
+    import bench
+    assert bench.stream_backward_kernels(dims) == expect
